@@ -1,0 +1,238 @@
+"""Synthetic workloads of the packed encoder forward: shapes, items and seeded tensors.
+
+Five workloads, each the shape of one of the encoders on the reference pages,
+with random weights (no trained checkpoint is available):
+
+  vit_layer_f32        one pre-LN ViT layer: 64 tokens, d 128, 2x64 heads, MLP 512
+  gemma_text_f32       EmbeddingGemma-style text encoder: 24 sandwich layers, d 512,
+                       8x64 heads, qk-norm + 1-D RoPE, window 512, gated GELU 2048,
+                       16 packed sequences of 32..2048 rows, final RMS + mean pool
+  lfm2_vit_f32         LFM2-VL-style ViT: 16 pre-LN layers, 1024 patches, d 768,
+                       12x64 heads, MLP 3072, final LayerNorm
+  zimage_dit_1056      Z-Image-style DiT stack: 30 sandwich layers, d 3840, 30x128
+                       heads, int8 row-scaled weights x f16 activations, qk-norm +
+                       2-D RoPE over a 32x32 grid + 32 caption rows, SwiGLU 10240
+  zimage_dit_cfg_8448  the same stack at a 64x64 grid + 128 caption rows as a CFG
+                       batch-2 program: rows [img0|img1|cap0|cap1]
+
+Only draws and shapes live here; the forward itself is computed by the HIP
+library (and, independently, by the oracle).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import synth
+
+MASTER_SEED = 0xE1C0DE00
+
+BLOCK_PRE_LN, BLOCK_SANDWICH = 0, 1
+PATH_F32, PATH_I8F16 = 0, 1
+MLP_GELU, MLP_GELU_GATED, MLP_SWIGLU = 0, 1, 2
+FINAL_NONE, FINAL_LN, FINAL_RMS_MEANPOOL = 0, 1, 2
+
+CONFIGS = {
+    "vit_layer_f32": dict(
+        num=1, block=BLOCK_PRE_LN, path=PATH_F32, mlp=MLP_GELU, d=128, nq=2, nkv=2, hd=64,
+        ff=512, layers=1, window=0, rope_sections=0, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / 8.0, rope_base=10000.0, x_scale=1.0, biases=True,
+        lengths=[64]),
+    "gemma_text_f32": dict(
+        num=2, block=BLOCK_SANDWICH, path=PATH_F32, mlp=MLP_GELU_GATED, d=512, nq=8, nkv=8,
+        hd=64, ff=2048, layers=24, window=512, rope_sections=1, final=FINAL_RMS_MEANPOOL,
+        eps=1e-6, attn_scale=1.0, rope_base=10000.0, x_scale=math.sqrt(512.0), biases=False,
+        nseq=16, len_lo=32, len_hi=2048),
+    "lfm2_vit_f32": dict(
+        num=3, block=BLOCK_PRE_LN, path=PATH_F32, mlp=MLP_GELU, d=768, nq=12, nkv=12, hd=64,
+        ff=3072, layers=16, window=0, rope_sections=0, final=FINAL_LN, eps=1e-6,
+        attn_scale=1.0 / 8.0, rope_base=10000.0, x_scale=1.0, biases=True,
+        lengths=[1024]),
+    "zimage_dit_1056": dict(
+        num=4, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
+        hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
+        grid=32, ncap=32, cfg_pair=False),
+    "zimage_dit_cfg_8448": dict(
+        num=5, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
+        hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
+        grid=64, ncap=128, cfg_pair=True),
+}
+
+
+@dataclass
+class Workload:
+    """One packed batch and its model, as host arrays.
+
+    items: per item, a list of (first row, row count) ranges (one or two);
+    grids: per item the image grid side G for 2-D positions, else 0.
+    layers[i]: tensor name -> array (float32 weights/norms/biases, or int8
+    weights with float32 row scales s_* on the int8 path); int8 weights may be
+    absent (lazy) and are then drawn by `int8_weight` on demand.
+    """
+    name: str
+    cfg: dict
+    rows: int
+    items: list
+    grids: list
+    x: np.ndarray
+    layers: list = field(default_factory=list)
+    final_w: np.ndarray | None = None
+    final_b: np.ndarray | None = None
+    seed: int = 0
+
+    @property
+    def ld(self):
+        c = self.cfg
+        return (c["nq"] + 2 * c["nkv"]) * c["hd"]
+
+
+def weight_shapes(cfg: dict) -> dict:
+    d, q, kv, ff = cfg["d"], cfg["nq"] * cfg["hd"], cfg["nkv"] * cfg["hd"], cfg["ff"]
+    s = {"wq": (q, d), "wk": (kv, d), "wv": (kv, d), "wo": (d, q),
+         "w_up": (ff, d), "w_down": (d, ff)}
+    if cfg["mlp"] != MLP_GELU:
+        s["w_gate"] = (ff, d)
+    return s
+
+
+def _normal(seed, name, shape, std, mean=0.0):
+    n = int(np.prod(shape))
+    z = synth.normal_np(synth.tensor_key(seed, name), 0, n)
+    return (mean + std * z).astype(np.float32).reshape(shape)
+
+
+def int8_weight_rows(seed: int, layer: int, name: str, shape, r0: int, r1: int) -> np.ndarray:
+    """Rows r0..r1-1 of an int8 weight (host draw of just those rows)."""
+    k = synth.tensor_key(seed, f"L{layer}.{name}")
+    cols = shape[1]
+    return synth.int8_np(k, r0 * cols, (r1 - r0) * cols).reshape(r1 - r0, cols)
+
+
+def int8_weight_torch(seed: int, layer: int, name: str, shape, device):
+    k = synth.tensor_key(seed, f"L{layer}.{name}")
+    return synth.int8_torch(k, 0, shape[0] * shape[1], device).view(shape[0], shape[1])
+
+
+def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
+    t = {}
+    d, hd = cfg["d"], cfg["hd"]
+    for name, shape in weight_shapes(cfg).items():
+        if cfg["path"] == PATH_F32:
+            t[name] = _normal(seed, f"L{li}.{name}", shape, 0.02)
+        else:
+            if not lazy_int8:
+                t[name] = int8_weight_rows(seed, li, name, shape, 0, shape[0])
+            sname = "s" + name[1:]
+            z = synth.normal_np(synth.tensor_key(seed, f"L{li}.{sname}"), 0, shape[0])
+            t[sname] = (0.002 * np.exp(0.25 * z)).astype(np.float32)
+    if cfg["biases"]:
+        for name, width in (("bq", cfg["nq"] * hd), ("bk", cfg["nkv"] * hd),
+                            ("bv", cfg["nkv"] * hd), ("bo", d), ("b_up", cfg["ff"]),
+                            ("b_down", d)):
+            t[name] = _normal(seed, f"L{li}.{name}", (width,), 0.01)
+    if cfg["block"] == BLOCK_PRE_LN:
+        for name in ("norm1_w", "norm2_w"):
+            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
+        for name in ("norm1_b", "norm2_b"):
+            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.01)
+    else:
+        for name in ("norm1_w", "post_attn_w", "norm2_w", "post_ff_w"):
+            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
+        for name in ("q_norm_w", "k_norm_w"):
+            t[name] = _normal(seed, f"L{li}.{name}", (hd,), 0.02, 1.0)
+    return t
+
+
+def layout(cfg: dict, lengths=None, grid=None, ncap=None, cfg_pair=None):
+    """(rows, items, grids) of a workload.
+
+    Sequences (1-D): `lengths` back to back, one single-range item each.
+    DiT (2-D): one item = G*G image rows + ncap caption rows; the CFG pair is two
+    items over rows [img0 | img1 | cap0 | cap1], each item = its image range then
+    its caption range.
+    """
+    if cfg["rope_sections"] == 2:
+        g = cfg["grid"] if grid is None else grid
+        nc = cfg["ncap"] if ncap is None else ncap
+        pair = cfg["cfg_pair"] if cfg_pair is None else cfg_pair
+        ni = g * g
+        if not pair:
+            return ni + nc, [[(0, ni), (ni, nc)] if nc else [(0, ni)]], [g]
+        items = [[(0, ni), (2 * ni, nc)] if nc else [(0, ni)],
+                 [(ni, ni), (2 * ni + nc, nc)] if nc else [(ni, ni)]]
+        return 2 * ni + 2 * nc, items, [g, g]
+    if lengths is None:
+        if "lengths" in cfg:
+            lengths = cfg["lengths"]
+        else:
+            k = synth.tensor_key(MASTER_SEED + cfg["num"], "lengths")
+            lengths = [int(v) for v in synth.ints_np(k, cfg["nseq"], cfg["len_lo"], cfg["len_hi"])]
+    items, r = [], 0
+    for n in lengths:
+        items.append([(r, int(n))])
+        r += int(n)
+    return r, items, [0] * len(items)
+
+
+def make(name: str, layers=None, lengths=None, grid=None, ncap=None, cfg_pair=None,
+         lazy_int8=False, overrides=None) -> Workload:
+    """Build workload `name`, optionally reduced (fewer layers, other lengths/grid)."""
+    cfg = dict(CONFIGS[name])
+    if overrides:
+        cfg.update(overrides)
+    if layers is not None:
+        cfg["layers"] = layers
+    seed = MASTER_SEED + cfg["num"]
+    rows, items, grids = layout(cfg, lengths, grid, ncap, cfg_pair)
+    d = cfg["d"]
+    if cfg["rope_sections"] == 2:
+        # image rows are one draw shared by every item (one latent, CFG pair);
+        # each item's caption rows are its own draw
+        x = np.empty((rows, d), np.float32)
+        for i, rr in enumerate(items):
+            (r0, ni) = rr[0]
+            x[r0:r0 + ni] = _normal(seed, "x.img", (ni, d), cfg["x_scale"])
+            if len(rr) > 1:
+                (c0, nc) = rr[1]
+                x[c0:c0 + nc] = _normal(seed, f"x.cap{i}", (nc, d), cfg["x_scale"])
+    else:
+        x = _normal(seed, "x", (rows, d), cfg["x_scale"])
+    w = Workload(name=name, cfg=cfg, rows=rows, items=items, grids=grids, x=x, seed=seed)
+    w.layers = [_layer(cfg, seed, li, lazy_int8) for li in range(cfg["layers"])]
+    if cfg["final"] != FINAL_NONE:
+        w.final_w = _normal(seed, "final_w", (d,), 0.02, 1.0)
+        if cfg["final"] == FINAL_LN:
+            w.final_b = _normal(seed, "final_b", (d,), 0.01)
+    return w
+
+
+def gemm_flops(w: Workload) -> float:
+    """Algorithmic GEMM flops of the whole forward (2 per multiply-add)."""
+    c = w.cfg
+    d, q, kv, ff = c["d"], c["nq"] * c["hd"], c["nkv"] * c["hd"], c["ff"]
+    per_row = d * (q + 2 * kv) + q * d + ff * d * (1 if c["mlp"] == MLP_GELU else 2) + ff * d
+    return 2.0 * per_row * w.rows * c["layers"]
+
+
+def visible_pairs(w: Workload) -> int:
+    """Sum over items of the (query, key) pairs the attention mask lets through."""
+    W = w.cfg["window"]
+    tot = 0
+    for rr in w.items:
+        L = sum(n for _, n in rr)
+        if W == 0 or W >= L - 1:
+            tot += L * L
+        else:
+            i = np.arange(L)
+            tot += int((np.minimum(i + W, L - 1) - np.maximum(i - W, 0) + 1).sum())
+    return tot
+
+
+def attn_flops(w: Workload) -> float:
+    """Algorithmic attention flops: 4*hd per visible pair per head per layer."""
+    c = w.cfg
+    return 4.0 * c["hd"] * c["nq"] * visible_pairs(w) * c["layers"]
