@@ -1,0 +1,124 @@
+"""GPU parity of the whole forward (encoder_forward / encoder_layer_forward)
+against the f64 oracle, per workload, plus the invariants that hold at any
+size: packed == separate, the CFG pair == two singles, the fused layer chain ==
+layer-by-layer, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import DEV, TOL_F32, TOL_I8F16, host, row_rel_err, say
+from transformer_encoder_forward_amd import binding as B
+from transformer_encoder_forward_amd import model as M
+from transformer_encoder_forward_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    B.context(0)
+
+
+def run(w, layers=None, x=None):
+    dm = M.DeviceModel(w, DEV, layers=layers)
+    db = M.DeviceBatch(w, DEV)
+    X = torch.from_numpy(np.ascontiguousarray(w.x if x is None else x)).to(DEV)
+    out = torch.empty((M.out_rows(w), w.cfg["d"]), dtype=torch.float32, device=DEV)
+    ws = dm.workspace(w.rows, DEV)
+    M.encoder_forward(dm, db, X, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def tol(w):
+    return TOL_I8F16 if w.cfg["path"] == wl.PATH_I8F16 else TOL_F32
+
+
+DIT_SMALL = dict(d=1024, nq=8, nkv=8, ff=2560)
+
+CASES = [
+    ("vit_layer_f32", dict()),
+    ("gemma_text_f32", dict(layers=2, lengths=[600, 37, 1100, 5, 130])),
+    ("lfm2_vit_f32", dict(layers=2)),
+    ("zimage_dit_1056", dict(layers=2, grid=8, ncap=8, overrides=DIT_SMALL)),
+    ("zimage_dit_1056", dict(layers=1, grid=4, ncap=4)),
+    ("zimage_dit_cfg_8448", dict(layers=2, grid=6, ncap=5, overrides=DIT_SMALL)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(CASES)])
+def test_forward_vs_oracle(name, kw):
+    w = wl.make(name, **kw)
+    say(f"forward {name} rows={w.rows} layers={w.cfg['layers']} d={w.cfg['d']}")
+    got = host(run(w))
+    ref = O.forward(w)
+    err = row_rel_err(got, ref)
+    say(f"  max row-relative error {err:.3e} (tolerance {tol(w):.0e})")
+    if w.cfg["path"] == wl.PATH_I8F16:
+        err64 = row_rel_err(got, O.forward(w, f16_sites=False))
+        say(f"  vs the pure-f64 diagnostic (no f16 sites): {err64:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= tol(w)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gemma_text_f32", dict(layers=3, lengths=[300, 77, 700])),
+    ("lfm2_vit_f32", dict(layers=2, overrides=dict(), lengths=[200])),
+    ("zimage_dit_cfg_8448", dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)),
+])
+def test_fused_chain_equals_layer_by_layer(name, kw):
+    """encoder_forward (each layer's last row op writes the next pre-norm) gives
+    the same bits as encoder_layer_forward called per layer."""
+    w = wl.make(name, **kw)
+    w.cfg["final"] = wl.FINAL_NONE
+    fused = run(w)
+    dm = M.DeviceModel(w, DEV)
+    db = M.DeviceBatch(w, DEV)
+    h = torch.from_numpy(w.x.copy()).to(DEV)
+    ws = dm.workspace(w.rows, DEV)
+    for li in range(w.cfg["layers"]):
+        M.encoder_layer_forward(dm, li, db, h, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, h)
+
+
+def test_packed_equals_separate_stack():
+    lengths = [513, 40, 1030]
+    w = wl.make("gemma_text_f32", layers=2, lengths=lengths)
+    packed = run(w)
+    r = 0
+    for i, n in enumerate(lengths):
+        ws_ = wl.make("gemma_text_f32", layers=2, lengths=[n])
+        alone = run(ws_, x=w.x[r:r + n])
+        assert torch.equal(alone[0], packed[i]), f"sequence {i}"
+        r += n
+
+
+def test_cfg_pair_equals_two_singles():
+    """The CFG batch-2 program gives each item the bits of its single forward."""
+    kw = dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)
+    w = wl.make("zimage_dit_cfg_8448", cfg_pair=True, **kw)
+    pair = run(w)
+    for i, rr in enumerate(w.items):
+        idx = np.concatenate([np.arange(r0, r0 + n) for r0, n in rr])
+        single = wl.make("zimage_dit_cfg_8448", cfg_pair=False, **kw)
+        alone = run(single, x=w.x[idx])
+        assert torch.equal(alone, pair[torch.from_numpy(idx).to(DEV)]), f"item {i}"
+
+
+def test_deterministic():
+    w = wl.make("gemma_text_f32", layers=2, lengths=[333, 64])
+    assert torch.equal(run(w), run(w))
+
+
+def test_nonfinite_input_flagged():
+    w = wl.make("gemma_text_f32", layers=1, lengths=[50, 60])
+    w.cfg["final"] = wl.FINAL_NONE
+    x = w.x.copy()
+    x[3, 5] = np.inf
+    out = host(run(w, x=x))
+    assert not np.isfinite(out[:50]).all()
+    assert np.isfinite(out[50:]).all()

@@ -1,0 +1,340 @@
+"""GPU parity of each op behind the C ABI against the f64 oracle.
+
+Integer-valued operands make every partial sum exact in f32 and f64, so those
+GEMM cases must match the oracle bit for bit (this pins offsets, strides, the
+weight slot, the MFMA output layout, bias and accumulate).  Random operands are
+held to the path's tolerance.  Attention is checked against brute force, with
+the one-hot mask probe bit-exact, and packed == separate bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_util import DEV, TOL_F32, TOL_I8F16, host, row_rel_err, say, to_dev
+from transformer_encoder_forward_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    B.context(0)
+
+
+# ---------------------------------------------------------------- GEMM f32
+
+@pytest.mark.parametrize("n,m,k", [(1, 1, 4), (37, 70, 36), (130, 257, 128), (257, 128, 512),
+                                   (64, 384, 128), (300, 96, 2048)])
+def test_gemm_f32_integer_exact(n, m, k):
+    say(f"gemm f32 integer n={n} m={m} k={k}")
+    rng = np.random.default_rng(n * 31 + m * 7 + k)
+    x = rng.integers(-8, 9, (n, k)).astype(np.float32)
+    w = rng.integers(-8, 9, (m, k)).astype(np.float32)
+    b = rng.integers(-5, 6, m).astype(np.float32)
+    y0 = rng.integers(-100, 100, (n, m)).astype(np.float32)
+    ref = O.linear(x, w, b)
+    X, Wd, Bd = to_dev(x), to_dev(w), to_dev(b)
+    Y = torch.zeros((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(X, Y, [Wd], [(n, m, k, k, m, 0, 0, 0)], bias=[Bd])
+    assert np.array_equal(host(Y), ref)
+    Y = to_dev(y0)
+    B.gemm_items(X, Y, [Wd], [(n, m, k, k, m, 0, 0, 0)], bias=[Bd], flags=B.ENC_Y_ACCUMULATE)
+    assert np.array_equal(host(Y), ref + y0)
+
+
+def test_gemm_f32_qkv_items_one_launch():
+    """q|k|v as three items of one launch into one panel at column offsets,
+    rows offset and strided input (x_off, ldx > k)."""
+    rng = np.random.default_rng(11)
+    n, d, qw, kw = 150, 128, 128, 64
+    ldx = d + 8
+    xfull = rng.integers(-8, 9, (n + 3, ldx)).astype(np.float32)
+    ws = [rng.integers(-8, 9, (mm, d)).astype(np.float32) for mm in (qw, kw, kw)]
+    ld = qw + 2 * kw
+    Y = torch.full((n, ld), -7.0, dtype=torch.float32, device=DEV)
+    items = [(n, qw, d, ldx, ld, 0, 3 * ldx, 0), (n, kw, d, ldx, ld, 1, 3 * ldx, qw),
+             (n, kw, d, ldx, ld, 2, 3 * ldx, qw + kw)]
+    B.gemm_items(to_dev(xfull), Y, [to_dev(w) for w in ws], items)
+    x = xfull[3:, :d]
+    ref = np.concatenate([O.linear(x, w) for w in ws], 1)
+    assert np.array_equal(host(Y), ref)
+
+
+@pytest.mark.parametrize("n,m,k", [(64, 384, 128), (1000, 1536, 512), (333, 512, 2048),
+                                   (1024, 3072, 768)])
+def test_gemm_f32_random(n, m, k):
+    say(f"gemm f32 random n={n} m={m} k={k}")
+    rng = np.random.default_rng(n + m + k)
+    x = rng.normal(0, 1, (n, k)).astype(np.float32)
+    w = (0.02 * rng.normal(0, 1, (m, k))).astype(np.float32)
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(w)], [(n, m, k, k, m, 0, 0, 0)])
+    err = row_rel_err(host(Y), O.linear(x, w))
+    say(f"  err {err:.2e}")
+    assert err <= TOL_F32
+
+
+def test_gemm_f32_gelu_epilogue():
+    rng = np.random.default_rng(5)
+    n, m, k = 77, 200, 64
+    x = rng.normal(0, 1, (n, k)).astype(np.float32)
+    w = (0.3 * rng.normal(0, 1, (m, k))).astype(np.float32)
+    b = (0.1 * rng.normal(0, 1, m)).astype(np.float32)
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(w)], [(n, m, k, k, m, 0, 0, 0)], bias=[to_dev(b)],
+                 flags=B.ENC_EPI_GELU_TANH)
+    ref = np.vectorize(O.gelu_tanh)(O.linear(x, w, b))
+    assert row_rel_err(host(Y), ref) <= TOL_F32
+
+
+def test_gemm_packed_rows_bit_identical():
+    """A row's output bits do not depend on how many rows share the launch."""
+    rng = np.random.default_rng(6)
+    k, m = 512, 300
+    x = rng.normal(0, 1, (900, k)).astype(np.float32)
+    w = rng.normal(0, 0.02, (m, k)).astype(np.float32)
+    W = to_dev(w)
+    Yall = torch.empty((900, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Yall, [W], [(900, m, k, k, m, 0, 0, 0)])
+    for r0, r1 in ((0, 1), (129, 200), (700, 900)):
+        Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
+        B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)])
+        assert torch.equal(Y, Yall[r0:r1])
+
+
+# ------------------------------------------------------------- GEMM int8 x f16
+
+@pytest.mark.parametrize("n,m,k", [(1, 1, 16), (45, 70, 48), (130, 257, 256), (300, 128, 3840)])
+def test_gemm_i8f16_integer_exact(n, m, k):
+    say(f"gemm i8f16 integer n={n} m={m} k={k}")
+    rng = np.random.default_rng(n * 3 + m + k)
+    x = rng.integers(-16, 17, (n, k)).astype(np.float16)
+    q = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    rs = (2.0 ** -rng.integers(0, 10, m)).astype(np.float32)
+    ref = O.linear_q8(x.astype(np.float64), q, rs)
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(q)], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
+                 row_scale=[to_dev(rs)])
+    assert np.array_equal(host(Y), ref)
+
+
+def test_gemm_i8f16_f16_output_and_items():
+    rng = np.random.default_rng(12)
+    n, d, f = 96, 256, 384
+    x = rng.normal(0, 1, (n, d)).astype(np.float16)
+    qs = [rng.integers(-127, 128, (f, d)).astype(np.int8) for _ in range(2)]
+    rss = [(0.002 * np.exp(0.25 * rng.normal(0, 1, f))).astype(np.float32) for _ in range(2)]
+    Y = torch.empty((n, 2 * f), dtype=torch.float16, device=DEV)
+    items = [(n, f, d, d, 2 * f, 0, 0, 0), (n, f, d, d, 2 * f, 1, 0, f)]
+    B.gemm_items(to_dev(x), Y, [to_dev(q) for q in qs], items, path=B.ENC_I8F16,
+                 row_scale=[to_dev(r) for r in rss], flags=B.ENC_Y_F16)
+    ref = np.concatenate([O.linear_q8(x.astype(np.float64), q, r) for q, r in zip(qs, rss)], 1)
+    ref16 = np.vectorize(O.round_f16)(ref)
+    assert row_rel_err(host(Y), ref16) <= TOL_I8F16
+
+
+@pytest.mark.parametrize("m,k", [(11520, 3840), (3840, 3840), (10240, 3840), (3840, 10240)])
+def test_gemm_i8f16_dit_shapes_sampled(m, k):
+    """The DiT's four GEMM shapes at 1056 rows; sampled rows vs the oracle."""
+    say(f"gemm i8f16 dit n=1056 m={m} k={k}")
+    rng = np.random.default_rng(m + k)
+    n = 1056
+    x = (rng.normal(0, 1, (n, k))).astype(np.float16)
+    q = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    rs = (0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32)
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(q)], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
+                 row_scale=[to_dev(rs)])
+    rows = np.array([0, 1, 127, 128, 511, 1000, 1023, 1024, 1055])
+    ref = O.linear_q8(x[rows].astype(np.float64), q, rs)
+    err = row_rel_err(host(Y)[rows], ref)
+    say(f"  err {err:.2e}")
+    assert err <= 1e-5
+
+
+# ------------------------------------------------------------------ attention
+
+def _panel(rng, rows, nq, nkv, hd, f16=False, qscale=1.0):
+    q = rng.normal(0, qscale, (rows, nq * hd))
+    k = rng.normal(0, 1, (rows, nkv * hd))
+    v = rng.normal(0, 1, (rows, nkv * hd))
+    p = np.concatenate([q, k, v], 1)
+    p = p.astype(np.float16 if f16 else np.float32)
+    return p
+
+
+def _split(p, nq, nkv, hd):
+    p = p.astype(np.float64)
+    return p[:, :nq * hd], p[:, nq * hd:(nq + nkv) * hd], p[:, (nq + nkv) * hd:]
+
+
+ATTN_CASES = [
+    ("single", [[(0, 64)]], 0),
+    ("ragged", [[(0, 1)], [(1, 37)], [(38, 130)], [(168, 300)], [(468, 5)]], 0),
+    ("window", [[(0, 700)], [(700, 33)], [(733, 260)]], 96),
+    ("window_big", [[(0, 1100)]], 512),
+    ("two_range", [[(0, 200), (420, 20)], [(200, 200), (440, 20)], [(400, 20)]], 0),
+]
+
+
+@pytest.mark.parametrize("name,items,window", ATTN_CASES)
+@pytest.mark.parametrize("hd,nq,nkv", [(64, 4, 4), (64, 4, 2), (128, 2, 1)])
+def test_attention_f32(name, items, window, hd, nq, nkv):
+    say(f"attention f32 {name} hd={hd} nq={nq} nkv={nkv} W={window}")
+    rows = max(r0 + n for rr in items for r0, n in rr)
+    rng = np.random.default_rng(hd + nq + rows)
+    p = _panel(rng, rows, nq, nkv, hd, qscale=0.5)
+    out = torch.full((rows, nq * hd), 0.0, dtype=torch.float32, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(to_dev(p), out, items, nq, nkv, hd, scale, window)
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, scale, window)
+    err = row_rel_err(host(out), ref)
+    say(f"  err {err:.2e}")
+    assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("name,items,window", ATTN_CASES)
+@pytest.mark.parametrize("hd,nq,nkv", [(128, 4, 4), (64, 4, 2)])
+def test_attention_f16(name, items, window, hd, nq, nkv):
+    say(f"attention f16 {name} hd={hd} nq={nq} nkv={nkv} W={window}")
+    rows = max(r0 + n for rr in items for r0, n in rr)
+    rng = np.random.default_rng(hd * 3 + nq + rows)
+    p = _panel(rng, rows, nq, nkv, hd, f16=True, qscale=0.5)
+    out = torch.zeros((rows, nq * hd), dtype=torch.float16, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(to_dev(p), out, items, nq, nkv, hd, scale, window, path=B.ENC_I8F16)
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = np.vectorize(O.round_f16)(O.attention(items, q, k, v, nq, nkv, hd, scale, window))
+    err = row_rel_err(host(out), ref)
+    say(f"  err {err:.2e}")
+    assert err <= TOL_I8F16
+
+
+@pytest.mark.parametrize("path", [B.ENC_F32, B.ENC_I8F16])
+@pytest.mark.parametrize("L,W", [(64, 0), (64, 5), (64, 31), (40, 39), (64, 1)])
+def test_attention_mask_probe(path, L, W):
+    """Q = 0, V = one-hot per key: o_i[j] > 0 exactly for visible keys j."""
+    hd = 64
+    f16 = path == B.ENC_I8F16
+    rng = np.random.default_rng(L + W)
+    k = rng.normal(0, 1, (L, hd))
+    v = np.eye(L, hd)
+    p = np.concatenate([np.zeros((L, hd)), k, v], 1).astype(np.float16 if f16 else np.float32)
+    out = torch.zeros((L, hd), dtype=torch.float16 if f16 else torch.float32, device=DEV)
+    B.attention_items(to_dev(p), out, [[(0, L)]], 1, 1, hd, 1.0, W, path=path)
+    got = host(out)[:, :L] > 0
+    i = np.arange(L)
+    pred = (np.abs(i[:, None] - i[None, :]) <= W) if W else np.ones((L, L), bool)
+    assert np.array_equal(got, pred)
+
+
+@pytest.mark.parametrize("path", [B.ENC_F32, B.ENC_I8F16])
+def test_attention_packed_equals_separate(path):
+    f16 = path == B.ENC_I8F16
+    nq, hd = 2, 128 if f16 else 64
+    items = [[(0, 150)], [(150, 37)], [(187, 300)]]
+    rows = 487
+    rng = np.random.default_rng(3)
+    p = _panel(rng, rows, nq, nq, hd, f16=f16)
+    dt = torch.float16 if f16 else torch.float32
+    out = torch.zeros((rows, nq * hd), dtype=dt, device=DEV)
+    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.1, 64, path=path)
+    for rr in items:
+        (r0, n), = rr
+        o1 = torch.zeros((n, nq * hd), dtype=dt, device=DEV)
+        B.attention_items(to_dev(p[r0:r0 + n]), o1, [[(0, n)]], nq, nq, hd, 0.1, 64, path=path)
+        assert torch.equal(o1, out[r0:r0 + n])
+
+
+# ------------------------------------------------------------------ row ops
+
+@pytest.mark.parametrize("d", [128, 512, 768, 3840])
+@pytest.mark.parametrize("f16", [False, True])
+def test_norms(d, f16):
+    rng = np.random.default_rng(d)
+    rows = 203
+    x = rng.normal(0, 3, (rows, d)).astype(np.float32)
+    w = rng.normal(1, 0.02, d).astype(np.float32)
+    b = rng.normal(0, 0.01, d).astype(np.float32)
+    dt = torch.float16 if f16 else torch.float32
+    tol = TOL_I8F16 if f16 else TOL_F32
+    Y = torch.empty((rows, d), dtype=dt, device=DEV)
+    B.rms_norm(to_dev(x), to_dev(w), 1e-6, Y, f16=f16)
+    assert row_rel_err(host(Y), O.rms_norm(x, w, 1e-6)) <= tol
+    B.layer_norm(to_dev(x), to_dev(w), to_dev(b), 1e-6, Y, f16=f16)
+    assert row_rel_err(host(Y), O.layer_norm(x, w, b, 1e-6)) <= tol
+
+
+@pytest.mark.parametrize("d", [512, 3840])
+@pytest.mark.parametrize("f16", [False, True])
+def test_add_norm_fused_equals_unfused(d, f16):
+    rng = np.random.default_rng(d + 1)
+    rows = 130
+    h = rng.normal(0, 3, (rows, d)).astype(np.float32)
+    t = rng.normal(0, 1, (rows, d)).astype(np.float32)
+    wp = rng.normal(1, 0.02, d).astype(np.float32)
+    wn = rng.normal(1, 0.02, d).astype(np.float32)
+    dt = torch.float16 if f16 else torch.float32
+    H, T = to_dev(h), to_dev(t)
+    A = torch.empty((rows, d), dtype=dt, device=DEV)
+    B.add_norm(H, T, to_dev(wp), 1e-6, to_dev(wn), A, f16=f16)
+    ref_h = h.astype(np.float64) + O.rms_norm(t, wp, 1e-6)
+    assert row_rel_err(host(H), ref_h) <= TOL_F32
+    assert row_rel_err(host(A), O.rms_norm(ref_h, wn, 1e-6)) <= (TOL_I8F16 if f16 else TOL_F32)
+    A2 = torch.empty_like(A)
+    B.rms_norm(H, to_dev(wn), 1e-6, A2, f16=f16)
+    assert torch.equal(A, A2)  # the fused next pre-norm gives the same bits
+
+
+@pytest.mark.parametrize("hd,sections,f16", [(64, 1, False), (64, 2, False), (128, 2, True),
+                                             (128, 1, True), (64, 1, True), (128, 2, False)])
+def test_qk_norm_rope(hd, sections, f16):
+    rng = np.random.default_rng(hd + sections)
+    rows, nq, nkv = 97, 3, 2
+    ld = (nq + 2 * nkv) * hd
+    p = rng.normal(0, 2, (rows, ld)).astype(np.float16 if f16 else np.float32)
+    qw = rng.normal(1, 0.02, hd).astype(np.float32)
+    kw = rng.normal(1, 0.02, hd).astype(np.float32)
+    pos = rng.integers(0, 2048, (rows, sections)).astype(np.int32)
+    cos, sin = B.rope_table(pos, hd, sections, 10000.0)
+    P = to_dev(p)
+    B.qk_norm_rope(P, nq, nkv, hd, to_dev(qw), to_dev(kw), 1e-6, to_dev(cos), to_dev(sin),
+                   sections, path=B.ENC_I8F16 if f16 else B.ENC_F32)
+    got = host(P)
+    pp = p.astype(np.float64)
+    refq = O.qk_norm_rope(pp[:, :nq * hd], nq, hd, qw, 1e-6, sections, pos, 10000.0)
+    refk = O.qk_norm_rope(pp[:, nq * hd:(nq + nkv) * hd], nkv, hd, kw, 1e-6, sections, pos, 10000.0)
+    tol = TOL_I8F16 if f16 else TOL_F32
+    assert row_rel_err(got[:, :nq * hd], refq) <= tol
+    assert row_rel_err(got[:, nq * hd:(nq + nkv) * hd], refk) <= tol
+    assert np.array_equal(got[:, (nq + nkv) * hd:], pp[:, (nq + nkv) * hd:])  # v untouched
+
+
+@pytest.mark.parametrize("kind,f16", [(B.ENC_ACT_GELU_TANH_GATED, False), (B.ENC_ACT_SWIGLU, True),
+                                      (B.ENC_ACT_SWIGLU, False)])
+def test_gated_act(kind, f16):
+    rng = np.random.default_rng(kind)
+    rows, ff = 77, 2048
+    gu = rng.normal(0, 2, (rows, 2 * ff)).astype(np.float32)
+    GU = to_dev(gu)
+    out = torch.empty((rows, ff), dtype=torch.float16 if f16 else torch.float32, device=DEV)
+    B.gated_act(GU[:, :ff], GU[:, ff:], out, kind, f16=f16)
+    g, u = gu[:, :ff].astype(np.float64), gu[:, ff:].astype(np.float64)
+    act = np.vectorize(O.gelu_tanh if kind == B.ENC_ACT_GELU_TANH_GATED else O.silu)
+    assert row_rel_err(host(out), act(g) * u) <= (TOL_I8F16 if f16 else TOL_F32)
+
+
+def test_mean_pool():
+    rng = np.random.default_rng(9)
+    rows, d = 300, 512
+    a = rng.normal(0, 1, (rows, d)).astype(np.float32)
+    items = [[(0, 100)], [(100, 1)], [(101, 150), (290, 10)], [(251, 39)]]
+    out = torch.empty((len(items), d), dtype=torch.float32, device=DEV)
+    B.mean_pool(to_dev(a), items, out)
+    ref = np.stack([np.concatenate([a[r0:r0 + n] for r0, n in rr]).astype(np.float64).mean(0)
+                    for rr in items])
+    assert row_rel_err(host(out), ref) <= TOL_F32

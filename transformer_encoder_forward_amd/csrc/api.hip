@@ -1,0 +1,841 @@
+// C ABI of libenc.so (include/enc.h): validation, planning and launch order.
+//
+// Every entry point validates its whole argument set on the host before it
+// enqueues anything (zimage.rs, cortiq-engine 0.7.6, module doc: an entry
+// returns before changing any output when it cannot honour the full contract;
+// egemma2.rs, cortiq-engine 0.8.39, `TextGpu::forward`: misshapen input is an
+// error).  Item tables go into kernel arguments; scratch comes from the
+// caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/enc.h"
+#include "kern.h"
+
+struct enc_ctx {
+    int device = 0;
+    std::string err;
+};
+
+namespace {
+
+using namespace enc;
+
+std::string g_create_err;
+
+struct Err {
+    enc_status st = ENC_OK;
+    std::string msg;
+    enc_status set(enc_status s, const char *fmt, ...) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        st = s;
+        msg = buf;
+        return s;
+    }
+};
+
+enc_status finish(enc_ctx *ctx, const Err &e) {
+    if (ctx) ctx->err = e.st == ENC_OK ? std::string() : e.msg;
+    return e.st;
+}
+
+void copy_msg(const Err &e, char *msg, size_t len) {
+    if (msg && len) {
+        size_t n = std::min(len - 1, e.msg.size());
+        memcpy(msg, e.msg.data(), n);
+        msg[n] = 0;
+    }
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+enc_status launch_status(Err &e, hipError_t h, const char *what) {
+    if (h != hipSuccess) return e.set(ENC_EDEVICE, "%s: %s", what, hipGetErrorString(h));
+    return ENC_OK;
+}
+
+// ---------------------------------------------------------------- gemm
+
+enc_status check_gemm(Err &e, const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n) {
+    if (!d || !items) return e.set(ENC_EINVAL, "gemm_items: null descriptor or items");
+    if (n < 1 || n > ENC_MAX_GEMM_ITEMS)
+        return e.set(ENC_EINVAL, "gemm_items: nitems %u outside 1..%d", n, ENC_MAX_GEMM_ITEMS);
+    if (d->path != ENC_F32 && d->path != ENC_I8F16)
+        return e.set(ENC_EINVAL, "gemm_items: unknown path %u", d->path);
+    if (!d->x || !d->y) return e.set(ENC_EINVAL, "gemm_items: null x or y");
+    if (d->flags & ~7u) return e.set(ENC_EINVAL, "gemm_items: unknown flags 0x%x", d->flags);
+    if ((d->flags & ENC_Y_F16) && (d->flags & ENC_Y_ACCUMULATE))
+        return e.set(ENC_EUNSUPPORTED, "gemm_items: accumulate needs an f32 output");
+    const bool i8 = d->path == ENC_I8F16;
+    const uint32_t kal = i8 ? 16 : 4, xal = i8 ? 8 : 4;
+    if (!aligned(d->x, 16) || !aligned(d->y, 4))
+        return e.set(ENC_EUNSUPPORTED, "gemm_items: x must be 16-byte aligned");
+    for (uint32_t i = 0; i < n; i++) {
+        const enc_gemm_item &it = items[i];
+        if (it.slot >= 4) return e.set(ENC_EINVAL, "gemm_items: item %u slot %u", i, it.slot);
+        if (!d->w[it.slot])
+            return e.set(ENC_EINVAL, "gemm_items: item %u: null weight in slot %u", i, it.slot);
+        if (!aligned(d->w[it.slot], 16))
+            return e.set(ENC_EUNSUPPORTED, "gemm_items: weight slot %u not 16-byte aligned", it.slot);
+        if (i8 && !d->row_scale[it.slot])
+            return e.set(ENC_EINVAL, "gemm_items: item %u: int8 weights need row scales", i);
+        if (it.m == 0 || it.k == 0)
+            return e.set(ENC_ESHAPE, "gemm_items: item %u has m=%u k=%u", i, it.m, it.k);
+        if (it.k % kal)
+            return e.set(ENC_EUNSUPPORTED, "gemm_items: item %u: k=%u not a multiple of %u", i, it.k,
+                         kal);
+        if (it.ldx < it.k || it.ldy < it.m)
+            return e.set(ENC_ESHAPE, "gemm_items: item %u: ldx %u < k %u or ldy %u < m %u", i,
+                         it.ldx, it.k, it.ldy, it.m);
+        if (it.ldx % xal || it.x_off % xal)
+            return e.set(ENC_EUNSUPPORTED, "gemm_items: item %u: ldx/x_off not multiples of %u", i,
+                         xal);
+        if ((uint64_t)it.n * it.ldx > (1ull << 40) || (uint64_t)it.n * it.ldy > (1ull << 40))
+            return e.set(ENC_ESHAPE, "gemm_items: item %u too large", i);
+    }
+    // Y regions of different items must not overlap (2-D rectangles when the
+    // strides agree, else address intervals).
+    for (uint32_t i = 0; i < n; i++)
+        for (uint32_t j = i + 1; j < n; j++) {
+            const enc_gemm_item &a = items[i], &b = items[j];
+            if (!a.n || !b.n) continue;
+            bool overlap;
+            if (a.ldy == b.ldy && a.y_off % a.ldy + a.m <= a.ldy && b.y_off % b.ldy + b.m <= b.ldy) {
+                const uint64_t ar = a.y_off / a.ldy, ac = a.y_off % a.ldy;
+                const uint64_t br = b.y_off / b.ldy, bc = b.y_off % b.ldy;
+                overlap = ar < br + b.n && br < ar + a.n && ac < bc + b.m && bc < ac + a.m;
+            } else {
+                const uint64_t a0 = a.y_off, a1 = a.y_off + (uint64_t)(a.n - 1) * a.ldy + a.m;
+                const uint64_t b0 = b.y_off, b1 = b.y_off + (uint64_t)(b.n - 1) * b.ldy + b.m;
+                overlap = a0 < b1 && b0 < a1;
+            }
+            if (overlap) return e.set(ENC_EINVAL, "gemm_items: items %u and %u write overlapping Y", i, j);
+        }
+    return ENC_OK;
+}
+
+void plan_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, GemmArgs &g) {
+    memset(&g, 0, sizeof g);
+    g.x = d->x;
+    g.y = d->y;
+    for (int s = 0; s < 4; s++) {
+        g.w[s] = d->w[s];
+        g.rs[s] = d->row_scale[s];
+        g.bias[s] = d->bias[s];
+    }
+    g.alpha = d->alpha;
+    g.flags = d->flags;
+    g.nitems = n;
+    uint32_t tiles = 0;
+    for (uint32_t i = 0; i < n; i++) {
+        GemmItemK &k = g.items[i];
+        k.n = items[i].n;
+        k.m = items[i].m;
+        k.k = items[i].k;
+        k.ldx = items[i].ldx;
+        k.ldy = items[i].ldy;
+        k.slot = items[i].slot;
+        k.x_off = items[i].x_off;
+        k.y_off = items[i].y_off;
+        k.tiles_m = (k.m + kGemmBN - 1) / kGemmBN;
+        k.tile0 = tiles;
+        tiles += k.tiles_m * ((k.n + kGemmBM - 1) / kGemmBM);
+    }
+    // unused trailing items never match (tile0 beyond every tile)
+    for (uint32_t i = n; i < (uint32_t)kMaxGemmItems; i++) g.items[i].tile0 = 0xffffffffu;
+    g.total_tiles = tiles;
+}
+
+hipError_t run_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, hipStream_t s) {
+    GemmArgs g;
+    plan_gemm(d, items, n, g);
+    return d->path == ENC_I8F16 ? launch_gemm_i8f16(g, s) : launch_gemm_f32(g, s);
+}
+
+// ----------------------------------------------------------- attention
+
+uint32_t item_len(const enc_item &it) { return it.r[0].n + (it.nr > 1 ? it.r[1].n : 0); }
+
+enc_status check_items(Err &e, const char *who, const enc_item *items, uint32_t n, uint32_t rows) {
+    if (!items && n) return e.set(ENC_EINVAL, "%s: null items", who);
+    std::vector<std::pair<uint64_t, uint64_t>> rr;
+    for (uint32_t i = 0; i < n; i++) {
+        const enc_item &it = items[i];
+        if (it.nr < 1 || it.nr > 2) return e.set(ENC_EINVAL, "%s: item %u has %u ranges", who, i, it.nr);
+        for (uint32_t r = 0; r < it.nr; r++) {
+            const uint64_t a = it.r[r].r0, b = a + it.r[r].n;
+            if (b > rows)
+                return e.set(ENC_EINVAL, "%s: item %u range [%llu,%llu) past %u rows", who, i,
+                             (unsigned long long)a, (unsigned long long)b, rows);
+            if (b > a) rr.push_back({a, b});
+        }
+    }
+    std::sort(rr.begin(), rr.end());
+    for (size_t i = 1; i < rr.size(); i++)
+        if (rr[i].first < rr[i - 1].second) return e.set(ENC_EINVAL, "%s: items overlap", who);
+    return ENC_OK;
+}
+
+enc_status check_attn(Err &e, const enc_attn_desc *d, const enc_item *items, uint32_t n) {
+    if (!d) return e.set(ENC_EINVAL, "attention_items: null descriptor");
+    if (d->path != ENC_F32 && d->path != ENC_I8F16)
+        return e.set(ENC_EINVAL, "attention_items: unknown path %u", d->path);
+    if (!d->qkv || !d->out) return e.set(ENC_EINVAL, "attention_items: null panel or output");
+    if (d->hd != 64 && d->hd != 128)
+        return e.set(ENC_EUNSUPPORTED, "attention_items: head dim %u (64 or 128)", d->hd);
+    if (!d->nq || !d->nkv || d->nq % d->nkv)
+        return e.set(ENC_EINVAL, "attention_items: nq %u not a multiple of nkv %u", d->nq, d->nkv);
+    if (d->ld % 8 || d->ldo % 8 || d->q_col % 8 || d->k_col % 8 || d->v_col % 8)
+        return e.set(ENC_EUNSUPPORTED, "attention_items: strides and column offsets must be multiples of 8");
+    if (d->q_col + d->nq * d->hd > d->ld || d->k_col + d->nkv * d->hd > d->ld ||
+        d->v_col + d->nkv * d->hd > d->ld)
+        return e.set(ENC_ESHAPE, "attention_items: q/k/v blocks do not fit the panel width %u", d->ld);
+    if (d->ldo < d->nq * d->hd)
+        return e.set(ENC_ESHAPE, "attention_items: ldo %u < nq*hd %u", d->ldo, d->nq * d->hd);
+    if (!aligned(d->qkv, 16) || !aligned(d->out, 16))
+        return e.set(ENC_EUNSUPPORTED, "attention_items: panel/output must be 16-byte aligned");
+    if (!(d->scale == d->scale) || std::isinf(d->scale))
+        return e.set(ENC_EINVAL, "attention_items: scale is not finite");
+    return check_items(e, "attention_items", items, n, d->rows);
+}
+
+hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t n, hipStream_t s) {
+    // longest items first (their tiles carry the most key blocks)
+    std::vector<uint32_t> order;
+    for (uint32_t i = 0; i < n; i++)
+        if (item_len(items[i])) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](uint32_t a, uint32_t b) { return item_len(items[a]) > item_len(items[b]); });
+    for (size_t c0 = 0; c0 < order.size(); c0 += kMaxAttnItems) {
+        AttnArgs a;
+        memset(&a, 0, sizeof a);
+        a.qkv = d->qkv;
+        a.out = d->out;
+        a.ld = d->ld;
+        a.ldo = d->ldo;
+        a.q_col = d->q_col;
+        a.k_col = d->k_col;
+        a.v_col = d->v_col;
+        a.nq = d->nq;
+        a.group = d->nq / d->nkv;
+        a.scale_log2 = (float)((double)d->scale * 1.4426950408889634);
+        a.window = d->window;
+        uint32_t tiles = 0, k = 0;
+        for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++, k++) {
+            const enc_item &it = items[order[c]];
+            a.items[k].r0a = it.r[0].r0;
+            a.items[k].na = it.r[0].n;
+            a.items[k].r0b = it.nr > 1 ? it.r[1].r0 : 0;
+            a.items[k].nb = it.nr > 1 ? it.r[1].n : 0;
+            a.items[k].tile0 = tiles;
+            tiles += (item_len(it) + kAttnQTile - 1) / kAttnQTile;
+        }
+        a.nitems = k;
+        a.ntiles = tiles;
+        hipError_t h = d->path == ENC_I8F16 ? launch_attn_f16(a, d->hd, s) : launch_attn_f32(a, d->hd, s);
+        if (h != hipSuccess) return h;
+    }
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------ row ops
+
+enc_status check_norm(Err &e, const char *who, const enc_norm_desc *d) {
+    if (!d) return e.set(ENC_EINVAL, "%s: null descriptor", who);
+    if (!d->x || !d->w || !d->y) return e.set(ENC_EINVAL, "%s: null x, w or y", who);
+    if (d->flags & ~1u) return e.set(ENC_EINVAL, "%s: unknown flags", who);
+    if (d->d == 0 || d->d % 4 || d->d > 4096)
+        return e.set(ENC_EUNSUPPORTED, "%s: width %u (multiple of 4, <= 4096)", who, d->d);
+    if (d->ldx < d->d || d->ldy < d->d) return e.set(ENC_ESHAPE, "%s: stride below width", who);
+    if (d->ldx % 4 || d->ldy % 4 || !aligned(d->x, 16) || !aligned(d->y, 16) || !aligned(d->w, 16) ||
+        (d->b && !aligned(d->b, 16)))
+        return e.set(ENC_EUNSUPPORTED, "%s: pointers 16-byte aligned, strides multiples of 4", who);
+    return ENC_OK;
+}
+
+enc_status check_add_norm(Err &e, const enc_add_norm_desc *d) {
+    if (!d) return e.set(ENC_EINVAL, "enc_add_norm: null descriptor");
+    if (!d->h || !d->t || !d->w_post) return e.set(ENC_EINVAL, "enc_add_norm: null h, t or w_post");
+    if (d->w_next && !d->a) return e.set(ENC_EINVAL, "enc_add_norm: w_next without an output");
+    if (d->flags & ~1u) return e.set(ENC_EINVAL, "enc_add_norm: unknown flags");
+    if (d->d == 0 || d->d % 4 || d->d > 4096)
+        return e.set(ENC_EUNSUPPORTED, "enc_add_norm: width %u (multiple of 4, <= 4096)", d->d);
+    if (!aligned(d->h, 16) || !aligned(d->t, 16) || !aligned(d->w_post, 16) ||
+        (d->w_next && (!aligned(d->w_next, 16) || !aligned(d->a, 16))))
+        return e.set(ENC_EUNSUPPORTED, "enc_add_norm: pointers must be 16-byte aligned");
+    return ENC_OK;
+}
+
+enc_status check_qk(Err &e, const enc_qk_desc *d) {
+    if (!d) return e.set(ENC_EINVAL, "enc_qk_norm_rope: null descriptor");
+    if (d->path != ENC_F32 && d->path != ENC_I8F16) return e.set(ENC_EINVAL, "enc_qk_norm_rope: path");
+    if (!d->panel || !d->q_norm_w || !d->k_norm_w)
+        return e.set(ENC_EINVAL, "enc_qk_norm_rope: null panel or norm weights");
+    if (d->hd != 64 && d->hd != 128)
+        return e.set(ENC_EUNSUPPORTED, "enc_qk_norm_rope: head dim %u (64 or 128)", d->hd);
+    if (d->sections > 2) return e.set(ENC_EINVAL, "enc_qk_norm_rope: sections %u", d->sections);
+    if (d->sections && (!d->cos || !d->sin)) return e.set(ENC_EINVAL, "enc_qk_norm_rope: null cos/sin");
+    if (d->q_col + d->nq * d->hd > d->ld || d->k_col + d->nkv * d->hd > d->ld)
+        return e.set(ENC_ESHAPE, "enc_qk_norm_rope: heads do not fit the panel width");
+    if ((uint64_t)d->rows * (d->nq + d->nkv) >= (1ull << 32) / 4)
+        return e.set(ENC_ESHAPE, "enc_qk_norm_rope: too many rows");
+    return ENC_OK;
+}
+
+enc_status check_act(Err &e, const enc_act_desc *d) {
+    if (!d) return e.set(ENC_EINVAL, "enc_gated_act: null descriptor");
+    if (d->kind != ENC_ACT_GELU_TANH_GATED && d->kind != ENC_ACT_SWIGLU)
+        return e.set(ENC_EINVAL, "enc_gated_act: unknown kind %u", d->kind);
+    if (!d->g || !d->u || !d->out) return e.set(ENC_EINVAL, "enc_gated_act: null pointer");
+    if (d->flags & ~1u) return e.set(ENC_EINVAL, "enc_gated_act: unknown flags");
+    if (d->ff % 4 || d->ldg % 4 || d->ldu % 4 || d->ldo % 4 || !aligned(d->g, 16) ||
+        !aligned(d->u, 16) || !aligned(d->out, 16))
+        return e.set(ENC_EUNSUPPORTED, "enc_gated_act: widths/strides multiples of 4, 16-byte pointers");
+    if (d->ldg < d->ff || d->ldu < d->ff || d->ldo < d->ff)
+        return e.set(ENC_ESHAPE, "enc_gated_act: stride below width");
+    return ENC_OK;
+}
+
+// ------------------------------------------------------------ model
+
+struct WsPlan {
+    size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0, total = 0;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsPlan plan_ws(const enc_model *M, uint32_t rows) {
+    WsPlan p;
+    size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0;
+    for (uint32_t l = 0; l < M->nlayers; l++) {
+        const enc_layer &L = M->layers[l];
+        const size_t esz = L.path == ENC_I8F16 ? 2 : 4;
+        a = std::max(a, (size_t)rows * L.d * esz);
+        panel = std::max(panel, (size_t)rows * (L.nq + 2 * L.nkv) * L.hd * esz);
+        att = std::max(att, (size_t)rows * L.nq * L.hd * esz);
+        t = std::max(t, (size_t)rows * L.d * 4);
+        if (L.mlp != ENC_MLP_GELU_TANH) gu = std::max(gu, (size_t)rows * 2 * L.ff * 4);
+        m = std::max(m, (size_t)rows * L.ff * (L.mlp == ENC_MLP_GELU_TANH ? 4 : esz));
+        h = std::max(h, (size_t)rows * L.d * 4);
+    }
+    size_t off = 0;
+    p.a = off; off += up256(a);
+    p.panel = off; off += up256(panel);
+    p.att = off; off += up256(att);
+    p.t = off; off += up256(t);
+    p.gu = off; off += up256(gu);
+    p.m = off; off += up256(m);
+    p.h = off; off += up256(h);  // residual stream (out holds it when final is NONE)
+    p.total = off;
+    return p;
+}
+
+enc_status check_layer(Err &e, uint32_t l, const enc_layer &L, const enc_layer &L0) {
+    if (L.block > 1 || L.path > 1 || L.mlp > 2)
+        return e.set(ENC_EINVAL, "layer %u: unknown block/path/mlp", l);
+    if (L.block != L0.block || L.path != L0.path || L.d != L0.d)
+        return e.set(ENC_EUNSUPPORTED, "layer %u: block kind, path and width must match layer 0", l);
+    if (L.d == 0 || L.d % 64 || L.d > 4096)
+        return e.set(ENC_EUNSUPPORTED, "layer %u: d %u (multiple of 64, <= 4096)", l, L.d);
+    if (L.ff == 0 || L.ff % 64) return e.set(ENC_EUNSUPPORTED, "layer %u: ff %u (multiple of 64)", l, L.ff);
+    if (L.hd != 64 && L.hd != 128) return e.set(ENC_EUNSUPPORTED, "layer %u: head dim %u", l, L.hd);
+    if (!L.nq || !L.nkv || L.nq % L.nkv) return e.set(ENC_EINVAL, "layer %u: nq %% nkv != 0", l);
+    if (L.rope_sections > 2) return e.set(ENC_EINVAL, "layer %u: rope_sections %u", l, L.rope_sections);
+    if (!(L.eps >= 0.0f) || !std::isfinite(L.attn_scale))
+        return e.set(ENC_EINVAL, "layer %u: eps/scale not finite", l);
+    if (!L.wq || !L.wk || !L.wv || !L.wo || !L.w_up || !L.w_down)
+        return e.set(ENC_EINVAL, "layer %u: null projection weight", l);
+    if (L.mlp != ENC_MLP_GELU_TANH && !L.w_gate) return e.set(ENC_EINVAL, "layer %u: gated MLP needs w_gate", l);
+    if (L.path == ENC_I8F16 &&
+        (!L.sq || !L.sk || !L.sv || !L.so || !L.s_up || !L.s_down || (L.w_gate && !L.s_gate)))
+        return e.set(ENC_EINVAL, "layer %u: int8 weights need row scales", l);
+    if (!L.norm1_w || !L.norm2_w) return e.set(ENC_EINVAL, "layer %u: null norm weights", l);
+    if (L.block == ENC_SANDWICH_RMS) {
+        if (!L.post_attn_w || !L.post_ff_w || !L.q_norm_w || !L.k_norm_w)
+            return e.set(ENC_EINVAL, "layer %u: sandwich block needs post/q/k norm weights", l);
+        if (L.mlp == ENC_MLP_GELU_TANH)
+            return e.set(ENC_EUNSUPPORTED, "layer %u: sandwich block takes a gated MLP", l);
+    } else {
+        if (L.path == ENC_I8F16) return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block runs the f32 path", l);
+        if (L.mlp != ENC_MLP_GELU_TANH)
+            return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block takes the GELU MLP", l);
+        if (L.rope_sections) return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block has no RoPE", l);
+    }
+    return ENC_OK;
+}
+
+enc_status check_model(Err &e, const enc_model *M, const enc_batch *B) {
+    if (!M || !B) return e.set(ENC_EINVAL, "null model or batch");
+    if (M->nlayers && !M->layers) return e.set(ENC_EINVAL, "null layers");
+    if (M->final_kind > 2) return e.set(ENC_EINVAL, "unknown final kind %u", M->final_kind);
+    if (M->final_kind != ENC_FINAL_NONE && !M->final_w) return e.set(ENC_EINVAL, "final norm needs final_w");
+    if (M->nlayers == 0 && M->final_kind != ENC_FINAL_NONE)
+        return e.set(ENC_EINVAL, "a final norm needs at least one layer (for the width)");
+    for (uint32_t l = 0; l < M->nlayers; l++)
+        if (check_layer(e, l, M->layers[l], M->layers[0]) != ENC_OK) return e.st;
+    if (!B->rows) return e.set(ENC_ESHAPE, "empty batch");
+    if (!B->nitems || !B->items) return e.set(ENC_EINVAL, "batch has no items");
+    if (check_items(e, "batch", B->items, B->nitems, B->rows) != ENC_OK) return e.st;
+    uint64_t covered = 0;
+    for (uint32_t i = 0; i < B->nitems; i++) covered += item_len(B->items[i]);
+    if (covered != B->rows) return e.set(ENC_ESHAPE, "items cover %llu of %u rows", (unsigned long long)covered, B->rows);
+    bool rope = false;
+    for (uint32_t l = 0; l < M->nlayers; l++) rope |= M->layers[l].rope_sections != 0;
+    if (rope && (!B->rope_cos || !B->rope_sin)) return e.set(ENC_EINVAL, "RoPE layers need cos/sin tables");
+    return ENC_OK;
+}
+
+struct Bufs {
+    void *a, *panel, *att;
+    float *t, *gu;
+    void *m;
+    float *h;
+};
+
+Bufs carve(void *ws, const WsPlan &p) {
+    char *b = (char *)ws;
+    return Bufs{b + p.a, b + p.panel, b + p.att, (float *)(b + p.t), (float *)(b + p.gu), b + p.m,
+                (float *)(b + p.h)};
+}
+
+#define TRY(expr)                                                                               \
+    do {                                                                                        \
+        hipError_t _h = (expr);                                                                 \
+        if (_h != hipSuccess) return _h;                                                        \
+    } while (0)
+
+hipError_t pre_norm(const enc_layer &L, uint32_t rows, const float *h, void *a, hipStream_t s) {
+    NormArgs n{rows, L.d, L.d, L.d, h, L.norm1_w, L.norm1_b, L.eps, a};
+    const bool f16 = L.path == ENC_I8F16;
+    return L.block == ENC_SANDWICH_RMS ? launch_rms_norm(n, f16, s) : launch_layer_norm(n, f16, s);
+}
+
+// One layer on h.  On entry, for the sandwich block, A holds rms(h; norm1)
+// (pre-LN computes its own LN).  On exit the last row op has written
+// A = rms(h; w_next) when w_next != NULL (sandwich only).
+hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Bufs &b,
+                     const float *w_next, hipStream_t s) {
+    const uint32_t rows = B->rows, d = L.d, hd = L.hd;
+    const uint32_t qw = L.nq * hd, kw = L.nkv * hd, ld = qw + 2 * kw;
+    const bool i8 = L.path == ENC_I8F16;
+    const bool sandwich = L.block == ENC_SANDWICH_RMS;
+    if (!sandwich) TRY(pre_norm(L, rows, h, b.a, s));
+
+    // q|k|v projections: one launch, three items
+    {
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.a;
+        g.y = b.panel;
+        g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
+        g.row_scale[0] = L.sq; g.row_scale[1] = L.sk; g.row_scale[2] = L.sv;
+        g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
+        g.alpha = 1.0f;
+        g.flags = i8 ? ENC_Y_F16 : 0;
+        enc_gemm_item it[3] = {{rows, qw, d, d, ld, 0, 0, 0},
+                               {rows, kw, d, d, ld, 1, 0, qw},
+                               {rows, kw, d, d, ld, 2, 0, qw + kw}};
+        TRY(run_gemm(&g, it, 3, s));
+    }
+    if (sandwich) {
+        QkArgs q{b.panel, rows, ld, 0, qw, L.nq, L.nkv, hd, L.rope_sections, L.q_norm_w, L.k_norm_w,
+                 L.eps, B->rope_cos, B->rope_sin};
+        TRY(launch_qk_norm_rope(q, i8, s));
+    }
+    {
+        enc_attn_desc a{};
+        a.path = L.path;
+        a.qkv = b.panel;
+        a.ld = ld;
+        a.q_col = 0;
+        a.k_col = qw;
+        a.v_col = qw + kw;
+        a.out = b.att;
+        a.ldo = qw;
+        a.nq = L.nq;
+        a.nkv = L.nkv;
+        a.hd = hd;
+        a.scale = L.attn_scale;
+        a.window = L.window;
+        a.rows = rows;
+        TRY(run_attention(&a, B->items, B->nitems, s));
+    }
+    // output projection: sandwich -> T; pre-LN -> h += att Wo^T + bo
+    {
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.att;
+        g.y = sandwich ? (void *)b.t : (void *)h;
+        g.w[0] = L.wo;
+        g.row_scale[0] = L.so;
+        g.bias[0] = L.bo;
+        g.alpha = 1.0f;
+        g.flags = sandwich ? 0 : ENC_Y_ACCUMULATE;
+        enc_gemm_item it{rows, d, qw, qw, d, 0, 0, 0};
+        TRY(run_gemm(&g, &it, 1, s));
+    }
+    if (sandwich) {
+        AddNormArgs an{rows, d, h, b.t, L.post_attn_w, L.norm2_w, L.eps, b.a};
+        TRY(launch_add_norm(an, i8, s));
+    } else {
+        NormArgs n{rows, d, d, d, h, L.norm2_w, L.norm2_b, L.eps, b.a};
+        TRY(launch_layer_norm(n, false, s));
+    }
+    // MLP
+    if (L.mlp == ENC_MLP_GELU_TANH) {
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.a;
+        g.y = b.m;
+        g.w[0] = L.w_up;
+        g.row_scale[0] = L.s_up;
+        g.bias[0] = L.b_up;
+        g.alpha = 1.0f;
+        g.flags = ENC_EPI_GELU_TANH;
+        enc_gemm_item it{rows, L.ff, d, d, L.ff, 0, 0, 0};
+        TRY(run_gemm(&g, &it, 1, s));
+    } else {
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.a;
+        g.y = b.gu;
+        g.w[0] = L.w_gate; g.w[1] = L.w_up;
+        g.row_scale[0] = L.s_gate; g.row_scale[1] = L.s_up;
+        g.alpha = 1.0f;
+        g.flags = 0;
+        enc_gemm_item it[2] = {{rows, L.ff, d, d, 2 * L.ff, 0, 0, 0},
+                               {rows, L.ff, d, d, 2 * L.ff, 1, 0, L.ff}};
+        TRY(run_gemm(&g, it, 2, s));
+        ActArgs ac{L.mlp == ENC_MLP_GELU_TANH_GATED ? (uint32_t)ENC_ACT_GELU_TANH_GATED
+                                                     : (uint32_t)ENC_ACT_SWIGLU,
+                   rows, L.ff, 2 * L.ff, 2 * L.ff, L.ff, b.gu, b.gu + L.ff, b.m};
+        TRY(launch_gated_act(ac, i8, s));
+    }
+    {
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.m;
+        g.y = sandwich ? (void *)b.t : (void *)h;
+        g.w[0] = L.w_down;
+        g.row_scale[0] = L.s_down;
+        g.bias[0] = L.b_down;
+        g.alpha = 1.0f;
+        g.flags = sandwich ? 0 : ENC_Y_ACCUMULATE;
+        enc_gemm_item it{rows, d, L.ff, L.ff, d, 0, 0, 0};
+        TRY(run_gemm(&g, &it, 1, s));
+    }
+    if (sandwich) {
+        AddNormArgs an{rows, d, h, b.t, L.post_ff_w, w_next, L.eps, b.a};
+        TRY(launch_add_norm(an, i8, s));
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+enc_status enc_create(int device, enc_ctx **out) {
+    if (!out) return ENC_EINVAL;
+    *out = nullptr;
+    hipDeviceProp_t p;
+    hipError_t h = hipGetDeviceProperties(&p, device);
+    if (h != hipSuccess) {
+        g_create_err = std::string("enc_create: ") + hipGetErrorString(h);
+        return ENC_EDEVICE;
+    }
+    if (!strstr(p.gcnArchName, "gfx950")) {
+        g_create_err = std::string("enc_create: device is ") + p.gcnArchName + ", the kernels are gfx950";
+        return ENC_EUNSUPPORTED;
+    }
+    enc_ctx *c = new enc_ctx;
+    c->device = device;
+    *out = c;
+    g_create_err.clear();
+    return ENC_OK;
+}
+
+void enc_destroy(enc_ctx *ctx) { delete ctx; }
+
+const char *enc_last_error(const enc_ctx *ctx) { return ctx ? ctx->err.c_str() : g_create_err.c_str(); }
+
+enc_status enc_check_gemm(const enc_gemm_desc *desc, const enc_gemm_item *items, uint32_t nitems,
+                          char *msg, size_t msg_len) {
+    Err e;
+    check_gemm(e, desc, items, nitems);
+    copy_msg(e, msg, msg_len);
+    return e.st;
+}
+
+enc_status enc_check_attention(const enc_attn_desc *desc, const enc_item *items, uint32_t nitems,
+                               char *msg, size_t msg_len) {
+    Err e;
+    check_attn(e, desc, items, nitems);
+    copy_msg(e, msg, msg_len);
+    return e.st;
+}
+
+enc_status enc_check_model(const enc_model *model, const enc_batch *batch, char *msg, size_t msg_len) {
+    Err e;
+    check_model(e, model, batch);
+    copy_msg(e, msg, msg_len);
+    return e.st;
+}
+
+enc_status gemm_items(enc_ctx *ctx, const enc_gemm_desc *desc, const enc_gemm_item *items,
+                      uint32_t nitems, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_gemm(e, desc, items, nitems) == ENC_OK)
+        launch_status(e, run_gemm(desc, items, nitems, (hipStream_t)stream), "gemm_items");
+    return finish(ctx, e);
+}
+
+enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_item *items,
+                           uint32_t nitems, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_attn(e, desc, items, nitems) == ENC_OK)
+        launch_status(e, run_attention(desc, items, nitems, (hipStream_t)stream), "attention_items");
+    return finish(ctx, e);
+}
+
+enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_norm(e, "enc_rms_norm", d) == ENC_OK) {
+        NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, nullptr, d->eps, d->y};
+        launch_status(e, launch_rms_norm(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_rms_norm");
+    }
+    return finish(ctx, e);
+}
+
+enc_status enc_layer_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_norm(e, "enc_layer_norm", d) == ENC_OK) {
+        NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, d->b, d->eps, d->y};
+        launch_status(e, launch_layer_norm(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_layer_norm");
+    }
+    return finish(ctx, e);
+}
+
+enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *d, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_add_norm(e, d) == ENC_OK) {
+        AddNormArgs a{d->rows, d->d, d->h, d->t, d->w_post, d->w_next, d->eps, d->a};
+        launch_status(e, launch_add_norm(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_add_norm");
+    }
+    return finish(ctx, e);
+}
+
+enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *d, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_qk(e, d) == ENC_OK) {
+        QkArgs q{d->panel, d->rows, d->ld, d->q_col, d->k_col, d->nq, d->nkv, d->hd, d->sections,
+                 d->q_norm_w, d->k_norm_w, d->eps, d->cos, d->sin};
+        launch_status(e, launch_qk_norm_rope(q, d->path == ENC_I8F16, (hipStream_t)stream),
+                      "enc_qk_norm_rope");
+    }
+    return finish(ctx, e);
+}
+
+enc_status enc_gated_act(enc_ctx *ctx, const enc_act_desc *d, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (check_act(e, d) == ENC_OK) {
+        ActArgs a{d->kind, d->rows, d->ff, d->ldg, d->ldu, d->ldo, d->g, d->u, d->out};
+        launch_status(e, launch_gated_act(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_gated_act");
+    }
+    return finish(ctx, e);
+}
+
+enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a, const enc_item *items,
+                         uint32_t nitems, float *out, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (!a || !out) {
+        e.set(ENC_EINVAL, "enc_mean_pool: null pointer");
+    } else if (nitems > (uint32_t)kMaxAttnItems) {
+        e.set(ENC_EUNSUPPORTED, "enc_mean_pool: at most %d items", kMaxAttnItems);
+    } else if (check_items(e, "enc_mean_pool", items, nitems, rows) == ENC_OK) {
+        PoolArgs p;
+        memset(&p, 0, sizeof p);
+        p.d = d;
+        p.nitems = nitems;
+        p.a = a;
+        p.out = out;
+        for (uint32_t i = 0; i < nitems; i++) {
+            p.items[i].r0a = items[i].r[0].r0;
+            p.items[i].na = items[i].r[0].n;
+            p.items[i].r0b = items[i].nr > 1 ? items[i].r[1].r0 : 0;
+            p.items[i].nb = items[i].nr > 1 ? items[i].r[1].n : 0;
+            if (!item_len(items[i])) {
+                e.set(ENC_EINVAL, "enc_mean_pool: item %u is empty", i);
+                return finish(ctx, e);
+            }
+        }
+        launch_status(e, launch_mean_pool(p, (hipStream_t)stream), "enc_mean_pool");
+    }
+    return finish(ctx, e);
+}
+
+size_t enc_workspace_bytes(const enc_model *model, uint32_t rows) {
+    if (!model || (model->nlayers && !model->layers)) return 0;
+    return plan_ws(model, rows).total;
+}
+
+enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_batch *batch, float *h,
+                                 void *ws, size_t ws_bytes, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (!layer || !h || !ws) {
+        e.set(ENC_EINVAL, "encoder_layer_forward: null layer, h or workspace");
+        return finish(ctx, e);
+    }
+    enc_model M{1, layer, ENC_FINAL_NONE, nullptr, nullptr, 0.0f};
+    if (check_model(e, &M, batch) != ENC_OK) return finish(ctx, e);
+    const WsPlan p = plan_ws(&M, batch->rows);
+    if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(h, 16)) {
+        e.set(ENC_EINVAL, "encoder_layer_forward: workspace needs %zu bytes, 256-byte aligned",
+              p.total);
+        return finish(ctx, e);
+    }
+    const Bufs b = carve(ws, p);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t hr = hipSuccess;
+    if (layer->block == ENC_SANDWICH_RMS) hr = pre_norm(*layer, batch->rows, h, b.a, s);
+    if (hr == hipSuccess) hr = run_layer(*layer, batch, h, b, nullptr, s);
+    launch_status(e, hr, "encoder_layer_forward");
+    return finish(ctx, e);
+}
+
+enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch *batch, const float *x,
+                           float *out, void *ws, size_t ws_bytes, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (!x || !out || !ws) {
+        e.set(ENC_EINVAL, "encoder_forward: null x, out or workspace");
+        return finish(ctx, e);
+    }
+    if (check_model(e, model, batch) != ENC_OK) return finish(ctx, e);
+    if (model->nlayers == 0) {
+        e.set(ENC_EINVAL, "encoder_forward: no layers");
+        return finish(ctx, e);
+    }
+    const WsPlan p = plan_ws(model, batch->rows);
+    if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(x, 16) || !aligned(out, 16)) {
+        e.set(ENC_EINVAL, "encoder_forward: workspace needs %zu bytes, 256-byte aligned", p.total);
+        return finish(ctx, e);
+    }
+    const enc_layer &L0 = model->layers[0];
+    const uint32_t rows = batch->rows, d = L0.d;
+    if (model->final_kind == ENC_FINAL_RMS_MEANPOOL && batch->nitems > (uint32_t)kMaxAttnItems) {
+        e.set(ENC_EUNSUPPORTED, "encoder_forward: mean pool takes at most %d items", kMaxAttnItems);
+        return finish(ctx, e);
+    }
+    const Bufs b = carve(ws, p);
+    hipStream_t s = (hipStream_t)stream;
+    float *h = model->final_kind == ENC_FINAL_NONE ? out : b.h;
+    hipError_t hr = hipSuccess;
+    if (h != x) hr = hipMemcpyAsync(h, x, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s);
+    if (hr == hipSuccess && L0.block == ENC_SANDWICH_RMS) hr = pre_norm(L0, rows, h, b.a, s);
+    for (uint32_t l = 0; l < model->nlayers && hr == hipSuccess; l++) {
+        const float *w_next = nullptr;
+        if (l + 1 < model->nlayers)
+            w_next = model->layers[l + 1].norm1_w;
+        else if (model->final_kind == ENC_FINAL_RMS_MEANPOOL && L0.block == ENC_SANDWICH_RMS &&
+                 L0.path == ENC_F32)
+            w_next = model->final_w;  // the final RMS (f32) written by the last row op
+        hr = run_layer(model->layers[l], batch, h, b, L0.block == ENC_SANDWICH_RMS ? w_next : nullptr, s);
+    }
+    if (hr == hipSuccess && model->final_kind == ENC_FINAL_LN) {
+        NormArgs n{rows, d, d, d, h, model->final_w, model->final_b, model->final_eps, out};
+        hr = launch_layer_norm(n, false, s);
+    } else if (hr == hipSuccess && model->final_kind == ENC_FINAL_RMS_MEANPOOL) {
+        float *a = (float *)b.t;  // f32 rows of rms(H; final_w)
+        if (L0.block == ENC_SANDWICH_RMS && L0.path == ENC_F32) {
+            a = (float *)b.a;
+        } else {
+            NormArgs n{rows, d, d, d, h, model->final_w, nullptr, model->final_eps, a};
+            hr = launch_rms_norm(n, false, s);
+        }
+        if (hr == hipSuccess) {
+            PoolArgs pa;
+            memset(&pa, 0, sizeof pa);
+            pa.d = d;
+            pa.nitems = batch->nitems;
+            pa.a = a;
+            pa.out = out;
+            for (uint32_t i = 0; i < batch->nitems; i++) {
+                const enc_item &it = batch->items[i];
+                pa.items[i].r0a = it.r[0].r0;
+                pa.items[i].na = it.r[0].n;
+                pa.items[i].r0b = it.nr > 1 ? it.r[1].r0 : 0;
+                pa.items[i].nb = it.nr > 1 ? it.r[1].n : 0;
+            }
+            hr = launch_mean_pool(pa, s);
+        }
+    }
+    launch_status(e, hr, "encoder_forward");
+    return finish(ctx, e);
+}
+
+// ------------------------------------------------------------ host helpers
+
+enc_status enc_positions(uint32_t rows, const enc_item *items, const uint32_t *grids, uint32_t nitems,
+                         uint32_t sections, int32_t *pos) {
+    if (!pos || (nitems && !items) || sections < 1 || sections > 2) return ENC_EINVAL;
+    if (sections == 2 && !grids) return ENC_EINVAL;
+    Err e;
+    if (check_items(e, "enc_positions", items, nitems, rows) != ENC_OK) return e.st;
+    for (uint32_t i = 0; i < nitems; i++) {
+        const enc_item &it = items[i];
+        const uint32_t L = item_len(it);
+        const uint32_t G = sections == 2 ? grids[i] : 0;
+        for (uint32_t t = 0; t < L; t++) {
+            const uint32_t row = t < it.r[0].n ? it.r[0].r0 + t : it.r[1].r0 + (t - it.r[0].n);
+            if (sections == 1) {
+                pos[row] = (int32_t)t;
+            } else if (t < G * G) {
+                pos[2 * row] = (int32_t)(t % G);      // column
+                pos[2 * row + 1] = (int32_t)(t / G);  // row
+            } else {
+                pos[2 * row] = pos[2 * row + 1] = (int32_t)(G + (t - G * G));
+            }
+        }
+    }
+    return ENC_OK;
+}
+
+enc_status enc_rope_table(uint32_t rows, uint32_t hd, uint32_t sections, const int32_t *pos, double base,
+                          float *cos_out, float *sin_out) {
+    if (!pos || !cos_out || !sin_out || sections < 1 || sections > 2 || hd == 0 || hd % (2 * sections))
+        return ENC_EINVAL;
+    const uint32_t S = hd / sections, half = S / 2;
+    for (uint32_t r = 0; r < rows; r++)
+        for (uint32_t s = 0; s < sections; s++)
+            for (uint32_t i = 0; i < half; i++) {
+                const double ang = (double)pos[(size_t)r * sections + s] * std::pow(base, -2.0 * i / S);
+                cos_out[(size_t)r * (hd / 2) + s * half + i] = (float)std::cos(ang);
+                sin_out[(size_t)r * (hd / 2) + s * half + i] = (float)std::sin(ang);
+            }
+    return ENC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Device-side helpers for gfx950 (CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace enc {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Butterfly sum over the 64 lanes; every lane ends with the same bits (each
+// lane adds the same pairs, only commuted).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// tanh(u) = sign(u) (1 - e) / (1 + e), e = exp(-2|u|): no cancellation for
+// small |u| beyond the f32 rounding of e.
+__device__ __forceinline__ float tanh_f32(float u) {
+    float e = __expf(-2.0f * fabsf(u));
+    float t = (1.0f - e) / (1.0f + e);
+    return copysignf(t, u);
+}
+
+// GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))).
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float c = 0.7978845608028654f;
+    return 0.5f * x * (1.0f + tanh_f32(c * (x + 0.044715f * x * x * x)));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
+__device__ __forceinline__ f32x4 ld4h(const _Float16 *p) {
+    f16x4 h = *reinterpret_cast<const f16x4 *>(p);
+    return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+__device__ __forceinline__ void st4h(_Float16 *p, f32x4 v) {
+    f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    *reinterpret_cast<f16x4 *>(p) = h;
+}
+
+}  // namespace enc

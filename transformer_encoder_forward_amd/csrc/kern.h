@@ -1,0 +1,104 @@
+// Kernel argument blocks and host launchers shared between the C-ABI layer
+// (api.hip) and the kernel translation units.  Plain structs passed by value
+// as kernel arguments; item tables live inside them.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace enc {
+
+constexpr int kMaxGemmItems = 4;
+constexpr int kMaxAttnItems = 64;  // per launch; longer lists are split
+
+struct GemmItemK {
+    uint32_t n, m, k, ldx, ldy, slot;
+    uint32_t tiles_m, tile0;  // tiles along m; first linear tile of this item
+    uint64_t x_off, y_off;
+};
+
+struct GemmArgs {
+    const void *x;
+    void *y;
+    const void *w[kMaxGemmItems];
+    const float *rs[kMaxGemmItems];
+    const float *bias[kMaxGemmItems];
+    float alpha;
+    uint32_t flags;
+    uint32_t nitems;
+    uint32_t total_tiles;
+    GemmItemK items[kMaxGemmItems];
+};
+
+struct AttnItemK {
+    uint32_t r0a, na, r0b, nb;  // ranges (nb = 0 for one range)
+    uint32_t tile0;             // first q-tile of this item in the launch
+};
+
+struct AttnArgs {
+    const void *qkv;
+    void *out;
+    uint32_t ld, ldo, q_col, k_col, v_col;
+    uint32_t nq, group;     // group = nq / nkv
+    float scale_log2;       // scale * log2(e): the softmax runs in base 2
+    uint32_t window;
+    uint32_t nitems, ntiles;
+    AttnItemK items[kMaxAttnItems];
+};
+
+struct NormArgs {
+    uint32_t rows, d, ldx, ldy;
+    const float *x;
+    const float *w;
+    const float *b;
+    float eps;
+    void *y;
+};
+
+struct AddNormArgs {
+    uint32_t rows, d;
+    float *h;
+    const float *t;
+    const float *w_post;
+    const float *w_next;
+    float eps;
+    void *a;
+};
+
+struct QkArgs {
+    void *panel;
+    uint32_t rows, ld, q_col, k_col, nq, nkv, hd, sections;
+    const float *qw, *kw;
+    float eps;
+    const float *cos, *sin;
+};
+
+struct ActArgs {
+    uint32_t kind, rows, ff, ldg, ldu, ldo;
+    const float *g, *u;
+    void *out;
+};
+
+struct PoolArgs {
+    uint32_t d, nitems;
+    const float *a;
+    float *out;
+    AttnItemK items[kMaxAttnItems];
+};
+
+// Launchers return hipGetLastError() after the launch (hipSuccess on success).
+hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s);
+hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s);
+hipError_t launch_rms_norm(const NormArgs &a, bool f16_out, hipStream_t s);
+hipError_t launch_layer_norm(const NormArgs &a, bool f16_out, hipStream_t s);
+hipError_t launch_add_norm(const AddNormArgs &a, bool f16_out, hipStream_t s);
+hipError_t launch_qk_norm_rope(const QkArgs &a, bool f16, hipStream_t s);
+hipError_t launch_gated_act(const ActArgs &a, bool f16_out, hipStream_t s);
+hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s);
+
+// Tile sizes the launchers and the planner agree on.
+constexpr int kGemmBM = 128, kGemmBN = 128;
+constexpr int kAttnQTile = 128;  // queries per attention block (4 waves x 32)
+
+}  // namespace enc

@@ -1,0 +1,109 @@
+"""Device-resident model and batch for encoder_forward: marshalling only.
+
+Weights are uploaded once as torch tensors on the device (PyTorch supplies the
+memory); the C structs hold their addresses.  RoPE positions and tables come
+from the library's host helpers (enc_positions, enc_rope_table).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import workloads as wl
+
+_F32_NAMES = ["bq", "bk", "bv", "bo", "b_up", "b_down", "norm1_w", "norm1_b", "norm2_w",
+              "norm2_b", "post_attn_w", "post_ff_w", "q_norm_w", "k_norm_w",
+              "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down"]
+_W_NAMES = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
+
+
+class DeviceModel:
+    def __init__(self, w: wl.Workload, device="cuda", layers=None):
+        self.cfg = cfg = w.cfg
+        self.keep = []
+        nl = len(w.layers) if layers is None else layers
+        self.nlayers = nl
+        self.layers = (B.Layer * max(1, nl))()
+        shapes = wl.weight_shapes(cfg)
+        for li in range(nl):
+            t = w.layers[li]
+            L = self.layers[li]
+            for n in B._LAYER_U32:
+                setattr(L, n, int(cfg[n]))
+            L.eps = cfg["eps"]
+            L.attn_scale = cfg["attn_scale"]
+            for n in _W_NAMES:
+                if n not in shapes:
+                    continue
+                if cfg["path"] == wl.PATH_I8F16 and n not in t:
+                    dev = wl.int8_weight_torch(w.seed, li, n, shapes[n], device)
+                else:
+                    arr = t[n]
+                    dev = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+                self.keep.append(dev)
+                setattr(L, n, dev.data_ptr())
+            for n in _F32_NAMES:
+                if t.get(n) is not None:
+                    dev = torch.from_numpy(np.ascontiguousarray(t[n], np.float32)).to(device)
+                    self.keep.append(dev)
+                    setattr(L, n, dev.data_ptr())
+        self.model = B.Model()
+        self.model.nlayers = nl
+        self.model.layers = self.layers
+        self.model.final_kind = int(cfg["final"])
+        self.model.final_eps = cfg["eps"]
+        for n in ("final_w", "final_b"):
+            a = getattr(w, n)
+            if a is not None:
+                dev = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device)
+                self.keep.append(dev)
+                setattr(self.model, n, dev.data_ptr())
+
+    def workspace_bytes(self, rows):
+        return B.lib().enc_workspace_bytes(C.byref(self.model), rows)
+
+    def workspace(self, rows, device="cuda"):
+        return torch.empty(self.workspace_bytes(rows), dtype=torch.uint8, device=device)
+
+
+class DeviceBatch:
+    def __init__(self, w: wl.Workload, device="cuda"):
+        cfg = w.cfg
+        self.rows = w.rows
+        self.items_py = w.items
+        self.items = B.make_items(w.items)
+        self.batch = B.Batch()
+        self.batch.rows = w.rows
+        self.batch.items = self.items
+        self.batch.nitems = len(w.items)
+        self.cos = self.sin = None
+        sec = cfg["rope_sections"]
+        if sec:
+            self.pos = B.positions(w.rows, w.items, w.grids, sec)
+            cos, sin = B.rope_table(self.pos, cfg["hd"], sec, cfg["rope_base"])
+            self.cos = torch.from_numpy(cos).to(device)
+            self.sin = torch.from_numpy(sin).to(device)
+            self.batch.rope_cos = self.cos.data_ptr()
+            self.batch.rope_sin = self.sin.data_ptr()
+
+
+def encoder_forward(model: DeviceModel, batch: DeviceBatch, x, out, ws, ctx=None, stream=None):
+    ctx = ctx or B.context()
+    ctx.check(B.lib().encoder_forward(ctx.h, C.byref(model.model), C.byref(batch.batch),
+                                      x.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                      B._stream(stream)))
+
+
+def encoder_layer_forward(model: DeviceModel, layer: int, batch: DeviceBatch, h, ws, ctx=None,
+                          stream=None):
+    ctx = ctx or B.context()
+    ctx.check(B.lib().encoder_layer_forward(ctx.h, C.byref(model.layers[layer]),
+                                            C.byref(batch.batch), h.data_ptr(), ws.data_ptr(),
+                                            ws.numel(), B._stream(stream)))
+
+
+def out_rows(w: wl.Workload):
+    return len(w.items) if w.cfg["final"] == wl.FINAL_RMS_MEANPOOL else w.rows
