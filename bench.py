@@ -1,0 +1,163 @@
+"""Throughput of the packed encoder forward on one MI355X.
+
+Default workload: the EmbeddingGemma-style text encoder (f32, 24 sandwich layers,
+d 512, 8x64 heads, qk-norm + 1-D RoPE, window 512, gated GELU 2048, 16 packed
+sequences of 32..2048 rows drawn from the seeded length stream, final RMS + mean
+pool), synthetic seeded inputs and random-init weights.  A step is one
+encoder_forward over the whole packed batch, inputs already resident in HBM.
+
+Prints one JSON line: value = encoder TFLOP/s, algorithmic (GEMM + attention)
+flops / wall time of K steps; the roofline of the dominant kernel class (the
+GEMMs) from per-launch HIP events recorded by the library on the stream the
+kernels run on; and the f64 oracle timed on the host cores on a bounded sample
+(one layer of the same batch).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"f32": 157.3, "i8f16": 2516.6}  # TFLOP/s, dense MFMA (FP32 / FP16), MI355X datasheet
+HBM_PEAK = 8000.0  # GB/s
+CPU_LAYERS = 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gemma_text_f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=None, help="(development) fewer layers")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by whole items with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_encoder_forward_amd import binding as B
+    from transformer_encoder_forward_amd import model as M
+    from transformer_encoder_forward_amd import workloads as wl
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    w = wl.make(args.workload, layers=args.layers, lazy_int8=True)
+    cfg = w.cfg
+    dm = M.DeviceModel(w, dev)
+    db = M.DeviceBatch(w, dev)
+    x = torch.from_numpy(w.x).to(dev)
+    out = torch.empty((M.out_rows(w), cfg["d"]), dtype=torch.float32, device=dev)
+    ws = dm.workspace(w.rows, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    print(f"[bench] {args.workload}: rows={w.rows} items={len(w.items)} layers={cfg['layers']} "
+          f"setup {setup_s:.1f}s", file=sys.stderr, flush=True)
+
+    ctx = B.context(0)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        M.encoder_forward(dm, db, x, out, ws, ctx=ctx, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    gflop = wl.gemm_flops(w)
+    aflop = wl.attn_flops(w)
+    tflops = (gflop + aflop) / (ms * 1e-3) / 1e12
+    dtype = "f32" if cfg["path"] == wl.PATH_F32 else "i8f16"
+    peak = PEAK[dtype]
+
+    # per-class GPU time from events the library records around each launch
+    B.prof_enable(True, ctx)
+    B.prof_read(ctx)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    prof = B.prof_read(ctx)
+    B.prof_enable(False, ctx)
+    g = prof["gemm"]
+    gemm_ms_launch = g["ms"] / max(1, g["launches"])
+    gemm_tf = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] else 0.0
+    classes = {k: dict(launches_per_step=v["launches"] / args.steps,
+                       ms_per_step=round(v["ms"] / args.steps, 4),
+                       tflops=round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["flops"] and v["ms"] else None,
+                       gbps=round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["bytes"] and v["ms"] else None)
+               for k, v in prof.items()}
+    print(f"[bench] {ms:.3f} ms/step, {tflops:.2f} TFLOP/s; classes {classes}", file=sys.stderr,
+          flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # a bounded sample of the same workload: its first CPU_LAYERS layers over the
+        # whole packed batch (about 10-20 s on 16 host cores)
+        nl = min(CPU_LAYERS, cfg["layers"])
+        sample = wl.make(args.workload, layers=nl, lazy_int8=False) if cfg["path"] == wl.PATH_F32 \
+            else None
+        if sample is not None:
+            sample.cfg["final"] = wl.FINAL_NONE
+            c0 = time.perf_counter()
+            oracle.forward(sample)
+            cdt = time.perf_counter() - c0
+            cfl = wl.gemm_flops(sample) + wl.attn_flops(sample)
+            cpu = {"value": round(cfl / cdt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
+                   "kind": "oracle",
+                   "sample": f"first {nl} of {cfg['layers']} layers over the same "
+                             f"{len(w.items)}-item batch ({w.rows} rows), "
+                             f"{cfl / 1e9:.1f} GFLOP in {cdt:.1f} s"}
+
+    res = {
+        "metric": "encoder TFLOP/s (GEMM+attn) and % of MI355X MFMA peak; tokens/s per layer",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+        "tokens_per_s_per_layer": round(w.rows / (ms * 1e-3 / cfg["layers"]), 1),
+        "config": {"workload": args.workload, "rows": w.rows, "items": len(w.items),
+                   "layers": cfg["layers"], "d": cfg["d"], "heads": f"{cfg['nq']}x{cfg['hd']}",
+                   "ff": cfg["ff"], "window": cfg["window"],
+                   "gemm_gflop": round(gflop / 1e9, 2), "attn_gflop": round(aflop / 1e9, 2),
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "gemm_f32_kernel" if dtype == "f32" else "gemm_i8f16_kernel",
+                     "bound": "mfma", "achieved": round(gemm_tf, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / peak, 4), "traffic": None,
+                     "launches_per_step": g["launches"] / args.steps,
+                     "avg_launch_ms": round(gemm_ms_launch, 5)},
+        "classes": classes,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -297,6 +297,27 @@ ENC_API enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const e
                            const float *x, float *out, void *ws, size_t ws_bytes,
                            enc_stream stream);
 
+/* --------------------------------------------------------- per-class timing */
+
+/* Launch classes ([EG] `Rec` and [ZI] `Rec`: one GPU time per op class under a
+ * profiling knob).  GEMM = gemm_items launches (also inside the layer/model
+ * calls), ATTN = attention_items launches, ROWS = every row op. */
+typedef enum { ENC_CLASS_GEMM = 0, ENC_CLASS_ATTN = 1, ENC_CLASS_ROWS = 2, ENC_NCLASS = 3 } enc_class;
+typedef struct {
+    uint64_t launches;
+    double ms;     /* summed GPU time between each launch's bracketing events */
+    double flops;  /* algorithmic: 2 n m k per GEMM item; 4 hd per visible (query, key) pair per head */
+    double bytes;  /* algorithmic HBM bytes: each row op's inputs read once and outputs written once */
+} enc_prof_stat;
+
+/* With profiling on, every kernel launch enqueued through ctx is bracketed by
+ * two hipEvent records on its stream (the events are created once and reused;
+ * no device memory is allocated).  enc_prof_read waits for the recorded events,
+ * writes the per-class totals since the previous read into stats[ENC_NCLASS]
+ * and starts a new interval.  Not for use under stream capture. */
+ENC_API enc_status enc_prof_enable(enc_ctx *ctx, int on);
+ENC_API enc_status enc_prof_read(enc_ctx *ctx, enc_prof_stat *stats);
+
 /* ---------------------------------------------------- host-only helpers */
 /* No HIP calls: usable and testable without a GPU. */
 

@@ -82,6 +82,8 @@ _I8 = C.POINTER(C.c_int8)
 
 
 def _setup(L):
+    L.or_threads.argtypes = []
+    L.or_threads.restype = C.c_int
     L.or_round_f16.argtypes = [C.c_double]
     L.or_round_f16.restype = C.c_double
     L.or_gelu_tanh.argtypes = [C.c_double]
@@ -128,6 +130,10 @@ def _items(items, grids=None):
 
 
 # --------------------------------------------------------------------------- ops
+
+def threads() -> int:
+    return lib().or_threads()
+
 
 def round_f16(x: float) -> float:
     return lib().or_round_f16(float(x))

@@ -14,11 +14,18 @@
  * Readings where the pages are silent are listed next to the code they shape.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define OR_API __attribute__((visibility("default")))
+
+/* OpenMP threads the oracle's parallel loops use. */
+OR_API int or_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ------------------------------------------------------------------ binary16 */
 

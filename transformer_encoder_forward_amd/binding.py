@@ -27,7 +27,8 @@ EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attenti
            "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
            "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
-           "enc_rope_table"]
+           "enc_rope_table", "enc_prof_enable", "enc_prof_read"]
+CLASS_NAMES = ["gemm", "attn", "rows"]
 
 
 class EncError(RuntimeError):
@@ -106,6 +107,11 @@ class Layer(C.Structure):
                 + [(n, C.c_void_p) for n in _LAYER_PTRS])
 
 
+class ProfStat(C.Structure):
+    _fields_ = [("launches", C.c_uint64), ("ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
 class Batch(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("items", C.POINTER(Item)), ("nitems", C.c_uint32),
                 ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p)]
@@ -158,10 +164,12 @@ def lib():
     L.enc_check_model.argtypes = [C.POINTER(Model), C.POINTER(Batch), C.c_char_p, C.c_size_t]
     L.enc_positions.argtypes = [C.c_uint32, C.POINTER(Item), P, C.c_uint32, C.c_uint32, P]
     L.enc_rope_table.argtypes = [C.c_uint32, C.c_uint32, C.c_uint32, P, C.c_double, P, P]
+    L.enc_prof_enable.argtypes = [P, C.c_int]
+    L.enc_prof_read.argtypes = [P, C.POINTER(ProfStat)]
     for f in ("gemm_items", "attention_items", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
               "enc_qk_norm_rope", "enc_gated_act", "enc_mean_pool", "encoder_layer_forward",
               "encoder_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
-              "enc_positions", "enc_rope_table"):
+              "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read"):
         getattr(L, f).restype = S
     _lib = L
     return L
@@ -319,6 +327,20 @@ def gated_act(g, u, out, kind, f16=False, ctx=None, stream=None):
     d.out, d.ldo = _ptr(out), out.stride(0)
     d.flags = ENC_Y_F16 if f16 else 0
     ctx.check(lib().enc_gated_act(ctx.h, C.byref(d), _stream(stream)))
+
+
+def prof_enable(on=True, ctx=None):
+    ctx = ctx or context()
+    ctx.check(lib().enc_prof_enable(ctx.h, 1 if on else 0))
+
+
+def prof_read(ctx=None):
+    """{class: dict(launches, ms, flops, bytes)} since the previous read."""
+    ctx = ctx or context()
+    st = (ProfStat * 3)()
+    ctx.check(lib().enc_prof_read(ctx.h, st))
+    return {CLASS_NAMES[i]: dict(launches=st[i].launches, ms=st[i].ms, flops=st[i].flops,
+                                 bytes=st[i].bytes) for i in range(3)}
 
 
 def mean_pool(a, items, out, ctx=None, stream=None):

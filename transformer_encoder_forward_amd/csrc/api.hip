@@ -19,14 +19,55 @@
 #include "../../include/enc.h"
 #include "kern.h"
 
+struct ProfRec {
+    int cls;
+    size_t ev;  // index of the event pair in the pool
+    double flops, bytes;
+};
+
 struct enc_ctx {
     int device = 0;
     std::string err;
+    bool prof = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+    std::vector<ProfRec> recs;
 };
 
 namespace {
 
 using namespace enc;
+
+// The ctx whose entry point is running on this thread (profiling hooks).
+thread_local enc_ctx *t_ctx = nullptr;
+
+struct CtxScope {
+    explicit CtxScope(enc_ctx *c) { t_ctx = c; }
+    ~CtxScope() { t_ctx = nullptr; }
+};
+
+// Brackets one launch with events on its stream when profiling is on.
+template <class F>
+hipError_t prof_launch(int cls, hipStream_t s, double flops, double bytes, F &&launch) {
+    enc_ctx *c = t_ctx;
+    if (!c || !c->prof) return launch();
+    const size_t i = c->recs.size();
+    if (i == c->pool.size()) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return hipErrorOutOfMemory;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return hipErrorOutOfMemory;
+        }
+        c->pool.push_back({a, b});
+    }
+    hipError_t h = hipEventRecord(c->pool[i].first, s);
+    if (h != hipSuccess) return h;
+    h = launch();
+    if (h != hipSuccess) return h;
+    h = hipEventRecord(c->pool[i].second, s);
+    if (h == hipSuccess) c->recs.push_back({cls, i, flops, bytes});
+    return h;
+}
 
 std::string g_create_err;
 
@@ -160,12 +201,24 @@ void plan_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, G
 hipError_t run_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, hipStream_t s) {
     GemmArgs g;
     plan_gemm(d, items, n, g);
-    return d->path == ENC_I8F16 ? launch_gemm_i8f16(g, s) : launch_gemm_f32(g, s);
+    double flops = 0;
+    for (uint32_t i = 0; i < n; i++) flops += 2.0 * items[i].n * items[i].m * items[i].k;
+    return prof_launch(ENC_CLASS_GEMM, s, flops, 0.0, [&] {
+        return d->path == ENC_I8F16 ? launch_gemm_i8f16(g, s) : launch_gemm_f32(g, s);
+    });
 }
 
 // ----------------------------------------------------------- attention
 
 uint32_t item_len(const enc_item &it) { return it.r[0].n + (it.nr > 1 ? it.r[1].n : 0); }
+
+// (query, key) pairs the mask lets through in an item of L rows: L^2 when
+// full, else L(2W+1) - W(W+1) (each edge row loses the part of its band that
+// falls outside the item).
+double visible_pairs(uint32_t L, uint32_t W) {
+    if (W == 0 || W + 1 >= L) return (double)L * L;
+    return (double)L * (2.0 * W + 1.0) - (double)W * (W + 1.0);
+}
 
 enc_status check_items(Err &e, const char *who, const enc_item *items, uint32_t n, uint32_t rows) {
     if (!items && n) return e.set(ENC_EINVAL, "%s: null items", who);
@@ -243,7 +296,12 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         }
         a.nitems = k;
         a.ntiles = tiles;
-        hipError_t h = d->path == ENC_I8F16 ? launch_attn_f16(a, d->hd, s) : launch_attn_f32(a, d->hd, s);
+        double pairs = 0;
+        for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++)
+            pairs += visible_pairs(item_len(items[order[c]]), d->window);
+        hipError_t h = prof_launch(ENC_CLASS_ATTN, s, 4.0 * d->hd * d->nq * pairs, 0.0, [&] {
+            return d->path == ENC_I8F16 ? launch_attn_f16(a, d->hd, s) : launch_attn_f32(a, d->hd, s);
+        });
         if (h != hipSuccess) return h;
     }
     return hipSuccess;
@@ -308,6 +366,34 @@ enc_status check_act(Err &e, const enc_act_desc *d) {
 }
 
 // ------------------------------------------------------------ model
+
+// Row-op launches with their algorithmic HBM bytes (inputs read once, outputs
+// written once, per-channel weights once).
+hipError_t rows_rms(const NormArgs &n, bool f16, hipStream_t s) {
+    const double b = (double)n.rows * n.d * (4 + (f16 ? 2 : 4)) + 4.0 * n.d;
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_rms_norm(n, f16, s); });
+}
+hipError_t rows_ln(const NormArgs &n, bool f16, hipStream_t s) {
+    const double b = (double)n.rows * n.d * (4 + (f16 ? 2 : 4)) + 8.0 * n.d;
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_layer_norm(n, f16, s); });
+}
+hipError_t rows_add_norm(const AddNormArgs &a, bool f16, hipStream_t s) {
+    const double b = (double)a.rows * a.d * (12 + (a.w_next ? (f16 ? 2 : 4) : 0)) + 8.0 * a.d;
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_add_norm(a, f16, s); });
+}
+hipError_t rows_qk(const QkArgs &q, bool f16, hipStream_t s) {
+    const double b = (double)q.rows * (q.nq + q.nkv) * q.hd * (f16 ? 4 : 8) +
+                     (q.sections ? (double)q.rows * q.hd * 4 : 0.0) + 8.0 * q.hd;
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_qk_norm_rope(q, f16, s); });
+}
+hipError_t rows_act(const ActArgs &a, bool f16, hipStream_t s) {
+    const double b = (double)a.rows * a.ff * (8 + (f16 ? 2 : 4));
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_gated_act(a, f16, s); });
+}
+hipError_t rows_pool(const PoolArgs &p, uint32_t rows, hipStream_t s) {
+    const double b = (double)rows * p.d * 4 + (double)p.nitems * p.d * 4;
+    return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_mean_pool(p, s); });
+}
 
 struct WsPlan {
     size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0, total = 0;
@@ -418,7 +504,7 @@ Bufs carve(void *ws, const WsPlan &p) {
 hipError_t pre_norm(const enc_layer &L, uint32_t rows, const float *h, void *a, hipStream_t s) {
     NormArgs n{rows, L.d, L.d, L.d, h, L.norm1_w, L.norm1_b, L.eps, a};
     const bool f16 = L.path == ENC_I8F16;
-    return L.block == ENC_SANDWICH_RMS ? launch_rms_norm(n, f16, s) : launch_layer_norm(n, f16, s);
+    return L.block == ENC_SANDWICH_RMS ? rows_rms(n, f16, s) : rows_ln(n, f16, s);
 }
 
 // One layer on h.  On entry, for the sandwich block, A holds rms(h; norm1)
@@ -451,7 +537,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
     if (sandwich) {
         QkArgs q{b.panel, rows, ld, 0, qw, L.nq, L.nkv, hd, L.rope_sections, L.q_norm_w, L.k_norm_w,
                  L.eps, B->rope_cos, B->rope_sin};
-        TRY(launch_qk_norm_rope(q, i8, s));
+        TRY(rows_qk(q, i8, s));
     }
     {
         enc_attn_desc a{};
@@ -487,10 +573,10 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
     }
     if (sandwich) {
         AddNormArgs an{rows, d, h, b.t, L.post_attn_w, L.norm2_w, L.eps, b.a};
-        TRY(launch_add_norm(an, i8, s));
+        TRY(rows_add_norm(an, i8, s));
     } else {
         NormArgs n{rows, d, d, d, h, L.norm2_w, L.norm2_b, L.eps, b.a};
-        TRY(launch_layer_norm(n, false, s));
+        TRY(rows_ln(n, false, s));
     }
     // MLP
     if (L.mlp == ENC_MLP_GELU_TANH) {
@@ -520,7 +606,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
         ActArgs ac{L.mlp == ENC_MLP_GELU_TANH_GATED ? (uint32_t)ENC_ACT_GELU_TANH_GATED
                                                      : (uint32_t)ENC_ACT_SWIGLU,
                    rows, L.ff, 2 * L.ff, 2 * L.ff, L.ff, b.gu, b.gu + L.ff, b.m};
-        TRY(launch_gated_act(ac, i8, s));
+        TRY(rows_act(ac, i8, s));
     }
     {
         enc_gemm_desc g{};
@@ -537,7 +623,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
     }
     if (sandwich) {
         AddNormArgs an{rows, d, h, b.t, L.post_ff_w, w_next, L.eps, b.a};
-        TRY(launch_add_norm(an, i8, s));
+        TRY(rows_add_norm(an, i8, s));
     }
     return hipSuccess;
 }
@@ -568,7 +654,44 @@ enc_status enc_create(int device, enc_ctx **out) {
     return ENC_OK;
 }
 
-void enc_destroy(enc_ctx *ctx) { delete ctx; }
+void enc_destroy(enc_ctx *ctx) {
+    if (!ctx) return;
+    for (auto &p : ctx->pool) {
+        (void)hipEventDestroy(p.first);
+        (void)hipEventDestroy(p.second);
+    }
+    delete ctx;
+}
+
+enc_status enc_prof_enable(enc_ctx *ctx, int on) {
+    if (!ctx) return ENC_EINVAL;
+    ctx->prof = on != 0;
+    ctx->err.clear();
+    return ENC_OK;
+}
+
+enc_status enc_prof_read(enc_ctx *ctx, enc_prof_stat *stats) {
+    if (!ctx || !stats) return ENC_EINVAL;
+    Err e;
+    for (int c = 0; c < ENC_NCLASS; c++) stats[c] = enc_prof_stat{0, 0.0, 0.0, 0.0};
+    for (const ProfRec &r : ctx->recs) {
+        const auto &ev = ctx->pool[r.ev];
+        float ms = 0.0f;
+        hipError_t h = hipEventSynchronize(ev.second);
+        if (h == hipSuccess) h = hipEventElapsedTime(&ms, ev.first, ev.second);
+        if (h != hipSuccess) {
+            e.set(ENC_EDEVICE, "enc_prof_read: %s", hipGetErrorString(h));
+            break;
+        }
+        enc_prof_stat &st = stats[r.cls];
+        st.launches++;
+        st.ms += ms;
+        st.flops += r.flops;
+        st.bytes += r.bytes;
+    }
+    ctx->recs.clear();
+    return finish(ctx, e);
+}
 
 const char *enc_last_error(const enc_ctx *ctx) { return ctx ? ctx->err.c_str() : g_create_err.c_str(); }
 
@@ -599,6 +722,7 @@ enc_status gemm_items(enc_ctx *ctx, const enc_gemm_desc *desc, const enc_gemm_it
                       uint32_t nitems, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_gemm(e, desc, items, nitems) == ENC_OK)
         launch_status(e, run_gemm(desc, items, nitems, (hipStream_t)stream), "gemm_items");
     return finish(ctx, e);
@@ -608,6 +732,7 @@ enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_it
                            uint32_t nitems, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_attn(e, desc, items, nitems) == ENC_OK)
         launch_status(e, run_attention(desc, items, nitems, (hipStream_t)stream), "attention_items");
     return finish(ctx, e);
@@ -616,9 +741,10 @@ enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_it
 enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_norm(e, "enc_rms_norm", d) == ENC_OK) {
         NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, nullptr, d->eps, d->y};
-        launch_status(e, launch_rms_norm(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_rms_norm");
+        launch_status(e, rows_rms(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_rms_norm");
     }
     return finish(ctx, e);
 }
@@ -626,9 +752,10 @@ enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream)
 enc_status enc_layer_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_norm(e, "enc_layer_norm", d) == ENC_OK) {
         NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, d->b, d->eps, d->y};
-        launch_status(e, launch_layer_norm(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_layer_norm");
+        launch_status(e, rows_ln(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_layer_norm");
     }
     return finish(ctx, e);
 }
@@ -636,9 +763,10 @@ enc_status enc_layer_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream strea
 enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *d, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_add_norm(e, d) == ENC_OK) {
         AddNormArgs a{d->rows, d->d, d->h, d->t, d->w_post, d->w_next, d->eps, d->a};
-        launch_status(e, launch_add_norm(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_add_norm");
+        launch_status(e, rows_add_norm(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_add_norm");
     }
     return finish(ctx, e);
 }
@@ -646,11 +774,11 @@ enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *d, enc_stream str
 enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *d, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_qk(e, d) == ENC_OK) {
         QkArgs q{d->panel, d->rows, d->ld, d->q_col, d->k_col, d->nq, d->nkv, d->hd, d->sections,
                  d->q_norm_w, d->k_norm_w, d->eps, d->cos, d->sin};
-        launch_status(e, launch_qk_norm_rope(q, d->path == ENC_I8F16, (hipStream_t)stream),
-                      "enc_qk_norm_rope");
+        launch_status(e, rows_qk(q, d->path == ENC_I8F16, (hipStream_t)stream), "enc_qk_norm_rope");
     }
     return finish(ctx, e);
 }
@@ -658,9 +786,10 @@ enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *d, enc_stream strea
 enc_status enc_gated_act(enc_ctx *ctx, const enc_act_desc *d, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (check_act(e, d) == ENC_OK) {
         ActArgs a{d->kind, d->rows, d->ff, d->ldg, d->ldu, d->ldo, d->g, d->u, d->out};
-        launch_status(e, launch_gated_act(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_gated_act");
+        launch_status(e, rows_act(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_gated_act");
     }
     return finish(ctx, e);
 }
@@ -669,6 +798,7 @@ enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a
                          uint32_t nitems, float *out, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (!a || !out) {
         e.set(ENC_EINVAL, "enc_mean_pool: null pointer");
     } else if (nitems > (uint32_t)kMaxAttnItems) {
@@ -690,7 +820,7 @@ enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a
                 return finish(ctx, e);
             }
         }
-        launch_status(e, launch_mean_pool(p, (hipStream_t)stream), "enc_mean_pool");
+        launch_status(e, rows_pool(p, rows, (hipStream_t)stream), "enc_mean_pool");
     }
     return finish(ctx, e);
 }
@@ -704,6 +834,7 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
                                  void *ws, size_t ws_bytes, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (!layer || !h || !ws) {
         e.set(ENC_EINVAL, "encoder_layer_forward: null layer, h or workspace");
         return finish(ctx, e);
@@ -729,6 +860,7 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
                            float *out, void *ws, size_t ws_bytes, enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
     if (!x || !out || !ws) {
         e.set(ENC_EINVAL, "encoder_forward: null x, out or workspace");
         return finish(ctx, e);
@@ -766,14 +898,14 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
     }
     if (hr == hipSuccess && model->final_kind == ENC_FINAL_LN) {
         NormArgs n{rows, d, d, d, h, model->final_w, model->final_b, model->final_eps, out};
-        hr = launch_layer_norm(n, false, s);
+        hr = rows_ln(n, false, s);
     } else if (hr == hipSuccess && model->final_kind == ENC_FINAL_RMS_MEANPOOL) {
         float *a = (float *)b.t;  // f32 rows of rms(H; final_w)
         if (L0.block == ENC_SANDWICH_RMS && L0.path == ENC_F32) {
             a = (float *)b.a;
         } else {
             NormArgs n{rows, d, d, d, h, model->final_w, nullptr, model->final_eps, a};
-            hr = launch_rms_norm(n, false, s);
+            hr = rows_rms(n, false, s);
         }
         if (hr == hipSuccess) {
             PoolArgs pa;
@@ -789,7 +921,7 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
                 pa.items[i].r0b = it.nr > 1 ? it.r[1].r0 : 0;
                 pa.items[i].nb = it.nr > 1 ? it.r[1].n : 0;
             }
-            hr = launch_mean_pool(pa, s);
+            hr = rows_pool(pa, rows, s);
         }
     }
     launch_status(e, hr, "encoder_forward");
