@@ -10,7 +10,7 @@ Prints one JSON line: value = encoder TFLOP/s, algorithmic (GEMM + attention)
 flops / wall time of K steps; the roofline of the dominant kernel class (the
 GEMMs) from per-launch HIP events recorded by the library on the stream the
 kernels run on; and the f64 oracle timed on the host cores on a bounded sample
-(one layer of the same batch).
+(the first layers of the same batch).
 """
 import argparse
 import json
@@ -37,7 +37,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by whole items with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path would shard by whole items with no exchange step)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
