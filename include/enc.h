@@ -56,9 +56,11 @@ typedef enum { ENC_F32 = 0, ENC_I8F16 = 1 } enc_path;
 
 /* Output flags of GEMM and row-op descriptors. */
 enum {
-    ENC_Y_F16 = 1u,         /* write f16 instead of f32 */
-    ENC_Y_ACCUMULATE = 2u,  /* Y += result (residual add fused into the epilogue) */
-    ENC_EPI_GELU_TANH = 4u  /* Y = gelu_tanh(result) (before any accumulate) */
+    ENC_Y_F16 = 1u,              /* write f16 instead of f32 */
+    ENC_Y_ACCUMULATE = 2u,       /* Y += result (residual add fused into the epilogue) */
+    ENC_EPI_GELU_TANH = 4u,      /* Y = gelu_tanh(result) (before any accumulate) */
+    ENC_EPI_GATE_GELU_TANH = 8u, /* gated: Y = gelu_tanh(gate) * up (see gemm_items) */
+    ENC_EPI_GATE_SILU = 16u      /* gated: Y = silu(gate) * up */
 };
 
 /* ------------------------------------------------------------------ context */
@@ -84,7 +86,12 @@ ENC_API const char *enc_last_error(const enc_ctx *ctx);
  *   r  += bias_s[j]                (when bias[s] != NULL)
  *   r   = gelu_tanh(r)             (ENC_EPI_GELU_TANH)
  *   Y[it.y_off + i*it.ldy + j] = r, or += r with ENC_Y_ACCUMULATE (f32 Y only)
- * where s = it.slot.  W_s is [m][k] row-major (the nn.Linear layout, [VE]
+ * where s = it.slot.  With ENC_EPI_GATE_GELU_TANH or ENC_EPI_GATE_SILU the item
+ * is a gated MLP projection ([EG] `Prog::gelu` "O = gelu_tanh(G)·U" on the z = 2
+ * gate/up launch; [ZI] SwiGLU `PSw`): gate_ij and up_ij are the r above for
+ * slots s and s + 1 (no bias), and Y[i][j] = act(gate_ij) * up_ij, so the
+ * gate/up pair never reaches memory.  The result equals the unfused gate/up
+ * GEMM followed by enc_gated_act bit for bit.  W_s is [m][k] row-major (the nn.Linear layout, [VE]
  * `VitGpuOps::linear`), dense with row stride k.
  * Geometry: k % 4 == 0 (F32) or k % 16 == 0 (I8F16); ldx, x_off multiples of 4
  * (F32) or 8 (I8F16); X, Y, W_s 16-byte aligned.  Items may not write
@@ -317,6 +324,15 @@ typedef struct {
  * and starts a new interval.  Not for use under stream capture. */
 ENC_API enc_status enc_prof_enable(enc_ctx *ctx, int on);
 ENC_API enc_status enc_prof_read(enc_ctx *ctx, enc_prof_stat *stats);
+
+/* MFMA issue-rate probe ([ZI] `bench_mma_peak`: a pure matrix-op loop with 16
+ * independent accumulators and no memory traffic).  One launch of `blocks`
+ * 256-thread blocks, each wave issuing iters x 16 MFMAs (ENC_F32:
+ * v_mfma_f32_32x32x2_f32; ENC_I8F16: v_mfma_f32_32x32x16_f16, the GEMMs'
+ * instructions); writes blocks*256 floats to out (dev) and the launch's
+ * flops to *flops.  Time it with events on `stream`. */
+ENC_API enc_status enc_mfma_peak(enc_ctx *ctx, uint32_t path, uint32_t blocks, uint32_t iters,
+                                 float *out, double *flops, enc_stream stream);
 
 /* ---------------------------------------------------- host-only helpers */
 /* No HIP calls: usable and testable without a GPU. */

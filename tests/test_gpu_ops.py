@@ -105,6 +105,47 @@ def test_gemm_packed_rows_bit_identical():
         assert torch.equal(Y, Yall[r0:r1])
 
 
+@pytest.mark.parametrize("path,act,n,ff,d", [
+    (B.ENC_F32, "gelu", 1000, 2048, 512), (B.ENC_F32, "gelu", 37, 200, 128),
+    (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64)])
+def test_gemm_gated_equals_unfused(path, act, n, ff, d):
+    """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
+    bit for bit, and == the oracle within tolerance."""
+    rng = np.random.default_rng(n + ff)
+    i8 = path == B.ENC_I8F16
+    if i8:
+        x = rng.normal(0, 1, (n, d)).astype(np.float16)
+        ws = [rng.integers(-127, 128, (ff, d)).astype(np.int8) for _ in range(2)]
+        rss = [(0.002 * np.exp(0.25 * rng.normal(0, 1, ff))).astype(np.float32) for _ in range(2)]
+        rs = [to_dev(r) for r in rss]
+    else:
+        x = rng.normal(0, 1, (n, d)).astype(np.float32)
+        ws = [rng.normal(0, 0.05, (ff, d)).astype(np.float32) for _ in range(2)]
+        rs = None
+    X, W = to_dev(x), [to_dev(w) for w in ws]
+    odt = torch.float16 if i8 else torch.float32
+    gflag = B.ENC_EPI_GATE_GELU_TANH if act == "gelu" else B.ENC_EPI_GATE_SILU
+    fused = torch.empty((n, ff), dtype=odt, device=DEV)
+    B.gemm_items(X, fused, W, [(n, ff, d, d, ff, 0, 0, 0)], path=path, row_scale=rs,
+                 flags=gflag | (B.ENC_Y_F16 if i8 else 0))
+    gu = torch.empty((n, 2 * ff), dtype=torch.float32, device=DEV)
+    B.gemm_items(X, gu, W, [(n, ff, d, d, 2 * ff, 0, 0, 0), (n, ff, d, d, 2 * ff, 1, 0, ff)],
+                 path=path, row_scale=rs)
+    unfused = torch.empty((n, ff), dtype=odt, device=DEV)
+    kind = B.ENC_ACT_GELU_TANH_GATED if act == "gelu" else B.ENC_ACT_SWIGLU
+    B.gated_act(gu[:, :ff], gu[:, ff:], unfused, kind, f16=i8)
+    assert torch.equal(fused, unfused)
+    xd = x.astype(np.float64)
+    if i8:
+        g, u = O.linear_q8(xd, ws[0], rss[0]), O.linear_q8(xd, ws[1], rss[1])
+    else:
+        g, u = O.linear(xd, ws[0]), O.linear(xd, ws[1])
+    ref = np.vectorize(O.gelu_tanh if act == "gelu" else O.silu)(g) * u
+    if i8:
+        ref = np.vectorize(O.round_f16)(ref)
+    assert row_rel_err(host(fused), ref) <= (TOL_I8F16 if i8 else TOL_F32)
+
+
 # ------------------------------------------------------------- GEMM int8 x f16
 
 @pytest.mark.parametrize("n,m,k", [(1, 1, 16), (45, 70, 48), (130, 257, 256), (300, 128, 3840)])

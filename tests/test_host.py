@@ -74,6 +74,19 @@ def test_check_gemm_rejects(mutate, items, want):
     assert msg
 
 
+def test_check_gemm_gated():
+    d = _gemm(flags=B.ENC_EPI_GATE_GELU_TANH)
+    assert B.check_gemm(d, [(4, 8, 8, 8, 8, 0, 0, 0)])[0] == B.ENC_OK
+    assert B.check_gemm(d, [(4, 8, 8, 8, 8, 1, 0, 0)])[0] == B.ENC_EINVAL  # no slot 2
+    d = _gemm(flags=B.ENC_EPI_GATE_SILU | B.ENC_Y_ACCUMULATE)
+    assert B.check_gemm(d, [(4, 8, 8, 8, 8, 0, 0, 0)])[0] == B.ENC_EUNSUPPORTED
+    d = _gemm(flags=B.ENC_EPI_GATE_SILU | B.ENC_EPI_GATE_GELU_TANH)
+    assert B.check_gemm(d, [(4, 8, 8, 8, 8, 0, 0, 0)])[0] == B.ENC_EINVAL
+    d = _gemm(flags=B.ENC_EPI_GATE_SILU)
+    d.bias[0] = BIAS
+    assert B.check_gemm(d, [(4, 8, 8, 8, 8, 0, 0, 0)])[0] == B.ENC_EUNSUPPORTED
+
+
 def test_check_gemm_int8_needs_scales_and_k16():
     d = _gemm(B.ENC_I8F16)
     assert B.check_gemm(d, [(4, 8, 32, 32, 8, 0, 0, 0)])[0] == B.ENC_OK
@@ -163,8 +176,8 @@ def test_workspace_grows_with_rows():
     a = B.lib().enc_workspace_bytes(C.byref(m), 1000)
     c = B.lib().enc_workspace_bytes(C.byref(m), 2000)
     assert c > a > 0 and a % 256 == 0
-    # A, panel, attention out, T, gate|up, m, H in f32 at d 512, ff 2048, 8x64 heads
-    per_row = 4 * (512 + 1536 + 512 + 512 + 4096 + 2048 + 512)
+    # A, panel, attention out, T, m, H in f32 at d 512, ff 2048, 8x64 heads
+    per_row = 4 * (512 + 1536 + 512 + 512 + 2048 + 512)
     assert a >= 1000 * per_row
 
 

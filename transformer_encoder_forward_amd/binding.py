@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libenc.so")
 ENC_OK, ENC_EINVAL, ENC_ESHAPE, ENC_EUNSUPPORTED, ENC_EDEVICE = range(5)
 ENC_F32, ENC_I8F16 = 0, 1
 ENC_Y_F16, ENC_Y_ACCUMULATE, ENC_EPI_GELU_TANH = 1, 2, 4
+ENC_EPI_GATE_GELU_TANH, ENC_EPI_GATE_SILU = 8, 16
 ENC_ACT_GELU_TANH_GATED, ENC_ACT_SWIGLU = 1, 2
 STATUS_NAMES = {0: "ENC_OK", 1: "ENC_EINVAL", 2: "ENC_ESHAPE", 3: "ENC_EUNSUPPORTED",
                 4: "ENC_EDEVICE"}
@@ -27,7 +28,7 @@ EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attenti
            "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
            "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
-           "enc_rope_table", "enc_prof_enable", "enc_prof_read"]
+           "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak"]
 CLASS_NAMES = ["gemm", "attn", "rows"]
 
 
@@ -166,10 +167,12 @@ def lib():
     L.enc_rope_table.argtypes = [C.c_uint32, C.c_uint32, C.c_uint32, P, C.c_double, P, P]
     L.enc_prof_enable.argtypes = [P, C.c_int]
     L.enc_prof_read.argtypes = [P, C.POINTER(ProfStat)]
+    L.enc_mfma_peak.argtypes = [P, C.c_uint32, C.c_uint32, C.c_uint32, P, C.POINTER(C.c_double), P]
     for f in ("gemm_items", "attention_items", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
               "enc_qk_norm_rope", "enc_gated_act", "enc_mean_pool", "encoder_layer_forward",
               "encoder_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
-              "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read"):
+              "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read",
+              "enc_mfma_peak"):
         getattr(L, f).restype = S
     _lib = L
     return L
@@ -341,6 +344,25 @@ def prof_read(ctx=None):
     ctx.check(lib().enc_prof_read(ctx.h, st))
     return {CLASS_NAMES[i]: dict(launches=st[i].launches, ms=st[i].ms, flops=st[i].flops,
                                  bytes=st[i].bytes) for i in range(3)}
+
+
+def mfma_peak(path, blocks=2048, iters=2000, reps=3, ctx=None):
+    """Measured MFMA ceiling in TFLOP/s (best of `reps` launches, timed with events)."""
+    import torch
+    ctx = ctx or context()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    fl = C.c_double()
+    s = torch.cuda.current_stream()
+    best = 0.0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        ctx.check(lib().enc_mfma_peak(ctx.h, path, blocks, iters, _ptr(out), C.byref(fl),
+                                      s.cuda_stream))
+        e1.record(s)
+        torch.cuda.synchronize()
+        best = max(best, fl.value / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
 
 
 def mean_pool(a, items, out, ctx=None, stream=None):

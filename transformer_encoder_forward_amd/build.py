@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libenc.so")
-SOURCES = ["api.hip", "gemm.hip", "attn.hip", "rowops.hip"]
+SOURCES = ["api.hip", "gemm.hip", "attn.hip", "rowops.hip", "peak.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -115,9 +115,14 @@ enc_status check_gemm(Err &e, const enc_gemm_desc *d, const enc_gemm_item *items
     if (d->path != ENC_F32 && d->path != ENC_I8F16)
         return e.set(ENC_EINVAL, "gemm_items: unknown path %u", d->path);
     if (!d->x || !d->y) return e.set(ENC_EINVAL, "gemm_items: null x or y");
-    if (d->flags & ~7u) return e.set(ENC_EINVAL, "gemm_items: unknown flags 0x%x", d->flags);
+    if (d->flags & ~31u) return e.set(ENC_EINVAL, "gemm_items: unknown flags 0x%x", d->flags);
     if ((d->flags & ENC_Y_F16) && (d->flags & ENC_Y_ACCUMULATE))
         return e.set(ENC_EUNSUPPORTED, "gemm_items: accumulate needs an f32 output");
+    const bool gated = d->flags & (ENC_EPI_GATE_GELU_TANH | ENC_EPI_GATE_SILU);
+    if (gated && ((d->flags & ENC_EPI_GATE_GELU_TANH) && (d->flags & ENC_EPI_GATE_SILU)))
+        return e.set(ENC_EINVAL, "gemm_items: two gated activations");
+    if (gated && (d->flags & (ENC_Y_ACCUMULATE | ENC_EPI_GELU_TANH)))
+        return e.set(ENC_EUNSUPPORTED, "gemm_items: a gated epilogue takes no accumulate or GELU flag");
     const bool i8 = d->path == ENC_I8F16;
     const uint32_t kal = i8 ? 16 : 4, xal = i8 ? 8 : 4;
     if (!aligned(d->x, 16) || !aligned(d->y, 4))
@@ -131,6 +136,15 @@ enc_status check_gemm(Err &e, const enc_gemm_desc *d, const enc_gemm_item *items
             return e.set(ENC_EUNSUPPORTED, "gemm_items: weight slot %u not 16-byte aligned", it.slot);
         if (i8 && !d->row_scale[it.slot])
             return e.set(ENC_EINVAL, "gemm_items: item %u: int8 weights need row scales", i);
+        if (gated) {
+            if (it.slot + 1 >= 4 || !d->w[it.slot + 1] || (i8 && !d->row_scale[it.slot + 1]))
+                return e.set(ENC_EINVAL, "gemm_items: gated item %u needs up weights in slot %u", i,
+                             it.slot + 1);
+            if (!aligned(d->w[it.slot + 1], 16))
+                return e.set(ENC_EUNSUPPORTED, "gemm_items: weight slot %u not 16-byte aligned", it.slot + 1);
+            if (d->bias[it.slot] || d->bias[it.slot + 1])
+                return e.set(ENC_EUNSUPPORTED, "gemm_items: a gated item takes no bias");
+        }
         if (it.m == 0 || it.k == 0)
             return e.set(ENC_ESHAPE, "gemm_items: item %u has m=%u k=%u", i, it.m, it.k);
         if (it.k % kal)
@@ -202,7 +216,8 @@ hipError_t run_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t
     GemmArgs g;
     plan_gemm(d, items, n, g);
     double flops = 0;
-    for (uint32_t i = 0; i < n; i++) flops += 2.0 * items[i].n * items[i].m * items[i].k;
+    const double mul = (d->flags & (ENC_EPI_GATE_GELU_TANH | ENC_EPI_GATE_SILU)) ? 2.0 : 1.0;
+    for (uint32_t i = 0; i < n; i++) flops += 2.0 * mul * items[i].n * items[i].m * items[i].k;
     return prof_launch(ENC_CLASS_GEMM, s, flops, 0.0, [&] {
         return d->path == ENC_I8F16 ? launch_gemm_i8f16(g, s) : launch_gemm_f32(g, s);
     });
@@ -411,7 +426,6 @@ WsPlan plan_ws(const enc_model *M, uint32_t rows) {
         panel = std::max(panel, (size_t)rows * (L.nq + 2 * L.nkv) * L.hd * esz);
         att = std::max(att, (size_t)rows * L.nq * L.hd * esz);
         t = std::max(t, (size_t)rows * L.d * 4);
-        if (L.mlp != ENC_MLP_GELU_TANH) gu = std::max(gu, (size_t)rows * 2 * L.ff * 4);
         m = std::max(m, (size_t)rows * L.ff * (L.mlp == ENC_MLP_GELU_TANH ? 4 : esz));
         h = std::max(h, (size_t)rows * L.d * 4);
     }
@@ -592,21 +606,18 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
         enc_gemm_item it{rows, L.ff, d, d, L.ff, 0, 0, 0};
         TRY(run_gemm(&g, &it, 1, s));
     } else {
+        // gate and up in one launch, act(gate) * up formed in the epilogue
         enc_gemm_desc g{};
         g.path = L.path;
         g.x = b.a;
-        g.y = b.gu;
+        g.y = b.m;
         g.w[0] = L.w_gate; g.w[1] = L.w_up;
         g.row_scale[0] = L.s_gate; g.row_scale[1] = L.s_up;
         g.alpha = 1.0f;
-        g.flags = 0;
-        enc_gemm_item it[2] = {{rows, L.ff, d, d, 2 * L.ff, 0, 0, 0},
-                               {rows, L.ff, d, d, 2 * L.ff, 1, 0, L.ff}};
-        TRY(run_gemm(&g, it, 2, s));
-        ActArgs ac{L.mlp == ENC_MLP_GELU_TANH_GATED ? (uint32_t)ENC_ACT_GELU_TANH_GATED
-                                                     : (uint32_t)ENC_ACT_SWIGLU,
-                   rows, L.ff, 2 * L.ff, 2 * L.ff, L.ff, b.gu, b.gu + L.ff, b.m};
-        TRY(rows_act(ac, i8, s));
+        g.flags = (L.mlp == ENC_MLP_GELU_TANH_GATED ? ENC_EPI_GATE_GELU_TANH : ENC_EPI_GATE_SILU) |
+                  (i8 ? ENC_Y_F16 : 0u);
+        enc_gemm_item it{rows, L.ff, d, d, L.ff, 0, 0, 0};
+        TRY(run_gemm(&g, &it, 1, s));
     }
     {
         enc_gemm_desc g{};
@@ -822,6 +833,21 @@ enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a
         }
         launch_status(e, rows_pool(p, rows, (hipStream_t)stream), "enc_mean_pool");
     }
+    return finish(ctx, e);
+}
+
+enc_status enc_mfma_peak(enc_ctx *ctx, uint32_t path, uint32_t blocks, uint32_t iters, float *out,
+                         double *flops, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    if (!out || !flops || !blocks || path > 1) {
+        e.set(ENC_EINVAL, "enc_mfma_peak: null output or bad arguments");
+        return finish(ctx, e);
+    }
+    const double per = path == ENC_I8F16 ? 32.0 * 32 * 16 * 2 : 32.0 * 32 * 2 * 2;
+    *flops = (double)blocks * 4 * iters * 16 * per;
+    launch_status(e, launch_mfma_peak(path == ENC_I8F16, blocks, iters, out, (hipStream_t)stream),
+                  "enc_mfma_peak");
     return finish(ctx, e);
 }
 

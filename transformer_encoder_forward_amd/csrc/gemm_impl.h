@@ -1,0 +1,691 @@
+// Item-table batched GEMM Y = epi(alpha * X W^T) on gfx950 MFMA: the kernel
+// template (the launcher in gemm.hip picks the instantiation per shape).
+//
+// What it computes: egemma2.rs (cortiq-engine 0.8.39), module doc "GEMM" and
+// `EgMm` (one item per grid z: q/k/v in one launch, gate/up in another);
+// zimage.rs (cortiq-engine 0.7.6), module doc "The chain" and `PMm` (int8
+// weight rows used exactly as half, per-output-row scale in an f32 epilogue).
+//
+// Design for CDNA4: a block of WGM x WGN waves owns a BM x BN output tile; each
+// wave owns (BM/WGM) x (BN/WGN) = FM x FN accumulator blocks of 32 x 32.  X and
+// W tiles of BK columns are staged through double-buffered LDS with one
+// barrier per K stage; the next stage's global loads are issued before the
+// current stage's MFMAs.  Inside a stage, lane half h owns the contiguous K
+// run [h*BK/2, (h+1)*BK/2), so every fragment read is a run of ds_read_b128.
+// The K order of an output element depends only on K and the instantiation,
+// never on the row count or the row's position, so packed and separate
+// batches give the same bits.
+//  - f32: v_mfma_f32_32x32x2_f32 (one k per lane half per step).
+//  - int8 x f16: W tiles are widened int8 -> f16 (exact) while being staged,
+//    X is f16; v_mfma_f32_32x32x16_f16 (8 k per lane half per step), f32
+//    accumulation.
+// Tiles are renumbered so that each XCD (blocks are dispatched round robin
+// over the 8 XCDs) owns a contiguous run, and inside an item the run walks
+// groups of GR row tiles column by column, so a group's X rows and the W
+// columns in flight stay in that XCD's L2.
+#pragma once
+#include <type_traits>
+
+#include "dev.h"
+#include "kern.h"
+
+namespace enc {
+namespace gemm {
+
+constexpr int GR = 8;  // row tiles per L2 group
+
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t G) {
+    const uint32_t x = b & 7u, j = b >> 3, q = G >> 3, r = G & 7u;
+    return x * q + min(x, r) + j;
+}
+
+struct TileCtx {
+    GemmItemK it;
+    const void *w;
+    const float *rs;
+    const float *bias;
+    int row0, col0;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ bool locate(const GemmArgs &a, TileCtx &t, int cols_per_tile = BN) {
+    const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    if (tile >= a.total_tiles) return false;
+    int sel = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxGemmItems; i++)
+        if (i < (int)a.nitems && tile >= a.items[i].tile0) sel = i;
+    t.it = a.items[0];
+#pragma unroll
+    for (int i = 1; i < kMaxGemmItems; i++)
+        if (sel == i) t.it = a.items[i];
+    t.w = a.w[0];
+    t.rs = a.rs[0];
+    t.bias = a.bias[0];
+#pragma unroll
+    for (int s = 1; s < kMaxGemmItems; s++)
+        if ((int)t.it.slot == s) {
+            t.w = a.w[s];
+            t.rs = a.rs[s];
+            t.bias = a.bias[s];
+        }
+    // item-local tile -> (row tile, col tile): groups of GR row tiles, each
+    // group walked column by column (row tile fastest)
+    const uint32_t local = tile - t.it.tile0;
+    const uint32_t tiles_n = (t.it.n + BM - 1) / BM, tm = t.it.tiles_m;
+    const uint32_t g = local / (GR * tm), in_g = local % (GR * tm);
+    const uint32_t rows_g = min((uint32_t)GR, tiles_n - g * GR);
+    t.row0 = (int)((g * GR + in_g % rows_g) * BM);
+    t.col0 = (int)((in_g / rows_g) * cols_per_tile);
+    return true;
+}
+
+// Gated epilogue flags (internal copies of the public ENC_EPI_GATE_* bits).
+constexpr uint32_t kGateGelu = 8u, kGateSilu = 16u;
+
+template <bool I8>
+struct Elem;
+template <>
+struct Elem<false> {
+    using T = float;
+    using V = f32x4;  // 16-byte LDS / global chunk
+    static constexpr int CE = 4;
+    static constexpr int KSTEP = 2;  // k per MFMA (both lane halves)
+};
+template <>
+struct Elem<true> {
+    using T = _Float16;
+    using V = f16x8;
+    static constexpr int CE = 8;
+    static constexpr int KSTEP = 16;
+};
+
+// 16 int8 -> 16 f16, exact: byte b, biased to b + 128 in [1, 255], is the low
+// mantissa of the half 1024 + (b + 128) (bits 0x6400 | byte); subtracting 1152
+// leaves b.  Two packed halves per 32-bit op.
+__device__ __forceinline__ void widen16(const int32_t w[4], f16x8 &lo, f16x8 &hi) {
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t u = (uint32_t)w[i] ^ 0x80808080u;
+        // bytes (0, 1) and (2, 3) of u as the low bytes of two halves each
+        o[2 * i] = __builtin_amdgcn_perm(0x64646464u, u, 0x05010400u);
+        o[2 * i + 1] = __builtin_amdgcn_perm(0x64646464u, u, 0x05030402u);
+    }
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        f16x2 a = __builtin_bit_cast(f16x2, o[i]) - bias;
+        f16x2 b = __builtin_bit_cast(f16x2, o[4 + i]) - bias;
+        lo[2 * i] = a[0];
+        lo[2 * i + 1] = a[1];
+        hi[2 * i] = b[0];
+        hi[2 * i + 1] = b[1];
+    }
+}
+
+// Epilogue for one 32x32 accumulator block: D[i][j] of lane l, register r sits
+// at i = 8*(r/4) + 4*(l/32) + r%4, j = l%32.
+template <bool I8>
+__device__ __forceinline__ void store_block(const GemmArgs &a, const TileCtx &t, const f32x16 &acc,
+                                            int rbase, int cbase, int lane) {
+    const int li = lane & 31, hf = lane >> 5;
+    const int c = cbase + li;
+    if (c >= (int)t.it.m) return;
+    float mul = a.alpha;
+    if (I8) mul *= t.rs[c];
+    const float b = t.bias ? t.bias[c] : 0.0f;
+    const bool f16 = a.flags & 1u, accum = a.flags & 2u, gelu = a.flags & 4u;
+    const size_t base = t.it.y_off + c;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int row = rbase + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (row >= (int)t.it.n) continue;
+        float v = acc[r] * mul + b;
+        if (gelu) v = gelu_tanh(v);
+        const size_t off = base + (size_t)row * t.it.ldy;
+        if (f16) {
+            reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+        } else {
+            float *y = reinterpret_cast<float *>(a.y) + off;
+            *y = accum ? *y + v : v;
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) {
+    using E = Elem<I8>;
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int CE = E::CE;
+    constexpr int LDS = BK + CE;  // padded row (elements): rows 16 bytes apart in bank phase
+    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
+    constexpr int HK = BK / 2;            // k per lane half per stage
+    constexpr int NV = HK / CE;           // 16-byte fragment chunks per lane per block
+    constexpr int NSTEP = BK / E::KSTEP;  // MFMA k-steps per stage
+    constexpr int A_CH = BM * BK / CE / NT;        // X chunks per thread per stage
+    constexpr int B_CH = I8 ? BN * BK / 16 / NT : BN * BK / CE / NT;
+    static_assert(FM >= 1 && FN >= 1 && BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "tile");
+    static_assert(BM * BK % (CE * NT) == 0 && (I8 ? BN * BK % (16 * NT) : BN * BK % (CE * NT)) == 0,
+                  "loads");
+    static_assert(HK % CE == 0, "fragments");
+
+    __shared__ __attribute__((aligned(16))) T As[2][BM][LDS];
+    __shared__ __attribute__((aligned(16))) T Bs[2][BN][LDS];
+    TileCtx t;
+    if (!locate<BM, BN>(a, t)) return;
+    const int n = t.it.n, m = t.it.m, K = t.it.k;
+    const T *X = reinterpret_cast<const T *>(a.x) + t.it.x_off;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    V ra[A_CH];
+    using BReg = typename std::conditional<I8, int32_t, V>::type;
+    constexpr int BRW = I8 ? 4 : 1;  // register words per B chunk
+    BReg rb[B_CH][BRW];
+
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            const int gk = k0 + c, gr = t.row0 + r;
+            if (gr < n && gk < K)
+                ra[i] = *reinterpret_cast<const V *>(X + (size_t)gr * t.it.ldx + gk);
+            else
+                ra[i] = V{};
+        }
+        if constexpr (I8) {
+            const int8_t *W = reinterpret_cast<const int8_t *>(t.w);
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                const int gk = k0 + c, gc = t.col0 + r;
+                if (gc < m && gk < K) {
+                    const int32_t *p = reinterpret_cast<const int32_t *>(W + (size_t)gc * K + gk);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) rb[i][q] = p[q];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) rb[i][q] = 0;
+                }
+            }
+        } else {
+            const float *W = reinterpret_cast<const float *>(t.w);
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                const int gk = k0 + c, gc = t.col0 + r;
+                rb[i][0] = (gc < m && gk < K) ? *reinterpret_cast<const V *>(W + (size_t)gc * K + gk) : V{};
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            *reinterpret_cast<V *>(&As[buf][r][c]) = ra[i];
+        }
+        if constexpr (I8) {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                f16x8 lo, hi;
+                widen16(rb[i], lo, hi);
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c]) = lo;
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c + 8]) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                *reinterpret_cast<V *>(&Bs[buf][r][c]) = rb[i][0];
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    const int nst = (K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int s = 0; s < nst; s++) {
+        const int buf = s & 1;
+        if (s + 1 < nst) gload((s + 1) * BK);
+        V fa[FM][NV], fb[FN][NV];
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int q = 0; q < NV; q++)
+                fa[i][q] = *reinterpret_cast<const V *>(&As[buf][wr * (BM / WGM) + i * 32 + li][HK * hf + CE * q]);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int q = 0; q < NV; q++)
+                fb[j][q] = *reinterpret_cast<const V *>(&Bs[buf][wc * (BN / WGN) + j * 32 + li][HK * hf + CE * q]);
+#pragma unroll
+        for (int kk = 0; kk < NSTEP; kk++)
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    if constexpr (I8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i][kk], fb[j][kk], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk / 4][kk % 4], fb[j][kk / 4][kk % 4],
+                                                                        acc[i][j], 0, 0, 0);
+                }
+        if (s + 1 < nst) sstore(buf ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            store_block<I8>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
+                            lane);
+}
+
+// Tiles of the item table for a BM x BN instantiation (fills tiles_m, tile0).
+inline uint32_t plan_tiles(GemmArgs &g, int BM, int BN) {
+    uint32_t tiles = 0;
+    for (uint32_t i = 0; i < g.nitems; i++) {
+        GemmItemK &k = g.items[i];
+        k.tiles_m = (k.m + BN - 1) / BN;
+        k.tile0 = tiles;
+        tiles += k.tiles_m * ((k.n + BM - 1) / BM);
+    }
+    for (uint32_t i = g.nitems; i < (uint32_t)kMaxGemmItems; i++) g.items[i].tile0 = 0xffffffffu;
+    g.total_tiles = tiles;
+    return tiles;
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+hipError_t launch(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, BM, BN);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WGM, WGN, I8, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    return hipGetLastError();
+}
+
+// Deeper-pipelined schedule of the same tile: global loads run two K stages
+// ahead (a ring of two register sets, loop unrolled by two so the ring index
+// is static), and inside a stage the fragments of k-step kk+1 are read from
+// LDS while the MFMAs of k-step kk run.  Same K order per output as
+// gemm_kernel, so results are bit-identical between the two schedules.
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel_v2(GemmArgs a) {
+    using E = Elem<I8>;
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int CE = E::CE;
+    constexpr int LDS = BK + CE;
+    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
+    constexpr int HK = BK / 2;
+    constexpr int NSTEP = BK / E::KSTEP;
+    constexpr int A_CH = BM * BK / CE / NT;
+    constexpr int B_CH = I8 ? BN * BK / 16 / NT : BN * BK / CE / NT;
+    // fragment of one k-step: f16 -> one V (8 halves); f32 -> one float
+    using F = typename std::conditional<I8, f16x8, float>::type;
+    static_assert(FM >= 1 && FN >= 1, "tile");
+    static_assert(BM * BK % (CE * NT) == 0 && (I8 ? BN * BK % (16 * NT) : BN * BK % (CE * NT)) == 0,
+                  "loads");
+
+    __shared__ __attribute__((aligned(16))) T As[2][BM][LDS];
+    __shared__ __attribute__((aligned(16))) T Bs[2][BN][LDS];
+    TileCtx t;
+    if (!locate<BM, BN>(a, t)) return;
+    const int n = t.it.n, m = t.it.m, K = t.it.k;
+    const T *X = reinterpret_cast<const T *>(a.x) + t.it.x_off;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    using BReg = typename std::conditional<I8, int32_t, V>::type;
+    constexpr int BRW = I8 ? 4 : 1;
+    V ra[2][A_CH];
+    BReg rb[2][B_CH][BRW];
+
+    auto gload = [&](int k0, V (&RA)[A_CH], BReg (&RB)[B_CH][BRW]) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            const int gk = k0 + c, gr = t.row0 + r;
+            if (gr < n && gk < K)
+                RA[i] = *reinterpret_cast<const V *>(X + (size_t)gr * t.it.ldx + gk);
+            else
+                RA[i] = V{};
+        }
+        if constexpr (I8) {
+            const int8_t *W = reinterpret_cast<const int8_t *>(t.w);
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                const int gk = k0 + c, gc = t.col0 + r;
+                if (gc < m && gk < K) {
+                    const int32_t *p = reinterpret_cast<const int32_t *>(W + (size_t)gc * K + gk);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) RB[i][q] = p[q];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) RB[i][q] = 0;
+                }
+            }
+        } else {
+            const float *W = reinterpret_cast<const float *>(t.w);
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                const int gk = k0 + c, gc = t.col0 + r;
+                RB[i][0] = (gc < m && gk < K) ? *reinterpret_cast<const V *>(W + (size_t)gc * K + gk) : V{};
+            }
+        }
+    };
+    auto sstore = [&](int buf, const V (&RA)[A_CH], const BReg (&RB)[B_CH][BRW]) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            *reinterpret_cast<V *>(&As[buf][r][c]) = RA[i];
+        }
+        if constexpr (I8) {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                f16x8 lo, hi;
+                widen16(RB[i], lo, hi);
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c]) = lo;
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c + 8]) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                *reinterpret_cast<V *>(&Bs[buf][r][c]) = RB[i][0];
+            }
+        }
+    };
+    // fragment of k-step kk for accumulator row block i / column block j
+    auto frag_a = [&](int buf, int i, int kk) -> F {
+        const T *p = &As[buf][wr * (BM / WGM) + i * 32 + li][HK * hf];
+        if constexpr (I8) return *reinterpret_cast<const f16x8 *>(p + 8 * kk);
+        else return p[kk];
+    };
+    auto frag_b = [&](int buf, int j, int kk) -> F {
+        const T *p = &Bs[buf][wc * (BN / WGN) + j * 32 + li][HK * hf];
+        if constexpr (I8) return *reinterpret_cast<const f16x8 *>(p + 8 * kk);
+        else return p[kk];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    auto compute = [&](int buf) {
+        F fa[2][FM], fb[2][FN];
+#pragma unroll
+        for (int i = 0; i < FM; i++) fa[0][i] = frag_a(buf, i, 0);
+#pragma unroll
+        for (int j = 0; j < FN; j++) fb[0][j] = frag_b(buf, j, 0);
+#pragma unroll
+        for (int kk = 0; kk < NSTEP; kk++) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < NSTEP) {
+#pragma unroll
+                for (int i = 0; i < FM; i++) fa[nxt][i] = frag_a(buf, i, kk + 1);
+#pragma unroll
+                for (int j = 0; j < FN; j++) fb[nxt][j] = frag_b(buf, j, kk + 1);
+            }
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    if constexpr (I8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                }
+        }
+    };
+
+    const int nst = (K + BK - 1) / BK;
+    gload(0, ra[0], rb[0]);
+    if (nst > 1) gload(BK, ra[1], rb[1]);
+    sstore(0, ra[0], rb[0]);
+    __syncthreads();
+    // stage s computes on LDS buf s&1; register set s&1 is free once stage s
+    // has been written to LDS, so it receives stage s+2
+    for (int s = 0; s < nst; s += 2) {
+        if (s + 2 < nst) gload((s + 2) * BK, ra[0], rb[0]);
+        compute(0);
+        if (s + 1 < nst) sstore(1, ra[1], rb[1]);
+        __syncthreads();
+        if (s + 1 >= nst) break;
+        if (s + 3 < nst) gload((s + 3) * BK, ra[1], rb[1]);
+        compute(1);
+        if (s + 2 < nst) sstore(0, ra[0], rb[0]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            store_block<I8>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
+                            lane);
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+hipError_t launch_v2(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, BM, BN);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((gemm_kernel_v2<BM, BN, BK, WGM, WGN, I8, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    return hipGetLastError();
+}
+
+// Gated MLP GEMM: Y[i][j] = act(alpha * gate_ij) * (alpha * up_ij), act =
+// gelu_tanh or silu, gate from weight slot s and up from slot s+1 (int8 path:
+// each times its own row scale).  Each wave's two 32-column accumulator blocks
+// are the gate and the up projections of the same 32 output columns, so the
+// product is formed in registers: the gate|up pair is never written out.  The
+// block tile covers BN/2 output columns; K order as gemm_kernel.
+template <int BM, int BN, int BK, int WGM, bool I8, int MINB>
+__global__ __launch_bounds__(64 * WGM * (BN / 64), MINB) void gemm_gated_kernel(GemmArgs a) {
+    constexpr int WGN = BN / 64;  // waves along N, each 32 gate + 32 up columns
+    using E = Elem<I8>;
+    using T = typename E::T;
+    using V = typename E::V;
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int CE = E::CE;
+    constexpr int LDS = BK + CE;
+    constexpr int FM = BM / WGM / 32, FN = 2;
+    constexpr int HK = BK / 2;
+    constexpr int NV = HK / CE;
+    constexpr int NSTEP = BK / E::KSTEP;
+    constexpr int A_CH = BM * BK / CE / NT;
+    constexpr int B_CH = I8 ? BN * BK / 16 / NT : BN * BK / CE / NT;
+    static_assert(FM >= 1 && BN % 64 == 0, "tile");
+    static_assert(BM * BK % (CE * NT) == 0 && (I8 ? BN * BK % (16 * NT) : BN * BK % (CE * NT)) == 0,
+                  "loads");
+
+    __shared__ __attribute__((aligned(16))) T As[2][BM][LDS];
+    __shared__ __attribute__((aligned(16))) T Bs[2][BN][LDS];
+    TileCtx t;
+    if (!locate<BM, BN>(a, t, BN / 2)) return;
+    // gate = slot s, up = slot s + 1
+    const void *wg = t.w, *wu = a.w[1];
+    const float *rg = t.rs, *ru = a.rs[1];
+#pragma unroll
+    for (int s2 = 1; s2 < kMaxGemmItems; s2++)
+        if ((int)t.it.slot + 1 == s2) {
+            wu = a.w[s2];
+            ru = a.rs[s2];
+        }
+    const int n = t.it.n, m = t.it.m, K = t.it.k;
+    const T *X = reinterpret_cast<const T *>(a.x) + t.it.x_off;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    // B tile row r holds weight row col0 + (r/64)*32 + r%32 of the gate
+    // ((r/32) even) or up ((r/32) odd) matrix
+    auto brow = [&](int r, const void *&w) -> int {
+        w = ((r >> 5) & 1) ? wu : wg;
+        return t.col0 + (r >> 6) * 32 + (r & 31);
+    };
+
+    V ra[A_CH];
+    using BReg = typename std::conditional<I8, int32_t, V>::type;
+    constexpr int BRW = I8 ? 4 : 1;
+    BReg rb[B_CH][BRW];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            const int gk = k0 + c, gr = t.row0 + r;
+            if (gr < n && gk < K)
+                ra[i] = *reinterpret_cast<const V *>(X + (size_t)gr * t.it.ldx + gk);
+            else
+                ra[i] = V{};
+        }
+        if constexpr (I8) {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                const void *w;
+                const int gc = brow(r, w), gk = k0 + c;
+                if (gc < m && gk < K) {
+                    const int32_t *p = reinterpret_cast<const int32_t *>(reinterpret_cast<const int8_t *>(w) +
+                                                                         (size_t)gc * K + gk);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) rb[i][q] = p[q];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) rb[i][q] = 0;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                const void *w;
+                const int gc = brow(r, w), gk = k0 + c;
+                rb[i][0] = (gc < m && gk < K)
+                               ? *reinterpret_cast<const V *>(reinterpret_cast<const float *>(w) + (size_t)gc * K + gk)
+                               : V{};
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            *reinterpret_cast<V *>(&As[buf][r][c]) = ra[i];
+        }
+        if constexpr (I8) {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / 16), c = (f % (BK / 16)) * 16;
+                f16x8 lo, hi;
+                widen16(rb[i], lo, hi);
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c]) = lo;
+                *reinterpret_cast<f16x8 *>(&Bs[buf][r][c + 8]) = hi;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < B_CH; i++) {
+                const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+                *reinterpret_cast<V *>(&Bs[buf][r][c]) = rb[i][0];
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    const int nst = (K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int s = 0; s < nst; s++) {
+        const int buf = s & 1;
+        if (s + 1 < nst) gload((s + 1) * BK);
+        V fa[FM][NV], fb[FN][NV];
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int q = 0; q < NV; q++)
+                fa[i][q] = *reinterpret_cast<const V *>(&As[buf][wr * (BM / WGM) + i * 32 + li][HK * hf + CE * q]);
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int q = 0; q < NV; q++)
+                fb[j][q] = *reinterpret_cast<const V *>(&Bs[buf][wc * 64 + j * 32 + li][HK * hf + CE * q]);
+#pragma unroll
+        for (int kk = 0; kk < NSTEP; kk++)
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    if constexpr (I8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i][kk], fb[j][kk], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk / 4][kk % 4], fb[j][kk / 4][kk % 4],
+                                                                        acc[i][j], 0, 0, 0);
+                }
+        if (s + 1 < nst) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    // epilogue: lane holds gate and up of the same (row, column)
+    const int c = t.col0 + wc * 32 + li;
+    if (c >= m) return;
+    float mg = a.alpha, mu = a.alpha;
+    if (I8) {
+        mg *= rg[c];
+        mu *= ru[c];
+    }
+    const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (row >= n) continue;
+            const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
+            const float v = (gelu ? gelu_tanh(g) : silu(g)) * u;
+            const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
+            if (f16)
+                reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+            else
+                reinterpret_cast<float *>(a.y)[off] = v;
+        }
+}
+
+template <int BM, int BN, int BK, int WGM, bool I8, int MINB>
+hipError_t launch_gated(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, BM, BN / 2);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((gemm_gated_kernel<BM, BN, BK, WGM, I8, MINB>), dim3(tiles), dim3(64 * WGM * (BN / 64)), 0, s,
+                       g);
+    return hipGetLastError();
+}
+
+}  // namespace gemm
+}  // namespace enc

@@ -96,6 +96,7 @@ hipError_t launch_add_norm(const AddNormArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_qk_norm_rope(const QkArgs &a, bool f16, hipStream_t s);
 hipError_t launch_gated_act(const ActArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s);
+hipError_t launch_mfma_peak(bool f16, uint32_t blocks, uint32_t iters, float *out, hipStream_t s);
 
 // Tile sizes the launchers and the planner agree on.
 constexpr int kGemmBM = 128, kGemmBN = 128;

@@ -159,63 +159,90 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
     }
 }
 
-// One wave per (row, head) over the nq q heads then the nkv k heads; lane owns
-// E = hd/64 consecutive channels.  The rotate_half partner of channel c is
-// c +- S/2, held by lane ^ (S/2/E) in the same slot.
+// One wave per row over all of its nq q heads and nkv k heads.  A head is held
+// by LH = hd / VE lanes, each owning VE consecutive channels (one 16-byte
+// vector: 4 f32 or 8 f16), so a wave covers 64 / LH heads per pass with fully
+// coalesced loads.  The per-head RMS is a butterfly inside the LH-lane group;
+// the rotate_half partner of channel c (c +- S/2) sits (S/2)/VE lanes away, in
+// the same vector slot.
 template <int HD, bool F16>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
-    constexpr int E = HD / 64;
-    const uint32_t heads = a.nq + a.nkv;
-    const uint32_t unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int VE = F16 ? 8 : 4;
+    constexpr int LH = HD / VE;   // lanes per head
+    constexpr int HP = 64 / LH;   // heads per pass
+    const uint32_t row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (unit >= a.rows * heads) return;
-    const uint32_t row = unit / heads, hh = unit % heads;
-    const bool isq = hh < a.nq;
-    const uint32_t col = isq ? a.q_col + hh * HD : a.k_col + (hh - a.nq) * HD;
-    const float *w = isq ? a.qw : a.kw;
-    const int c0 = lane * E;
-    float x[E];
-    if (F16) {
-        const _Float16 *p = reinterpret_cast<const _Float16 *>(a.panel) + (size_t)row * a.ld + col + c0;
-#pragma unroll
-        for (int e = 0; e < E; e++) x[e] = (float)p[e];
-    } else {
-        const float *p = reinterpret_cast<const float *>(a.panel) + (size_t)row * a.ld + col + c0;
-#pragma unroll
-        for (int e = 0; e < E; e++) x[e] = p[e];
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; e++) ss = fmaf(x[e], x[e], ss);
-    const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)HD + a.eps);
-#pragma unroll
-    for (int e = 0; e < E; e++) x[e] = x[e] * inv * w[c0 + e];
+    if (row >= a.rows) return;
+    const int hsub = lane / LH, c0 = (lane % LH) * VE;
+    const uint32_t heads = a.nq + a.nkv;
+    const int S = a.sections ? HD / (int)a.sections : HD, half = S / 2;
+    const int s_idx = c0 / S, i0 = c0 % S;
+    const bool first = i0 < half;
+    const int ti = s_idx * half + (first ? i0 : i0 - half);
+    const int pmask = half / VE;  // partner lane distance (power of two)
+    float cs[VE], sn[VE];
     if (a.sections) {
-        const int S = HD / (int)a.sections, half = S / 2;
-        const int mask = half / E;
-        const float *cs = a.cos + (size_t)row * (HD / 2);
-        const float *sn = a.sin + (size_t)row * (HD / 2);
-        float y[E];
+        const float *cp = a.cos + (size_t)row * (HD / 2) + ti;
+        const float *sp = a.sin + (size_t)row * (HD / 2) + ti;
 #pragma unroll
-        for (int e = 0; e < E; e++) {
-            const float xp = __shfl_xor(x[e], mask, 64);
-            const int c = c0 + e, s = c / S, i = c % S;
-            const bool first = i < half;
-            const int ti = s * half + (first ? i : i - half);
-            const float cv = cs[ti], sv = sn[ti];
-            y[e] = first ? x[e] * cv - xp * sv : x[e] * cv + xp * sv;
+        for (int e = 0; e < VE; e++) {
+            cs[e] = cp[e];
+            sn[e] = sp[e];
         }
-#pragma unroll
-        for (int e = 0; e < E; e++) x[e] = y[e];
     }
-    if (F16) {
-        _Float16 *p = reinterpret_cast<_Float16 *>(a.panel) + (size_t)row * a.ld + col + c0;
+    for (uint32_t h0 = 0; h0 < heads; h0 += HP) {
+        const uint32_t hh = h0 + hsub;
+        const bool valid = hh < heads;
+        const bool isq = hh < a.nq;
+        const uint32_t col = isq ? a.q_col + hh * HD : a.k_col + (hh - a.nq) * HD;
+        const float *w = isq ? a.qw : a.kw;
+        float x[VE];
+        if (valid) {
+            if (F16) {
+                const f16x8 v = *reinterpret_cast<const f16x8 *>(
+                    reinterpret_cast<const _Float16 *>(a.panel) + (size_t)row * a.ld + col + c0);
 #pragma unroll
-        for (int e = 0; e < E; e++) p[e] = (_Float16)x[e];
-    } else {
-        float *p = reinterpret_cast<float *>(a.panel) + (size_t)row * a.ld + col + c0;
+                for (int e = 0; e < VE; e++) x[e] = (float)v[e % 8];
+            } else {
+                const f32x4 v = ld4(reinterpret_cast<const float *>(a.panel) + (size_t)row * a.ld + col + c0);
 #pragma unroll
-        for (int e = 0; e < E; e++) p[e] = x[e];
+                for (int e = 0; e < VE; e++) x[e] = v[e % 4];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; e++) x[e] = 0.0f;
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VE; e++) ss = fmaf(x[e], x[e], ss);
+#pragma unroll
+        for (int o = LH / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
+        if (valid) {
+#pragma unroll
+            for (int e = 0; e < VE; e++) x[e] = x[e] * inv * w[c0 + e];
+        }
+        if (a.sections) {
+            float y[VE];
+#pragma unroll
+            for (int e = 0; e < VE; e++) {
+                const float xp = __shfl_xor(x[e], pmask, 64);
+                y[e] = first ? x[e] * cs[e] - xp * sn[e] : x[e] * cs[e] + xp * sn[e];
+            }
+#pragma unroll
+            for (int e = 0; e < VE; e++) x[e] = y[e];
+        }
+        if (valid) {
+            if (F16) {
+                f16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; e++) v[e] = (_Float16)x[e % VE];
+                *reinterpret_cast<f16x8 *>(reinterpret_cast<_Float16 *>(a.panel) + (size_t)row * a.ld + col + c0) = v;
+            } else {
+                st4(reinterpret_cast<float *>(a.panel) + (size_t)row * a.ld + col + c0,
+                    f32x4{x[0], x[1 % VE], x[2 % VE], x[3 % VE]});
+            }
+        }
     }
 }
 
@@ -238,18 +265,28 @@ __global__ __launch_bounds__(256) void gated_act_kernel(ActArgs a) {
     }
 }
 
-// out[i][j] = mean over item i's rows of a[r][j]; one thread per column, rows
-// summed in order (deterministic).
+// out[i][j] = mean over item i's rows of a[r][j].  A block takes one item and
+// 64 columns; wave w sums rows t = w, w+4, ... (lane = column, coalesced
+// 256-byte loads), and the four partial sums are added in wave order:
+// deterministic.
 __global__ __launch_bounds__(256) void mean_pool_kernel(PoolArgs a) {
-    const uint32_t j = blockIdx.x * 256 + threadIdx.x, i = blockIdx.y;
-    if (j >= a.d || i >= a.nitems) return;
+    __shared__ float part[4][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t j = blockIdx.x * 64 + lane, i = blockIdx.y;
     const AttnItemK it = a.items[i];
+    const uint32_t L = it.na + it.nb;
     float s = 0.0f;
-    for (uint32_t t = 0; t < it.na; t++) s += a.a[(size_t)(it.r0a + t) * a.d + j];
-    for (uint32_t t = 0; t < it.nb; t++) s += a.a[(size_t)(it.r0b + t) * a.d + j];
-    a.out[(size_t)i * a.d + j] = s / (float)(it.na + it.nb);
+    if (j < a.d) {
+        for (uint32_t t = wave; t < L; t += 4) {
+            const uint32_t r = t < it.na ? it.r0a + t : it.r0b + (t - it.na);
+            s += a.a[(size_t)r * a.d + j];
+        }
+    }
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && j < a.d)
+        a.out[(size_t)i * a.d + j] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / (float)L;
 }
-
 
 }  // namespace
 
@@ -309,9 +346,8 @@ hipError_t launch_add_norm(const AddNormArgs &a, bool f16, hipStream_t s) {
 }
 
 hipError_t launch_qk_norm_rope(const QkArgs &a, bool f16, hipStream_t s) {
-    const size_t units = (size_t)a.rows * (a.nq + a.nkv);
-    if (!units) return hipSuccess;
-    const dim3 grid((unsigned)((units + 3) / 4));
+    if (!a.rows || !(a.nq + a.nkv)) return hipSuccess;
+    const dim3 grid((a.rows + 3) / 4);
     if (a.hd == 64) {
         if (f16) hipLaunchKernelGGL((qk_norm_rope_kernel<64, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((qk_norm_rope_kernel<64, false>), grid, dim3(256), 0, s, a);
@@ -333,7 +369,7 @@ hipError_t launch_gated_act(const ActArgs &a, bool f16, hipStream_t s) {
 
 hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s) {
     if (!a.nitems || !a.d) return hipSuccess;
-    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 255) / 256, a.nitems), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 63) / 64, a.nitems), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
