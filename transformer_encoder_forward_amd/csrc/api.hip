@@ -299,18 +299,15 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         a.group = d->nq / d->nkv;
         a.scale_log2 = (float)((double)d->scale * 1.4426950408889634);
         a.window = d->window;
-        uint32_t tiles = 0, k = 0;
+        uint32_t k = 0;
         for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++, k++) {
             const enc_item &it = items[order[c]];
             a.items[k].r0a = it.r[0].r0;
             a.items[k].na = it.r[0].n;
             a.items[k].r0b = it.nr > 1 ? it.r[1].r0 : 0;
             a.items[k].nb = it.nr > 1 ? it.r[1].n : 0;
-            a.items[k].tile0 = tiles;
-            tiles += (item_len(it) + kAttnQTile - 1) / kAttnQTile;
         }
         a.nitems = k;
-        a.ntiles = tiles;
         double pairs = 0;
         for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++)
             pairs += visible_pairs(item_len(items[order[c]]), d->window);

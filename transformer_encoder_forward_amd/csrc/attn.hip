@@ -1,37 +1,21 @@
-// Non-causal flash attention over packed items on gfx950 MFMA.
+// Launchers of the flash attention.
 //
-// What it computes: egemma2.rs (cortiq-engine 0.8.39), module doc "Attention"
-// and `att_plan` (bidirectional window: keys [q0 - W, q_last + W] clipped to
-// the sequence; GQA head map h / (nq / nkv)), and the staged flash of
-// `VisionGpu::forward`; zimage.rs (cortiq-engine 0.7.6), module doc (flash
-// with K/V blocks staged in threadgroup memory; an item = its image range plus
-// its caption range, `PFa`).  Online softmax: no score matrix is written.
-//
-// Design for CDNA4: a 256-thread block takes 128 queries of one item and one
-// head; each wave owns 32 queries.  Per 32-key block the wave computes the
-// TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs, so lane l holds query l%32
-// and 16 of the block's keys: the row max and row sum are 16 lane-local steps
-// plus one exchange with lane l^32, and P^T is already in the B-operand layout
-// of O^T = V^T P^T.  The running max/sum/rescale therefore never leave the lane.
-// K/V blocks are double-buffered in LDS and shared by the 4 waves; waves whose
-// queries see none of a block (window, ragged tail) skip its MFMAs.  The
-// softmax runs in base 2 with log2(e) folded into the scale.
-//  - f32 path: v_mfma_f32_32x32x2_f32 for both products (hd 64 or 128).
-//  - f16 path: v_mfma_f32_32x32x16_f16; V is staged transposed (V^T[d][key])
-//    so the A operand of O^T is two 8-byte LDS reads; P is rounded to f16.
-// Blocks are ordered head-fastest so the heads of one query tile run side by
-// side and each XCD sees a fixed head subset; the host orders items longest
-// first.
+// f16 path: the kernel template in attn_impl.h (mask fast path, lazy rescale).
+// f32 path: the kernel below, the same S^T = K Q^T / O^T = V^T P^T scheme in its
+// plain form: with 64-cycle FP32 MFMAs the softmax VALU work is hidden anyway,
+// and the plain form keeps the register count at 128 (4 waves per SIMD).
+// What both compute: egemma2.rs (cortiq-engine 0.8.39), module doc "Attention"
+// and `att_plan`; zimage.rs (cortiq-engine 0.7.6), module doc and `PFa`.
 #include <math.h>
 
-#include "dev.h"
-#include "kern.h"
+#include "attn_impl.h"
 
 namespace enc {
 
-namespace {
+namespace f32path {
 
-constexpr int KB = 32;  // keys per block
+constexpr int KB = 32;   // keys per block
+constexpr int kQT = 128;  // queries per block (4 waves x 32)
 
 struct ItemCtx {
     AttnItemK it;
@@ -44,8 +28,8 @@ __device__ __forceinline__ void locate(const AttnArgs &a, uint32_t tile, ItemCtx
         if (tile >= a.items[i].tile0) sel = i;
     c.it = a.items[sel];
     c.L = (int)(c.it.na + c.it.nb);
-    c.q_lo = (int)(tile - c.it.tile0) * kAttnQTile;
-    c.q_hi = min(c.q_lo + kAttnQTile, c.L);
+    c.q_lo = (int)(tile - c.it.tile0) * kQT;
+    c.q_hi = min(c.q_lo + kQT, c.L);
     c.k_lo = 0;
     c.k_hi = c.L;
     if (a.window) {
@@ -210,156 +194,22 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ f16 path
+}  // namespace f32path
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_f16_kernel(AttnArgs a) {
-    constexpr int LDK = HD + 8;     // halves
-    constexpr int LDVT = KB + 8;    // halves, V^T rows
-    constexpr int NQ8 = HD / 16;    // f16x8 of q per lane
-    constexpr int NLD = KB * HD / 8 / 256;  // 8-half chunks of K (and V) per thread
-    __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KB][LDK];
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[2][HD][LDVT];
-
-    const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
-    ItemCtx c;
-    locate(a, tile, c);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 31, hf = lane >> 5;
-    const int kvh = head / a.group;
-    const _Float16 *P = reinterpret_cast<const _Float16 *>(a.qkv);
-    const uint32_t W = a.window;
-
-    const int tq = c.q_lo + wave * 32 + li;
-    const bool qvalid = tq < c.q_hi;
-    const int wq0 = c.q_lo + wave * 32, wq1 = min(wq0 + 32, c.q_hi);
-
-    f16x8 qf[NQ8];
-    {
-        const _Float16 *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col +
-                             head * HD + (HD / 2) * hf;
-#pragma unroll
-        for (int j = 0; j < NQ8; j++)
-            qf[j] = qvalid ? *reinterpret_cast<const f16x8 *>(qp + 8 * j) : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-
-    f16x8 rk[NLD], rv[NLD];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < NLD; i++) {
-            const int f = tid + 256 * i, key = f / (HD / 8), ch = (f % (HD / 8)) * 8;
-            const int t = kb + key;
-            if (t < c.k_hi) {
-                const _Float16 *base = P + (size_t)row_of(c.it, t) * a.ld + kvh * HD + ch;
-                rk[i] = *reinterpret_cast<const f16x8 *>(base + a.k_col);
-                rv[i] = *reinterpret_cast<const f16x8 *>(base + a.v_col);
-            } else {
-                rk[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                rv[i] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < NLD; i++) {
-            const int f = tid + 256 * i, key = f / (HD / 8), ch = (f % (HD / 8)) * 8;
-            *reinterpret_cast<f16x8 *>(&Ks[buf][key][ch]) = rk[i];
-#pragma unroll
-            for (int e = 0; e < 8; e++) Vt[buf][ch + e][key] = rv[i][e];
-        }
-    };
-
-    f32x16 o[HD / 32];
-#pragma unroll
-    for (int b = 0; b < HD / 32; b++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) o[b][r] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
-    if (nblk > 0) {
-        gload(c.k_lo);
-        sstore(0);
-    }
-    __syncthreads();
-    for (int b = 0; b < nblk; b++) {
-        const int kb = c.k_lo + b * KB, buf = b & 1;
-        if (b + 1 < nblk) gload(kb + KB);
-        if (block_active(wq0, wq1, kb, c.k_hi, W)) {
-            f32x16 s;
-#pragma unroll
-            for (int r = 0; r < 16; r++) s[r] = 0.0f;
-            const _Float16 *kr = &Ks[buf][li][(HD / 2) * hf];
-#pragma unroll
-            for (int j = 0; j < NQ8; j++) {
-                const f16x8 kf = *reinterpret_cast<const f16x8 *>(kr + 8 * j);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], s, 0, 0, 0);
-            }
-            float sv[16];
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                const bool vis = qvalid && key < c.k_hi && (!W || abs(tq - key) <= (int)W);
-                sv[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
-            }
-            const float alpha = softmax_step(sv, m_run, l_run);
-#pragma unroll
-            for (int d = 0; d < HD / 32; d++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) o[d][r] *= alpha;
-            // B operand: this lane's p for keys 16*s2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
-#pragma unroll
-            for (int s2 = 0; s2 < 2; s2++) {
-                f16x8 pb;
-#pragma unroll
-                for (int e = 0; e < 8; e++) pb[e] = (_Float16)sv[8 * s2 + e];
-#pragma unroll
-                for (int d = 0; d < HD / 32; d++) {
-                    const _Float16 *vr = &Vt[buf][32 * d + li][16 * s2 + 4 * hf];
-                    const f16x4 v0 = *reinterpret_cast<const f16x4 *>(vr);
-                    const f16x4 v1 = *reinterpret_cast<const f16x4 *>(vr + 8);
-                    const f16x8 va = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb, o[d], 0, 0, 0);
-                }
-            }
-        }
-        if (b + 1 < nblk) sstore(buf ^ 1);
-        __syncthreads();
-    }
-    if (qvalid) {
-        const float inv = 1.0f / l_run;
-        _Float16 *out = reinterpret_cast<_Float16 *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
-#pragma unroll
-        for (int d = 0; d < HD / 32; d++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
-                           (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
-                *reinterpret_cast<f16x4 *>(out + 32 * d + 8 * q + 4 * hf) = v;
-            }
-    }
-}
-
-}  // namespace
-
-hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s) {
-    const uint32_t blocks = a.ntiles * a.nq;
-    if (!blocks) return hipSuccess;
+hipError_t launch_attn_f32(const AttnArgs &a0, uint32_t hd, hipStream_t s) {
+    AttnArgs a = a0;
+    const uint32_t tiles = attn::plan_tiles(a, f32path::kQT);
+    if (!tiles) return hipSuccess;
     if (hd == 64)
-        hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(f32path::attn_f32_kernel<64>, dim3(tiles * a.nq), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(f32path::attn_f32_kernel<128>, dim3(tiles * a.nq), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s) {
-    const uint32_t blocks = a.ntiles * a.nq;
-    if (!blocks) return hipSuccess;
-    if (hd == 64)
-        hipLaunchKernelGGL(attn_f16_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(attn_f16_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (hd == 64) return attn::launch<64, true, 4, 4, true>(a, s);
+    return attn::launch<128, true, 4, 2, true>(a, s);
 }
 
 }  // namespace enc

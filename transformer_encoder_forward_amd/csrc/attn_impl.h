@@ -1,0 +1,313 @@
+// Non-causal flash attention over packed items on gfx950 MFMA: the kernel
+// template (attn.hip picks the instantiation).
+//
+// What it computes: egemma2.rs (cortiq-engine 0.8.39), module doc "Attention"
+// and `att_plan` (bidirectional window: keys [q0 - W, q_last + W] clipped to
+// the sequence; GQA head map h / (nq / nkv)), and the staged flash of
+// `VisionGpu::forward`; zimage.rs (cortiq-engine 0.7.6), module doc (flash with
+// K/V blocks staged in threadgroup memory; an item = its image range plus its
+// caption range, `PFa`).  Online softmax: no score matrix is written.
+//
+// Design for CDNA4: a block of NW waves takes 32*NW queries of one item and
+// one head; each wave owns 32 queries.  Per 32-key block the wave computes the
+// TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs, so lane l holds query l%32
+// and 16 of the block's keys: the row max and row sum are 16 lane-local steps
+// plus one exchange with lane l^32, and P^T is already in the B-operand layout
+// of O^T = V^T P^T.  K/V blocks are double-buffered in LDS and shared by the
+// block's waves.  VALU work per score is kept small: blocks that lie wholly
+// inside every query's window skip the mask, and the running output is
+// rescaled only when some query's running max actually grew (otherwise the
+// factor is exactly 1).  Waves whose queries see none of a block skip it.  The
+// softmax runs in base 2 with log2(e) folded into the scale.
+//  - f32 path: v_mfma_f32_32x32x2_f32 for both products.
+//  - f16 path: v_mfma_f32_32x32x16_f16; V is staged transposed in LDS as key
+//    pairs (one 32-bit write per channel and pair), so the A operand of O^T is
+//    two 8-byte reads; P is rounded to f16 for P V, the softmax stays f32.
+#pragma once
+#include <math.h>
+
+#include <type_traits>
+
+#include "dev.h"
+#include "kern.h"
+
+namespace enc {
+namespace attn {
+
+constexpr int KB = 32;  // keys per block
+
+struct ItemCtx {
+    AttnItemK it;
+    int L, q_lo, q_hi, k_lo, k_hi;
+};
+
+template <int QT>
+__device__ __forceinline__ void locate(const AttnArgs &a, uint32_t tile, ItemCtx &c) {
+    uint32_t sel = 0;
+    for (uint32_t i = 1; i < a.nitems; i++)
+        if (tile >= a.items[i].tile0) sel = i;
+    c.it = a.items[sel];
+    c.L = (int)(c.it.na + c.it.nb);
+    c.q_lo = (int)(tile - c.it.tile0) * QT;
+    c.q_hi = min(c.q_lo + QT, c.L);
+    c.k_lo = 0;
+    c.k_hi = c.L;
+    if (a.window) {
+        c.k_lo = max(0, c.q_lo - (int)a.window);
+        c.k_hi = min(c.L, c.q_hi + (int)a.window);
+    }
+}
+
+__device__ __forceinline__ int row_of(const AttnItemK &it, int t) {
+    return t < (int)it.na ? (int)it.r0a + t : (int)it.r0b + (t - (int)it.na);
+}
+
+// OPT: the mask fast path and the lazy rescale (they pay off where the VALU
+// competes with fast FP16 MFMAs; with FP32 MFMAs they only cost registers).
+template <int HD, bool F16, int NW, int MINW, bool OPT>
+__global__ __launch_bounds__(64 * NW, MINW) void attn_kernel(AttnArgs a) {
+    using T = typename std::conditional<F16, _Float16, float>::type;
+    constexpr int QT = 32 * NW, NT = 64 * NW;
+    constexpr int CE = F16 ? 8 : 4;              // elements per 16-byte chunk
+    constexpr int LDK = HD + CE;                 // K rows (elements)
+    // f16: V^T rows of KB/2 key pairs (u32), stride 18 words so that the four
+    // channel groups one staging instruction writes land on distinct banks; f32: V rows
+    constexpr int LDV = F16 ? KB / 2 + 2 : HD + 8;
+    constexpr int KU = KB * HD / CE;                            // K chunks per block
+    constexpr int VU = F16 ? (KB / 2) * (HD / 8) : KB * HD / CE;  // V units per block
+    constexpr int NKC = (KU + NT - 1) / NT, NVC = (VU + NT - 1) / NT;  // per thread
+    __shared__ __attribute__((aligned(16))) T Ks[2][KB][LDK];
+    using VS = typename std::conditional<F16, uint32_t, float>::type;
+    __shared__ __attribute__((aligned(16))) VS Vs[2][F16 ? HD : KB][LDV];
+
+    const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
+    ItemCtx c;
+    locate<QT>(a, tile, c);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int kvh = head / a.group;
+    const T *P = reinterpret_cast<const T *>(a.qkv);
+    const int W = (int)a.window;
+
+    const int tq = c.q_lo + wave * 32 + li;
+    const bool qvalid = tq < c.q_hi;
+    const int wq0 = c.q_lo + wave * 32, wq1 = min(wq0 + 32, c.q_hi);
+
+    // this lane's query, channels (hd/2)*hf .. +hd/2 (its half of each dot product)
+    using QF = typename std::conditional<F16, f16x8, f32x4>::type;
+    constexpr int NQ = HD / 2 / CE;
+    QF qf[NQ];
+    {
+        const T *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col + head * HD + (HD / 2) * hf;
+#pragma unroll
+        for (int j = 0; j < NQ; j++) qf[j] = qvalid ? *reinterpret_cast<const QF *>(qp + CE * j) : QF{};
+    }
+
+    QF rk[NKC];
+    QF rv[F16 ? 2 * NVC : NVC];
+    auto gload = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < NKC; i++) {
+            const int f = tid + NT * i, key = f / (HD / CE), ch = (f % (HD / CE)) * CE;
+            const int t = kb + key;
+            rk[i] = (f < KU && t < c.k_hi) ? *reinterpret_cast<const QF *>(P + (size_t)row_of(c.it, t) * a.ld + a.k_col +
+                                                               kvh * HD + ch)
+                               : QF{};
+        }
+        if constexpr (F16) {
+            // unit = (key pair p, 8 channels ch..ch+7): rows 2p and 2p+1;
+            // consecutive lanes take consecutive pairs
+#pragma unroll
+            for (int i = 0; i < NVC; i++) {
+                const int f = tid + NT * i, p = f % (KB / 2), ch = (f / (KB / 2)) * 8;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int t = kb + 2 * p + h;
+                    rv[2 * i + h] = (f < VU && t < c.k_hi) ? *reinterpret_cast<const QF *>(P + (size_t)row_of(c.it, t) * a.ld +
+                                                                               a.v_col + kvh * HD + ch)
+                                               : QF{};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NVC; i++) {
+                const int f = tid + NT * i, key = f / (HD / CE), ch = (f % (HD / CE)) * CE;
+                const int t = kb + key;
+                rv[i] = (f < VU && t < c.k_hi) ? *reinterpret_cast<const QF *>(P + (size_t)row_of(c.it, t) * a.ld + a.v_col +
+                                                                   kvh * HD + ch)
+                                   : QF{};
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NKC; i++) {
+            const int f = tid + NT * i, key = f / (HD / CE), ch = (f % (HD / CE)) * CE;
+            if (f < KU) *reinterpret_cast<QF *>(&Ks[buf][key][ch]) = rk[i];
+        }
+        if constexpr (F16) {
+#pragma unroll
+            for (int i = 0; i < NVC; i++) {
+                const int f = tid + NT * i, p = f % (KB / 2), ch = (f / (KB / 2)) * 8;
+                if (f < VU) {
+#pragma unroll
+                    for (int e = 0; e < 8; e++) {
+                        const f16x2 pr = {rv[2 * i][e], rv[2 * i + 1][e]};
+                        Vs[buf][ch + e][p] = __builtin_bit_cast(uint32_t, pr);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NVC; i++) {
+                const int f = tid + NT * i, key = f / (HD / CE), ch = (f % (HD / CE)) * CE;
+                if (f < VU) *reinterpret_cast<f32x4 *>(&Vs[buf][key][ch]) = rv[i];
+            }
+        }
+    };
+
+    f32x16 o[HD / 32];
+#pragma unroll
+    for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
+    if (nblk > 0) {
+        gload(c.k_lo);
+        sstore(0);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; b++) {
+        const int kb = c.k_lo + b * KB, buf = b & 1;
+        if (b + 1 < nblk) gload(kb + KB);
+        // does any (query, key) pair of this wave x block pass the mask?
+        const bool active = wq0 < wq1 && kb < c.k_hi &&
+                            (!W || (kb <= wq1 - 1 + W && kb + KB - 1 >= wq0 - W));
+        if (active) {
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; r++) s[r] = 0.0f;
+            const T *kr = &Ks[buf][li][(HD / 2) * hf];
+#pragma unroll
+            for (int j = 0; j < NQ; j++) {
+                const QF kf = *reinterpret_cast<const QF *>(kr + CE * j);
+                if constexpr (F16) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], s, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[j][e], s, 0, 0, 0);
+                }
+            }
+            // every pair visible: all 32 queries valid, all keys inside the item
+            // and inside every query's window
+            const bool full = OPT && wq1 - wq0 == 32 && kb + KB <= c.k_hi &&
+                              (!W || (wq1 - 1 - kb <= W && kb + KB - 1 - wq0 <= W));
+            float sv[16];
+            if (full) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) sv[r] = s[r] * a.scale_log2;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    const bool vis = qvalid && key < c.k_hi && (!W || abs(tq - key) <= W);
+                    sv[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
+                }
+            }
+            float mx = sv[0];
+#pragma unroll
+            for (int r = 1; r < 16; r++) mx = fmaxf(mx, sv[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);
+            // the output and the running sum are rescaled only when some query's
+            // max grew; otherwise the factor would be exactly 1
+            if (!OPT || __any(m_new > m_run)) {
+                const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+                l_run *= alpha;
+#pragma unroll
+                for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                sv[r] = exp2f(sv[r] - m_use);
+                rs += sv[r];
+            }
+            l_run += rs + __shfl_xor(rs, 32, 64);
+            if constexpr (F16) {
+                // B operand: this lane's p for keys 16*s2 + {4hf..4hf+3, 8+4hf..8+4hf+3}
+#pragma unroll
+                for (int s2 = 0; s2 < 2; s2++) {
+                    f16x8 pb;
+#pragma unroll
+                    for (int e = 0; e < 8; e++) pb[e] = (_Float16)sv[8 * s2 + e];
+#pragma unroll
+                    for (int d = 0; d < HD / 32; d++) {
+                        const uint32_t *vr = &Vs[buf][32 * d + li][8 * s2 + 2 * hf];
+                        const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
+                        const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 4);
+                        const uint4 vv = {v0.x, v0.y, v1.x, v1.y};
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb, o[d], 0, 0, 0);
+                    }
+                }
+            } else {
+                // O^T[d][q] += V^T[d][key] P^T[key][q]; step r pairs lane halves' keys
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const float *vr = &Vs[buf][8 * (r >> 2) + 4 * hf + (r & 3)][li];
+#pragma unroll
+                    for (int d = 0; d < HD / 32; d++)
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * d], sv[r], o[d], 0, 0, 0);
+                }
+            }
+        }
+        if (b + 1 < nblk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+    if (qvalid) {
+        const float inv = 1.0f / l_run;
+        T *out = reinterpret_cast<T *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int ch = 32 * d + 8 * q + 4 * hf;
+                if constexpr (F16) {
+                    f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
+                               (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
+                    *reinterpret_cast<f16x4 *>(out + ch) = v;
+                } else {
+                    st4(out + ch, f32x4{o[d][4 * q] * inv, o[d][4 * q + 1] * inv, o[d][4 * q + 2] * inv,
+                                        o[d][4 * q + 3] * inv});
+                }
+            }
+    }
+}
+
+// Tiles of the launch for QT queries per block (fills tile0, ntiles).
+inline uint32_t plan_tiles(AttnArgs &a, int QT) {
+    uint32_t tiles = 0;
+    for (uint32_t i = 0; i < a.nitems; i++) {
+        a.items[i].tile0 = tiles;
+        tiles += (a.items[i].na + a.items[i].nb + QT - 1) / QT;
+    }
+    a.ntiles = tiles;
+    return tiles;
+}
+
+template <int HD, bool F16, int NW, int MINW, bool OPT>
+hipError_t launch(AttnArgs a, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(a, 32 * NW);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((attn_kernel<HD, F16, NW, MINW, OPT>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace attn
+}  // namespace enc

@@ -153,7 +153,7 @@ __device__ __forceinline__ void store_block(const GemmArgs &a, const TileCtx &t,
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB, bool PRIO = false>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) {
     using E = Elem<I8>;
     using T = typename E::T;
@@ -272,6 +272,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) 
 #pragma unroll
             for (int q = 0; q < NV; q++)
                 fb[j][q] = *reinterpret_cast<const V *>(&Bs[buf][wc * (BN / WGN) + j * 32 + li][HK * hf + CE * q]);
+        // the MFMA phase runs at raised wave priority, so a wave ready to issue
+        // matrix ops wins over a wave of the other block that is staging
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < NSTEP; kk++)
 #pragma unroll
@@ -284,6 +287,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk / 4][kk % 4], fb[j][kk / 4][kk % 4],
                                                                         acc[i][j], 0, 0, 0);
                 }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         if (s + 1 < nst) sstore(buf ^ 1);
         __syncthreads();
     }
@@ -309,11 +313,11 @@ inline uint32_t plan_tiles(GemmArgs &g, int BM, int BN) {
     return tiles;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB, bool PRIO = false>
 hipError_t launch(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WGM, WGN, I8, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WGM, WGN, I8, MINB, PRIO>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
     return hipGetLastError();
 }
 
@@ -684,6 +688,139 @@ hipError_t launch_gated(GemmArgs g, hipStream_t s) {
     if (!tiles) return hipSuccess;
     hipLaunchKernelGGL((gemm_gated_kernel<BM, BN, BK, WGM, I8, MINB>), dim3(tiles), dim3(64 * WGM * (BN / 64)), 0, s,
                        g);
+    return hipGetLastError();
+}
+
+// int8 x f16 with W bypassing LDS: each wave loads its own W fragments (the
+// 32-byte K run a lane half owns in a stage, for each of its FN column blocks)
+// straight from global memory into registers two stages ahead, and widens them
+// to f16 right before the MFMAs (8 int8 -> 8 f16 per k-step).  Only X is
+// staged through LDS, halving LDS traffic and removing W's staging writes.
+// Same K order as gemm_kernel<.., BK, .., true, ..>: bit-identical results.
+__device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
+    const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u0, 0x05010400u)) - bias;
+    const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u0, 0x05030402u)) - bias;
+    const f16x2 c = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u1, 0x05010400u)) - bias;
+    const f16x2 d = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u1, 0x05030402u)) - bias;
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int MINB>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_i8_v3_kernel(GemmArgs a) {
+    constexpr int NT = 64 * WGM * WGN;
+    constexpr int CE = 8;
+    constexpr int LDS = BK + CE;
+    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
+    constexpr int HK = BK / 2;           // k per lane half per stage
+    constexpr int NSTEP = BK / 16;
+    constexpr int A_CH = BM * BK / CE / NT;
+    constexpr int BW = HK / 4;           // 32-bit words of W per lane per column block per stage
+    static_assert(BM * BK % (CE * NT) == 0 && HK % 16 == 0, "tile");
+
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][LDS];
+    TileCtx t;
+    if (!locate<BM, BN>(a, t)) return;
+    const int n = t.it.n, m = t.it.m, K = t.it.k;
+    const _Float16 *X = reinterpret_cast<const _Float16 *>(a.x) + t.it.x_off;
+    const int8_t *Wq = reinterpret_cast<const int8_t *>(t.w);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    f16x8 ra[A_CH];
+    uint32_t wb[2][FN][BW];  // W register ring: two stages
+    auto aload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            const int gk = k0 + c, gr = t.row0 + r;
+            ra[i] = (gr < n && gk < K) ? *reinterpret_cast<const f16x8 *>(X + (size_t)gr * t.it.ldx + gk)
+                                       : f16x8{};
+        }
+    };
+    auto astore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; i++) {
+            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
+            *reinterpret_cast<f16x8 *>(&As[buf][r][c]) = ra[i];
+        }
+    };
+    auto wload = [&](int k0, uint32_t (&w)[FN][BW]) {
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int gc = t.col0 + wc * (BN / WGN) + j * 32 + li, gk = k0 + HK * hf;
+            const uint4 *p = reinterpret_cast<const uint4 *>(Wq + (size_t)gc * K + gk);
+#pragma unroll
+            for (int q = 0; q < BW / 4; q++) {
+                // 16-byte chunks: K % 16 == 0, so a chunk is wholly inside or outside
+                const uint4 v = (gc < m && gk + 16 * q < K) ? p[q] : uint4{0, 0, 0, 0};
+                w[j][4 * q] = v.x;
+                w[j][4 * q + 1] = v.y;
+                w[j][4 * q + 2] = v.z;
+                w[j][4 * q + 3] = v.w;
+            }
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    auto compute = [&](int buf, const uint32_t (&w)[FN][BW]) {
+#pragma unroll
+        for (int kk = 0; kk < NSTEP; kk++) {
+            f16x8 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+                fa[i] = *reinterpret_cast<const f16x8 *>(&As[buf][wr * (BM / WGM) + i * 32 + li][HK * hf + 8 * kk]);
+#pragma unroll
+            for (int j = 0; j < FN; j++) fb[j] = widen8(w[j][2 * kk], w[j][2 * kk + 1]);
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    const int nst = (K + BK - 1) / BK;
+    aload(0);
+    wload(0, wb[0]);
+    if (nst > 1) wload(BK, wb[1]);
+    astore(0);
+    __syncthreads();
+    for (int s = 0; s < nst; s += 2) {
+        if (s + 1 < nst) aload((s + 1) * BK);
+        compute(0, wb[0]);
+        if (s + 2 < nst) wload((s + 2) * BK, wb[0]);
+        if (s + 1 < nst) astore(1);
+        __syncthreads();
+        if (s + 1 >= nst) break;
+        if (s + 2 < nst) aload((s + 2) * BK);
+        compute(1, wb[1]);
+        if (s + 3 < nst) wload((s + 3) * BK, wb[1]);
+        if (s + 2 < nst) astore(0);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+            store_block<true>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
+                              lane);
+}
+
+template <int BM, int BN, int BK, int WGM, int WGN, int MINB>
+hipError_t launch_i8_v3(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, BM, BN);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((gemm_i8_v3_kernel<BM, BN, BK, WGM, WGN, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
     return hipGetLastError();
 }
 

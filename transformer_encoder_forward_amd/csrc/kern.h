@@ -100,6 +100,5 @@ hipError_t launch_mfma_peak(bool f16, uint32_t blocks, uint32_t iters, float *ou
 
 // Tile sizes the launchers and the planner agree on.
 constexpr int kGemmBM = 128, kGemmBN = 128;
-constexpr int kAttnQTile = 128;  // queries per attention block (4 waves x 32)
 
 }  // namespace enc
