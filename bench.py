@@ -26,6 +26,30 @@ HBM_PEAK = 8000.0  # GB/s
 CPU_LAYERS = 4
 
 
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_impl.h", "gemm.hip"):
+        with open(os.path.join(ROOT, "transformer_encoder_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 --pmc summary of this
+    workload, or None when it is missing or was taken on other GEMM sources."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    src = re.search(r"gemm_source_sha256:\s*([0-9a-f]+)", txt)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.e+]+)", txt)
+    if not src or not val or src.group(1) != gemm_source_hash():
+        return None
+    return float(val.group(1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,11 +171,15 @@ def main():
                    "ff": cfg["ff"], "window": cfg["window"],
                    "gemm_gflop": round(gflop / 1e9, 2), "attn_gflop": round(aflop / 1e9, 2),
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "gemm_f32_kernel" if dtype == "f32" else "gemm_i8f16_kernel",
+        "roofline": {"kernel": "GEMM class: gemm_kernel + gemm_gated_kernel ("
+                               + ("FP32" if dtype == "f32" else "int8 x f16") + " MFMA)",
                      "bound": "mfma", "achieved": round(gemm_tf, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gemm_tf / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / peak, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "alg_bytes_per_launch": round(g["bytes"] / max(1, g["launches"])),
                      "launches_per_step": g["launches"] / args.steps,
-                     "avg_launch_ms": round(gemm_ms_launch, 5)},
+                     "avg_launch_ms": round(gemm_ms_launch, 5),
+                     "gemm_source_sha256": gemm_source_hash()},
         "classes": classes,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),

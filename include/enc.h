@@ -314,7 +314,8 @@ typedef struct {
     uint64_t launches;
     double ms;     /* summed GPU time between each launch's bracketing events */
     double flops;  /* algorithmic: 2 n m k per GEMM item; 4 hd per visible (query, key) pair per head */
-    double bytes;  /* algorithmic HBM bytes: each row op's inputs read once and outputs written once */
+    double bytes;  /* algorithmic HBM bytes: inputs read once and outputs written once (row ops;
+                      GEMM: X, the weights and Y; attention: not counted) */
 } enc_prof_stat;
 
 /* With profiling on, every kernel launch enqueued through ctx is bracketed by

@@ -215,10 +215,19 @@ void plan_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, G
 hipError_t run_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, hipStream_t s) {
     GemmArgs g;
     plan_gemm(d, items, n, g);
-    double flops = 0;
-    const double mul = (d->flags & (ENC_EPI_GATE_GELU_TANH | ENC_EPI_GATE_SILU)) ? 2.0 : 1.0;
-    for (uint32_t i = 0; i < n; i++) flops += 2.0 * mul * items[i].n * items[i].m * items[i].k;
-    return prof_launch(ENC_CLASS_GEMM, s, flops, 0.0, [&] {
+    // algorithmic work: 2 n m k flops per product; bytes = X read once, each
+    // weight matrix read once, Y written once (read too when accumulating)
+    double flops = 0, bytes = 0;
+    const bool gated = d->flags & (ENC_EPI_GATE_GELU_TANH | ENC_EPI_GATE_SILU);
+    const double mul = gated ? 2.0 : 1.0;
+    const double xs = d->path == ENC_I8F16 ? 2 : 4, ws = d->path == ENC_I8F16 ? 1 : 4;
+    const double ys = (d->flags & ENC_Y_F16) ? 2 : 4, yrw = (d->flags & ENC_Y_ACCUMULATE) ? 2 : 1;
+    for (uint32_t i = 0; i < n; i++) {
+        const enc_gemm_item &it = items[i];
+        flops += 2.0 * mul * it.n * it.m * it.k;
+        bytes += xs * it.n * it.k + ws * mul * it.m * it.k + ys * yrw * it.n * it.m;
+    }
+    return prof_launch(ENC_CLASS_GEMM, s, flops, bytes, [&] {
         return d->path == ENC_I8F16 ? launch_gemm_i8f16(g, s) : launch_gemm_f32(g, s);
     });
 }
