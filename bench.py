@@ -95,15 +95,16 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     assert torch.isfinite(out).all().item(), "non-finite output"
 
     gflop = wl.gemm_flops(w)
@@ -130,6 +131,9 @@ def main():
                for k, v in prof.items()}
     print(f"[bench] {ms:.3f} ms/step, {tflops:.2f} TFLOP/s; classes {classes}", file=sys.stderr,
           flush=True)
+
+    # the chip's MFMA ceiling for this dtype, measured by a register-only kernel
+    measured_peak = B.mfma_peak(0 if dtype == "f32" else 1, ctx=ctx)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -159,12 +163,16 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_median": round(per_step[len(per_step) // 2], 4),
+        "ms_min": round(per_step[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
         "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+        "measured_mfma_peak": round(measured_peak, 1),
+        "pct_of_measured_peak": round(100.0 * tflops / measured_peak, 2),
         "tokens_per_s_per_layer": round(w.rows / (ms * 1e-3 / cfg["layers"]), 1),
         "config": {"workload": args.workload, "rows": w.rows, "items": len(w.items),
                    "layers": cfg["layers"], "d": cfg["d"], "heads": f"{cfg['nq']}x{cfg['hd']}",

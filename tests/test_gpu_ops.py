@@ -107,7 +107,8 @@ def test_gemm_packed_rows_bit_identical():
 
 @pytest.mark.parametrize("path,act,n,ff,d", [
     (B.ENC_F32, "gelu", 1000, 2048, 512), (B.ENC_F32, "gelu", 37, 200, 128),
-    (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64)])
+    (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64),
+    (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192)])
 def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
     bit for bit, and == the oracle within tolerance."""
@@ -135,7 +136,9 @@ def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     kind = B.ENC_ACT_GELU_TANH_GATED if act == "gelu" else B.ENC_ACT_SWIGLU
     B.gated_act(gu[:, :ff], gu[:, ff:], unfused, kind, f16=i8)
     assert torch.equal(fused, unfused)
-    xd = x.astype(np.float64)
+    # the oracle's scalar activations: every row of small cases, sampled rows of large ones
+    rows = np.arange(n) if n * ff <= 2_000_000 else np.array([0, 1, 255, 256, n - 1])
+    xd = x[rows].astype(np.float64)
     if i8:
         g, u = O.linear_q8(xd, ws[0], rss[0]), O.linear_q8(xd, ws[1], rss[1])
     else:
@@ -143,7 +146,7 @@ def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     ref = np.vectorize(O.gelu_tanh if act == "gelu" else O.silu)(g) * u
     if i8:
         ref = np.vectorize(O.round_f16)(ref)
-    assert row_rel_err(host(fused), ref) <= (TOL_I8F16 if i8 else TOL_F32)
+    assert row_rel_err(host(fused)[rows], ref) <= (TOL_I8F16 if i8 else TOL_F32)
 
 
 # ------------------------------------------------------------- GEMM int8 x f16
@@ -160,6 +163,39 @@ def test_gemm_i8f16_integer_exact(n, m, k):
     B.gemm_items(to_dev(x), Y, [to_dev(q)], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
                  row_scale=[to_dev(rs)])
     assert np.array_equal(host(Y), ref)
+
+
+# shapes that take the 256 x 256 direct-to-LDS kernel (K % 64 == 0, >= 200 tiles):
+# one K stage, exactly the LDS ring, ring wrap-around; ragged rows and columns
+@pytest.mark.parametrize("n,m,k", [(520, 17000, 64), (520, 17000, 192), (513, 17000, 320)])
+def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
+    say(f"gemm i8f16 wide integer n={n} m={m} k={k}")
+    rng = np.random.default_rng(n + m + k)
+    x = rng.integers(-16, 17, (n, k)).astype(np.float16)
+    q = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    rs = (2.0 ** -rng.integers(0, 10, m)).astype(np.float32)
+    ref = O.linear_q8(x.astype(np.float64), q, rs)
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(q)], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
+                 row_scale=[to_dev(rs)])
+    assert np.array_equal(host(Y), ref)
+
+
+def test_gemm_i8f16_kernel_choice_bit_identical():
+    """Rows computed in a launch of 256 x 256 tiles and in small launches of
+    128 x 128 tiles give the same bits (one K order for every int8 kernel)."""
+    rng = np.random.default_rng(77)
+    n, m, k = 520, 17000, 256
+    x = rng.normal(0, 1, (n, k)).astype(np.float16)
+    W = to_dev(rng.integers(-127, 128, (m, k)).astype(np.int8))
+    rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32))]
+    Yall = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Yall, [W], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs)
+    for r0, r1 in ((0, 1), (250, 300), (450, 520)):
+        Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
+        B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
+                     row_scale=rs)
+        assert torch.equal(Y, Yall[r0:r1])
 
 
 def test_gemm_i8f16_f16_output_and_items():

@@ -691,12 +691,7 @@ hipError_t launch_gated(GemmArgs g, hipStream_t s) {
     return hipGetLastError();
 }
 
-// int8 x f16 with W bypassing LDS: each wave loads its own W fragments (the
-// 32-byte K run a lane half owns in a stage, for each of its FN column blocks)
-// straight from global memory into registers two stages ahead, and widens them
-// to f16 right before the MFMAs (8 int8 -> 8 f16 per k-step).  Only X is
-// staged through LDS, halving LDS traffic and removing W's staging writes.
-// Same K order as gemm_kernel<.., BK, .., true, ..>: bit-identical results.
+// 8 int8 (two 32-bit words) -> 8 f16, exact (the widen16 construction).
 __device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
     const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
     const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
@@ -707,61 +702,140 @@ __device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int MINB>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_i8_v3_kernel(GemmArgs a) {
-    constexpr int NT = 64 * WGM * WGN;
-    constexpr int CE = 8;
-    constexpr int LDS = BK + CE;
-    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
-    constexpr int HK = BK / 2;           // k per lane half per stage
-    constexpr int NSTEP = BK / 16;
-    constexpr int A_CH = BM * BK / CE / NT;
-    constexpr int BW = HK / 4;           // 32-bit words of W per lane per column block per stage
-    static_assert(BM * BK % (CE * NT) == 0 && HK % 16 == 0, "tile");
+// ---------------------------------------------------------------------------
+// int8 x f16 GEMM fed by direct global -> LDS loads (global_load_lds_dwordx4).
+//
+// 256 x 256 block tile, 8 waves as 2 x 4, each wave 128 x 64 outputs (4 x 2
+// accumulator blocks), W kept as int8 in LDS and widened per fragment.  Three
+// LDS stages of 64 K each (48 KB): the loads of stage s+3 are issued as soon
+// as every wave has finished reading stage s, so two stages of loads are in
+// flight while one is computed, and no register holds staged data.
+//
+// A load instruction writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so
+// the LDS tiles are swizzled instead of padded: X row r (128 bytes = 8 chunks
+// of 8 halves) keeps chunk c at position c ^ ((r >> 1) & 7); W row r (64 bytes
+// = 4 chunks of 16 int8) keeps chunk c at position c ^ ((r >> 2) & 3).  Every
+// 16 consecutive lanes of a fragment read then hit 16 distinct bank groups.
+//
+// The compiler cannot tell LDS reads apart from the in-flight LDS-bound loads
+// and would wait for all of them before every read, so the fragment reads are
+// issued as ds_read_b128 in inline assembly and their completion is awaited
+// explicitly (lgkmcnt), tying the fragment registers to the wait.
+//
+// Same K order as gemm_kernel<.., 64, .., true, ..>: stage 64, lane half h
+// owns k in [32h, 32h + 32), k-step kk the 8 values at 32h + 8kk.  Requires
+// K % 64 == 0.  Rows past n and columns past m load clamped (finite) rows and
+// are never stored.
+#define ENC_GLOBAL(p) ((const void __attribute__((address_space(1))) *)(p))
+#define ENC_SHARED(p) ((void __attribute__((address_space(3))) *)(p))
 
-    __shared__ __attribute__((aligned(16))) _Float16 As[2][BM][LDS];
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)ENC_SHARED(const_cast<void *>(p));
+}
+
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3, u32x4 &b0, u32x4 &b1) {
+    asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits
+    // [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8] at maximum)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
+    constexpr int BM = 256, BN = 256, WGN = 4, BK = 64, FM = 4, FN = 2, NS = 3;
+    constexpr int A_BYTES = BM * BK * 2, S_BYTES = A_BYTES + BN * BK;
+    constexpr int NDMA = 6;  // load instructions per wave per stage (4 X + 2 W)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
+
     TileCtx t;
-    if (!locate<BM, BN>(a, t)) return;
+    if (!locate<BM, BN>(a, t, GATED ? BN / 2 : BN)) return;
+    const int8_t *wg = reinterpret_cast<const int8_t *>(t.w), *wu = wg;
+    const float *rg = t.rs, *ru = t.rs;
+    if constexpr (GATED) {
+        wu = reinterpret_cast<const int8_t *>(a.w[1]);
+        ru = a.rs[1];
+#pragma unroll
+        for (int s2 = 1; s2 < kMaxGemmItems; s2++)
+            if ((int)t.it.slot + 1 == s2) {
+                wu = reinterpret_cast<const int8_t *>(a.w[s2]);
+                ru = a.rs[s2];
+            }
+    }
     const int n = t.it.n, m = t.it.m, K = t.it.k;
     const _Float16 *X = reinterpret_cast<const _Float16 *>(a.x) + t.it.x_off;
-    const int8_t *Wq = reinterpret_cast<const int8_t *>(t.w);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hf = lane >> 5;
     const int wr = wave / WGN, wc = wave % WGN;
 
-    f16x8 ra[A_CH];
-    uint32_t wb[2][FN][BW];  // W register ring: two stages
-    auto aload = [&](int k0) {
+    // sources of this lane's load instructions (k offset added per stage)
+    const _Float16 *asrc[4];
 #pragma unroll
-        for (int i = 0; i < A_CH; i++) {
-            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
-            const int gk = k0 + c, gr = t.row0 + r;
-            ra[i] = (gr < n && gk < K) ? *reinterpret_cast<const f16x8 *>(X + (size_t)gr * t.it.ldx + gk)
-                                       : f16x8{};
+    for (int q = 0; q < 4; q++) {
+        const int r = 8 * (4 * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        asrc[q] = X + (size_t)min(t.row0 + r, n - 1) * t.it.ldx + 8 * c;
+    }
+    const int8_t *bsrc[2];
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int r = 16 * (2 * wave + q) + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+        const int8_t *w = wg;
+        int col = t.col0 + r;
+        if constexpr (GATED) {
+            w = ((r >> 5) & 1) ? wu : wg;
+            col = t.col0 + (r >> 6) * 32 + (r & 31);
         }
+        bsrc[q] = w + (size_t)min(col, m - 1) * K + 16 * c;
+    }
+    auto dma = [&](int s) {
+        uint8_t *buf = smem + (s % NS) * S_BYTES;
+        const int k0 = s * BK;
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(asrc[q] + k0), ENC_SHARED(buf + (4 * wave + q) * 1024), 16,
+                                             0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(bsrc[q] + k0),
+                                             ENC_SHARED(buf + A_BYTES + (2 * wave + q) * 1024), 16, 0, 0);
     };
-    auto astore = [&](int buf) {
+
+    // fragment addresses: X row wr*128 + 32 i + li, chunk 4 hf + kk; W row
+    // wc*64 + 32 j + li, chunk 2 hf + p (p = kk / 2, one read per two k-steps)
+    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t arow = lds0 + (uint32_t)(wr * 128 + li) * 128u;
+    const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * 64 + li) * 64u;
+    const int sa = (li >> 1) & 7, sb = (li >> 2) & 3;
+    uint32_t asw[4], bsw[2];
 #pragma unroll
-        for (int i = 0; i < A_CH; i++) {
-            const int f = tid + NT * i, r = f / (BK / CE), c = (f % (BK / CE)) * CE;
-            *reinterpret_cast<f16x8 *>(&As[buf][r][c]) = ra[i];
-        }
+    for (int kk = 0; kk < 4; kk++) asw[kk] = (uint32_t)(((4 * hf + kk) ^ sa) * 16);
+#pragma unroll
+    for (int p = 0; p < 2; p++) bsw[p] = (uint32_t)(((2 * hf + p) ^ sb) * 16);
+
+    u32x4 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+    auto read_a = [&](u32x4 (&d)[FM], int b, int kk) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) d[i] = ds_read16(arow + b * S_BYTES + 4096 * i + asw[kk]);
     };
-    auto wload = [&](int k0, uint32_t (&w)[FN][BW]) {
+    auto read_b = [&](u32x4 (&d)[FN], int b, int p) {
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int gc = t.col0 + wc * (BN / WGN) + j * 32 + li, gk = k0 + HK * hf;
-            const uint4 *p = reinterpret_cast<const uint4 *>(Wq + (size_t)gc * K + gk);
-#pragma unroll
-            for (int q = 0; q < BW / 4; q++) {
-                // 16-byte chunks: K % 16 == 0, so a chunk is wholly inside or outside
-                const uint4 v = (gc < m && gk + 16 * q < K) ? p[q] : uint4{0, 0, 0, 0};
-                w[j][4 * q] = v.x;
-                w[j][4 * q + 1] = v.y;
-                w[j][4 * q + 2] = v.z;
-                w[j][4 * q + 3] = v.w;
-            }
-        }
+        for (int j = 0; j < FN; j++) d[j] = ds_read16(brow + b * S_BYTES + 2048 * j + bsw[p]);
     };
 
     f32x16 acc[FM][FN];
@@ -771,56 +845,92 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_i8_v3_kernel(GemmAr
         for (int j = 0; j < FN; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
-
-    auto compute = [&](int buf, const uint32_t (&w)[FN][BW]) {
+    auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int half) {
 #pragma unroll
-        for (int kk = 0; kk < NSTEP; kk++) {
-            f16x8 fa[FM], fb[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++)
-                fa[i] = *reinterpret_cast<const f16x8 *>(&As[buf][wr * (BM / WGM) + i * 32 + li][HK * hf + 8 * kk]);
-#pragma unroll
-            for (int j = 0; j < FN; j++) fb[j] = widen8(w[j][2 * kk], w[j][2 * kk + 1]);
+        for (int j = 0; j < FN; j++) {
+            const f16x8 b = widen8(fb[j][2 * half], fb[j][2 * half + 1]);
 #pragma unroll
             for (int i = 0; i < FM; i++)
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[i]), b, acc[i][j], 0,
+                                                                   0, 0);
         }
     };
 
-    const int nst = (K + BK - 1) / BK;
-    aload(0);
-    wload(0, wb[0]);
-    if (nst > 1) wload(BK, wb[1]);
-    astore(0);
-    __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-        if (s + 1 < nst) aload((s + 1) * BK);
-        compute(0, wb[0]);
-        if (s + 2 < nst) wload((s + 2) * BK, wb[0]);
-        if (s + 1 < nst) astore(1);
-        __syncthreads();
-        if (s + 1 >= nst) break;
-        if (s + 2 < nst) aload((s + 2) * BK);
-        compute(1, wb[1]);
-        if (s + 3 < nst) wload((s + 3) * BK, wb[1]);
-        if (s + 2 < nst) astore(0);
-        __syncthreads();
+    const int nst = K / BK;
+    dma(0);
+    if (nst > 1) dma(1);
+    if (nst > 2) dma(2);
+    if (nst > 2)
+        vm_wait<2 * NDMA>();
+    else if (nst > 1)
+        vm_wait<NDMA>();
+    else
+        vm_wait<0>();
+    block_barrier();
+    read_a(fa0, 0, 0);
+    read_b(fb0, 0, 0);
+    for (int s = 0; s < nst; s++) {
+        const int b = s % NS;
+        read_a(fa1, b, 1);
+        lgkm_wait<4>(fa0[0], fa0[1], fa0[2], fa0[3], fb0[0], fb0[1]);
+        mma(fa0, fb0, 0);
+        read_a(fa0, b, 2);
+        read_b(fb1, b, 1);
+        lgkm_wait<6>(fa1[0], fa1[1], fa1[2], fa1[3], fb0[0], fb0[1]);
+        mma(fa1, fb0, 1);
+        read_a(fa1, b, 3);
+        lgkm_wait<4>(fa0[0], fa0[1], fa0[2], fa0[3], fb1[0], fb1[1]);
+        mma(fa0, fb1, 0);
+        // stage s+1 landed (own loads), own reads of buffer b done; after the
+        // barrier every wave's are, so b takes stage s+3
+        if (s + 2 < nst)
+            vm_wait<NDMA>();
+        else
+            vm_wait<0>();
+        lgkm_wait<0>(fa1[0], fa1[1], fa1[2], fa1[3], fb1[0], fb1[1]);
+        block_barrier();
+        if (s + 3 < nst) dma(s + 3);
+        if (s + 1 < nst) {
+            read_a(fa0, (s + 1) % NS, 0);
+            read_b(fb0, (s + 1) % NS, 0);
+        }
+        mma(fa1, fb1, 1);
     }
+
+    if constexpr (!GATED) {
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+        for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++)
-            store_block<true>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
-                              lane);
+            for (int j = 0; j < FN; j++)
+                store_block<true>(a, t, acc[i][j], t.row0 + wr * 128 + i * 32, t.col0 + wc * 64 + j * 32, lane);
+    } else {
+        const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
+        const int c = t.col0 + wc * 32 + li;
+        if (c < m) {
+            const float mg = a.alpha * rg[c], mu = a.alpha * ru[c];
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int row = t.row0 + wr * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (row >= n) continue;
+                    const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
+                    const float v = (gelu ? gelu_tanh(g) : silu(g)) * u;
+                    const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
+                    if (f16)
+                        reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+                    else
+                        reinterpret_cast<float *>(a.y)[off] = v;
+                }
+        }
+    }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, int MINB>
-hipError_t launch_i8_v3(GemmArgs g, hipStream_t s) {
-    const uint32_t tiles = plan_tiles(g, BM, BN);
+template <bool GATED>
+hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, 256, GATED ? 128 : 256);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_i8_v3_kernel<BM, BN, BK, WGM, WGN, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    hipLaunchKernelGGL((gemm_q8d_kernel<GATED>), dim3(tiles), dim3(512), 0, s, g);
     return hipGetLastError();
 }
 
