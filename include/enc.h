@@ -330,8 +330,10 @@ ENC_API enc_status enc_prof_read(enc_ctx *ctx, enc_prof_stat *stats);
  * independent accumulators and no memory traffic).  One launch of `blocks`
  * 256-thread blocks, each wave issuing iters x 16 MFMAs (ENC_F32:
  * v_mfma_f32_32x32x2_f32; ENC_I8F16: v_mfma_f32_32x32x16_f16, the GEMMs'
- * instructions); writes blocks*256 floats to out (dev) and the launch's
- * flops to *flops.  Time it with events on `stream`. */
+ * instructions) on random operands that change from one MFMA to the next, as
+ * in a GEMM (constant operands let the chip hold a higher clock than real data
+ * does); writes blocks*256 floats to out (dev) and the launch's flops to
+ * *flops.  Time it with events on `stream`. */
 ENC_API enc_status enc_mfma_peak(enc_ctx *ctx, uint32_t path, uint32_t blocks, uint32_t iters,
                                  float *out, double *flops, enc_stream stream);
 
