@@ -99,10 +99,11 @@ def _setup(L):
                                   C.c_double]
     L.or_attention.argtypes = [C.c_int, C.POINTER(Item), C.c_int, C.c_int, C.c_int, _D, C.c_int,
                                _D, C.c_int, _D, C.c_int, _D, C.c_int, C.c_double, C.c_int]
+    L.or_attention_rows.argtypes = L.or_attention.argtypes + [_I8]
     L.or_encoder_forward.argtypes = [C.POINTER(Model), C.c_int64, C.c_int, C.POINTER(Item), _D,
                                      _D, C.c_int]
     for f in ("or_rms_norm", "or_layer_norm", "or_linear", "or_linear_q8", "or_positions",
-              "or_qk_norm_rope", "or_attention", "or_encoder_forward"):
+              "or_qk_norm_rope", "or_attention", "or_attention_rows", "or_encoder_forward"):
         getattr(L, f).restype = None
 
 
@@ -200,15 +201,23 @@ def qk_norm_rope(x, nh, hd, w, eps, sections, pos, base):
     return y
 
 
-def attention(items, q, k, v, nq, nkv, hd, scale, window, rows=None):
-    """Per-item softmax attention; q [rows][nq*hd], k/v [rows][nkv*hd] -> o [rows][nq*hd]."""
+def attention(items, q, k, v, nq, nkv, hd, scale, window, rows=None, query_rows=None):
+    """Per-item softmax attention; q [rows][nq*hd], k/v [rows][nkv*hd] -> o [rows][nq*hd].
+    With `query_rows`, only those output rows are computed (the others stay 0)."""
     q, qp = _d(q)
     k, kp = _d(k)
     v, vp = _d(v)
     o = np.zeros((q.shape[0], nq * hd))
     it = _items(items)
-    lib().or_attention(len(items), it, nq, nkv, hd, qp, q.shape[1], kp, k.shape[1], vp,
-                       v.shape[1], o.ctypes.data_as(_D), nq * hd, scale, window)
+    if query_rows is None:
+        lib().or_attention(len(items), it, nq, nkv, hd, qp, q.shape[1], kp, k.shape[1], vp,
+                           v.shape[1], o.ctypes.data_as(_D), nq * hd, scale, window)
+    else:
+        sel = np.zeros(q.shape[0], np.int8)
+        sel[np.asarray(query_rows)] = 1
+        lib().or_attention_rows(len(items), it, nq, nkv, hd, qp, q.shape[1], kp, k.shape[1], vp,
+                                v.shape[1], o.ctypes.data_as(_D), nq * hd, scale, window,
+                                sel.ctypes.data_as(_I8))
     return o
 
 

@@ -293,9 +293,10 @@ OR_API void or_qk_norm_rope(int64_t rows, int nh, int hd, double *x, const float
  * [ZI] `PFa` (an item = its image and caption ranges).  GQA: query head h reads
  * kv head h / (nq / nkv) ([EG] `att_plan`).  q/k/v/o are [rows][ld*] with the
  * head's hd columns at h*hd. */
-OR_API void or_attention(int nitems, const or_item *items, int nq, int nkv, int hd,
-                         const double *q, int ldq, const double *k, int ldk, const double *v,
-                         int ldv, double *o, int ldo, double scale, int window)
+static void attention_impl(int nitems, const or_item *items, int nq, int nkv, int hd,
+                           const double *q, int ldq, const double *k, int ldk, const double *v,
+                           int ldv, double *o, int ldo, double scale, int window,
+                           const char *qsel)
 {
     for (int ii = 0; ii < nitems; ii++) {
         const or_item *it = &items[ii];
@@ -306,6 +307,8 @@ OR_API void or_attention(int nitems, const or_item *items, int nq, int nkv, int 
             for (int ti = 0; ti < L; ti++) {
                 int kvh = h / group;
                 int ri = item_row(it, ti);
+                if (qsel && !qsel[ri])
+                    continue;
                 const double *qi = q + (int64_t)ri * ldq + h * hd;
                 double *s = (double *)malloc(sizeof(double) * L);
                 char *vis = (char *)malloc((size_t)L);
@@ -342,6 +345,25 @@ OR_API void or_attention(int nitems, const or_item *items, int nq, int nkv, int 
             }
         }
     }
+}
+
+OR_API void or_attention(int nitems, const or_item *items, int nq, int nkv, int hd,
+                         const double *q, int ldq, const double *k, int ldk, const double *v,
+                         int ldv, double *o, int ldo, double scale, int window)
+{
+    attention_impl(nitems, items, nq, nkv, hd, q, ldq, k, ldk, v, ldv, o, ldo, scale, window,
+                   NULL);
+}
+
+/* The same attention for the query rows r with qsel[r] != 0 only (the other
+ * output rows are left untouched): the full-size checks sample query rows. */
+OR_API void or_attention_rows(int nitems, const or_item *items, int nq, int nkv, int hd,
+                              const double *q, int ldq, const double *k, int ldk,
+                              const double *v, int ldv, double *o, int ldo, double scale,
+                              int window, const char *qsel)
+{
+    attention_impl(nitems, items, nq, nkv, hd, q, ldq, k, ldk, v, ldv, o, ldo, scale, window,
+                   qsel);
 }
 
 /* ---------------------------------------------------------------------- model */

@@ -443,3 +443,21 @@ def test_nonfinite_input_propagates(oracle):
     out = oracle.forward(w)
     assert not np.isfinite(out[:5]).all()
     assert np.isfinite(out[5:]).all()
+
+
+def test_attention_query_subset_equals_full(oracle):
+    """The query-row-subset entry returns the full attention's bits on the chosen
+    rows and leaves every other row untouched (it is the same computation)."""
+    rng = np.random.default_rng(10)
+    hd, nq, nkv, rows = 16, 4, 2, 30
+    q = rng.normal(0, 1, (rows, nq * hd))
+    k = rng.normal(0, 1, (rows, nkv * hd))
+    v = rng.normal(0, 1, (rows, nkv * hd))
+    items = [[(0, 10), (25, 5)], [(10, 15)]]
+    for window in (0, 3):
+        full = oracle.attention(items, q, k, v, nq, nkv, hd, 0.4, window)
+        sel = [0, 9, 11, 24, 27]
+        part = oracle.attention(items, q, k, v, nq, nkv, hd, 0.4, window, query_rows=sel)
+        assert np.array_equal(part[sel], full[sel])
+        rest = np.setdiff1d(np.arange(rows), sel)
+        assert not part[rest].any()
