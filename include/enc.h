@@ -167,7 +167,7 @@ ENC_API enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, cons
 /* RMSNorm y = x * w / sqrt(mean(x^2) + eps), gain multiplying directly ([EG]
  * `Prog::rms`).  LayerNorm y = (x - mean) / sqrt(var + eps) * w + b, population
  * variance ([VE] `VitGpuOps::layernorm`; b may be NULL).  Output f32, or f16
- * with ENC_Y_F16. */
+ * with ENC_Y_F16.  rows = 0 is a no-op (the pointers may then be NULL). */
 typedef struct {
     uint32_t rows, d;
     const float *x;   /* (dev) [rows][ldx] */
@@ -232,7 +232,10 @@ ENC_API enc_status enc_gated_act(enc_ctx *ctx, const enc_act_desc *desc, enc_str
 
 /* Mean of each item's rows: out[i][j] = (1/|I|) sum_{r in I} a[r][j], f32.
  * With a = rms(H) * w_final this is the final norm + mean pool of [EG]
- * `TextGpu::forward` (per-row inverse RMS, then the weighted mean). */
+ * `TextGpu::forward` (per-row inverse RMS, then the weighted mean).  Any number
+ * of items; an empty item is ENC_EINVAL (its mean is undefined).  The rows of an
+ * item are summed in a fixed order, so the result does not depend on the other
+ * items. */
 ENC_API enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a,
                          const enc_item *items, uint32_t nitems, float *out, enc_stream stream);
 
@@ -279,7 +282,8 @@ typedef struct {
 
 /* All layers share d, path and block kind.  final: NONE -> out = H [rows][d];
  * LN -> out = LN(H; final_w, final_b) [rows][d] ([VE] step 4, post-LN);
- * RMS_MEANPOOL -> out[i] = mean over item i of rms(H_r; final_w), [nitems][d]. */
+ * RMS_MEANPOOL -> out[i] = mean over item i of rms(H_r; final_w), [nitems][d]
+ * (every item must then be non-empty: ENC_EINVAL otherwise). */
 typedef struct {
     uint32_t nlayers;
     const enc_layer *layers; /* (host) */

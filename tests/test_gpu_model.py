@@ -122,3 +122,24 @@ def test_nonfinite_input_flagged():
     out = host(run(w, x=x))
     assert not np.isfinite(out[:50]).all()
     assert np.isfinite(out[50:]).all()
+
+
+def test_empty_and_one_row_sequences():
+    """A packed batch with a one-row sequence and an empty one: every row matches
+    the oracle (final RMS, no pool); with the mean pool the empty sequence is
+    refused (its mean is undefined) before anything runs."""
+    w = wl.make("gemma_text_f32", layers=2, lengths=[40, 1, 0, 25])
+    w.cfg["final"] = wl.FINAL_NONE
+    assert row_rel_err(host(run(w)), O.forward(w)) <= TOL_F32
+    w.cfg["final"] = wl.FINAL_RMS_MEANPOOL
+    with pytest.raises(RuntimeError, match="empty"):
+        run(w)
+
+
+def test_many_sequences_pooled():
+    """More sequences than one pool launch takes (64): 150 short sequences."""
+    lengths = [1 + (7 * i) % 13 for i in range(150)]
+    w = wl.make("gemma_text_f32", layers=1, lengths=lengths)
+    got = host(run(w))
+    assert got.shape == (150, w.cfg["d"])
+    assert row_rel_err(got, O.forward(w)) <= TOL_F32

@@ -329,7 +329,7 @@ def test_attention_packed_equals_separate(path):
 
 # ------------------------------------------------------------------ row ops
 
-@pytest.mark.parametrize("d", [128, 512, 768, 3840])
+@pytest.mark.parametrize("d", [4, 128, 512, 768, 3840, 4096])
 @pytest.mark.parametrize("f16", [False, True])
 def test_norms(d, f16):
     rng = np.random.default_rng(d)
@@ -415,3 +415,57 @@ def test_mean_pool():
     ref = np.stack([np.concatenate([a[r0:r0 + n] for r0, n in rr]).astype(np.float64).mean(0)
                     for rr in items])
     assert row_rel_err(host(out), ref) <= TOL_F32
+
+
+# ------------------------------------------------------------- edge cases
+
+def test_gemm_empty_items():
+    """Items with no rows are no-ops beside non-empty ones; a launch of empty items
+    leaves Y untouched."""
+    rng = np.random.default_rng(31)
+    n, m, k = 70, 96, 64
+    x = rng.integers(-8, 9, (n, k)).astype(np.float32)
+    w = rng.integers(-8, 9, (m, k)).astype(np.float32)
+    Y = torch.full((n, 2 * m), 7.0, device=DEV)
+    B.gemm_items(to_dev(x), Y, [to_dev(w)], [(0, m, k, k, 2 * m, 0, 0, 0), (n, m, k, k, 2 * m, 0, 0, m)])
+    got = host(Y)
+    assert np.array_equal(got[:, m:], O.linear(x, w))
+    assert (got[:, :m] == 7.0).all()
+    B.gemm_items(to_dev(x), Y, [to_dev(w)], [(0, m, k, k, 2 * m, 0, 0, 0)])
+    assert np.array_equal(host(Y), got)
+
+
+@pytest.mark.parametrize("path", [B.ENC_F32, B.ENC_I8F16])
+def test_attention_empty_and_one_row_items(path):
+    f16 = path == B.ENC_I8F16
+    rng = np.random.default_rng(32)
+    rows, nq, nkv, hd = 50, 2, 2, 64
+    items = [[(0, 0)], [(0, 1)], [(1, 0), (1, 0)], [(1, 49)]]
+    p = _panel(rng, rows, nq, nkv, hd, f16=f16)
+    out = torch.full((rows, nq * hd), 5.0, dtype=torch.float16 if f16 else torch.float32, device=DEV)
+    B.attention_items(to_dev(p), out, items, nq, nkv, hd, 0.125, 0, path=path)
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, 0.125, 0)
+    assert row_rel_err(host(out), ref) <= (TOL_I8F16 if f16 else TOL_F32)
+    assert np.array_equal(host(out)[0], v[0])  # a one-row item returns its own value
+
+
+def test_row_ops_zero_rows():
+    w = to_dev(np.ones(256, np.float32))
+    x = torch.empty((0, 256), dtype=torch.float32, device=DEV)
+    y = torch.empty((0, 256), dtype=torch.float32, device=DEV)
+    B.rms_norm(x, w, 1e-6, y)
+    B.layer_norm(x, w, w, 1e-6, y)
+    torch.cuda.synchronize()
+
+
+def test_mean_pool_many_items_and_empty_refused():
+    """More items than one launch takes (64); an empty item is refused."""
+    rows, d = 1000, 40
+    a = torch.arange(rows * d, dtype=torch.float32, device=DEV).reshape(rows, d) % 1000.0
+    items = [[(2 * i, 2)] for i in range(rows // 2)]
+    out = torch.empty((rows // 2, d), dtype=torch.float32, device=DEV)
+    B.mean_pool(a, items, out)
+    assert torch.equal(out, (a[0::2] + a[1::2]) / 2)
+    with pytest.raises(RuntimeError, match="empty"):
+        B.mean_pool(a, [[(0, 3)], [(3, 0)]], out)

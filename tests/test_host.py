@@ -210,3 +210,13 @@ def test_rope_table_is_rounded_f64(sections, hd):
     for got, ref in ((cos, np.cos(ang)), (sin, np.sin(ang))):
         ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
         assert np.all(np.abs(got.astype(np.float64) - ref) <= 0.5 * ulp + 1e-300)
+
+
+def test_check_model_pool_needs_nonempty_items():
+    w, m, b, keep = _fake_model("gemma_text_f32", lengths=[5, 7])
+    items = B.make_items([[(0, 5)], [(5, 0)], [(5, 7)]])
+    b.items, b.nitems = items, 3
+    st, msg = B.check_model(m, b)
+    assert st == B.ENC_EINVAL and "empty" in msg
+    m.final_kind = 0  # no pool: an empty sequence is fine
+    assert B.check_model(m, b)[0] == B.ENC_OK

@@ -332,7 +332,8 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
 
 enc_status check_norm(Err &e, const char *who, const enc_norm_desc *d) {
     if (!d) return e.set(ENC_EINVAL, "%s: null descriptor", who);
-    if (!d->x || !d->w || !d->y) return e.set(ENC_EINVAL, "%s: null x, w or y", who);
+    // no rows: nothing is read or written, so the pointers may be null
+    if (d->rows && (!d->x || !d->w || !d->y)) return e.set(ENC_EINVAL, "%s: null x, w or y", who);
     if (d->flags & ~1u) return e.set(ENC_EINVAL, "%s: unknown flags", who);
     if (d->d == 0 || d->d % 4 || d->d > 4096)
         return e.set(ENC_EUNSUPPORTED, "%s: width %u (multiple of 4, <= 4096)", who, d->d);
@@ -416,6 +417,29 @@ hipError_t rows_pool(const PoolArgs &p, uint32_t rows, hipStream_t s) {
     return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_mean_pool(p, s); });
 }
 
+// Mean pool of any number of items: launches of at most kMaxAttnItems items.
+hipError_t pool_items(const enc_item *items, uint32_t nitems, uint32_t rows, uint32_t d, const float *a,
+                      float *out, hipStream_t s) {
+    for (uint32_t i0 = 0; i0 < nitems; i0 += kMaxAttnItems) {
+        PoolArgs p;
+        memset(&p, 0, sizeof p);
+        p.d = d;
+        p.nitems = std::min<uint32_t>(kMaxAttnItems, nitems - i0);
+        p.a = a;
+        p.out = out + (size_t)i0 * d;
+        for (uint32_t i = 0; i < p.nitems; i++) {
+            const enc_item &it = items[i0 + i];
+            p.items[i].r0a = it.r[0].r0;
+            p.items[i].na = it.r[0].n;
+            p.items[i].r0b = it.nr > 1 ? it.r[1].r0 : 0;
+            p.items[i].nb = it.nr > 1 ? it.r[1].n : 0;
+        }
+        const hipError_t hr = rows_pool(p, rows, s);
+        if (hr != hipSuccess) return hr;
+    }
+    return hipSuccess;
+}
+
 struct WsPlan {
     size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0, total = 0;
 };
@@ -496,6 +520,10 @@ enc_status check_model(Err &e, const enc_model *M, const enc_batch *B) {
     uint64_t covered = 0;
     for (uint32_t i = 0; i < B->nitems; i++) covered += item_len(B->items[i]);
     if (covered != B->rows) return e.set(ENC_ESHAPE, "items cover %llu of %u rows", (unsigned long long)covered, B->rows);
+    if (M->final_kind == ENC_FINAL_RMS_MEANPOOL)
+        for (uint32_t i = 0; i < B->nitems; i++)
+            if (!item_len(B->items[i]))
+                return e.set(ENC_EINVAL, "item %u is empty: its mean pool is undefined", i);
     bool rope = false;
     for (uint32_t l = 0; l < M->nlayers; l++) rope |= M->layers[l].rope_sections != 0;
     if (rope && (!B->rope_cos || !B->rope_sin)) return e.set(ENC_EINVAL, "RoPE layers need cos/sin tables");
@@ -818,26 +846,13 @@ enc_status enc_mean_pool(enc_ctx *ctx, uint32_t rows, uint32_t d, const float *a
     CtxScope cs(ctx);
     if (!a || !out) {
         e.set(ENC_EINVAL, "enc_mean_pool: null pointer");
-    } else if (nitems > (uint32_t)kMaxAttnItems) {
-        e.set(ENC_EUNSUPPORTED, "enc_mean_pool: at most %d items", kMaxAttnItems);
     } else if (check_items(e, "enc_mean_pool", items, nitems, rows) == ENC_OK) {
-        PoolArgs p;
-        memset(&p, 0, sizeof p);
-        p.d = d;
-        p.nitems = nitems;
-        p.a = a;
-        p.out = out;
-        for (uint32_t i = 0; i < nitems; i++) {
-            p.items[i].r0a = items[i].r[0].r0;
-            p.items[i].na = items[i].r[0].n;
-            p.items[i].r0b = items[i].nr > 1 ? items[i].r[1].r0 : 0;
-            p.items[i].nb = items[i].nr > 1 ? items[i].r[1].n : 0;
+        for (uint32_t i = 0; i < nitems; i++)
             if (!item_len(items[i])) {
-                e.set(ENC_EINVAL, "enc_mean_pool: item %u is empty", i);
+                e.set(ENC_EINVAL, "enc_mean_pool: item %u is empty (its mean is undefined)", i);
                 return finish(ctx, e);
             }
-        }
-        launch_status(e, rows_pool(p, rows, (hipStream_t)stream), "enc_mean_pool");
+        launch_status(e, pool_items(items, nitems, rows, d, a, out, (hipStream_t)stream), "enc_mean_pool");
     }
     return finish(ctx, e);
 }
@@ -909,10 +924,6 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
     }
     const enc_layer &L0 = model->layers[0];
     const uint32_t rows = batch->rows, d = L0.d;
-    if (model->final_kind == ENC_FINAL_RMS_MEANPOOL && batch->nitems > (uint32_t)kMaxAttnItems) {
-        e.set(ENC_EUNSUPPORTED, "encoder_forward: mean pool takes at most %d items", kMaxAttnItems);
-        return finish(ctx, e);
-    }
     const Bufs b = carve(ws, p);
     hipStream_t s = (hipStream_t)stream;
     float *h = model->final_kind == ENC_FINAL_NONE ? out : b.h;
@@ -939,22 +950,7 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
             NormArgs n{rows, d, d, d, h, model->final_w, nullptr, model->final_eps, a};
             hr = rows_rms(n, false, s);
         }
-        if (hr == hipSuccess) {
-            PoolArgs pa;
-            memset(&pa, 0, sizeof pa);
-            pa.d = d;
-            pa.nitems = batch->nitems;
-            pa.a = a;
-            pa.out = out;
-            for (uint32_t i = 0; i < batch->nitems; i++) {
-                const enc_item &it = batch->items[i];
-                pa.items[i].r0a = it.r[0].r0;
-                pa.items[i].na = it.r[0].n;
-                pa.items[i].r0b = it.nr > 1 ? it.r[1].r0 : 0;
-                pa.items[i].nb = it.nr > 1 ? it.r[1].n : 0;
-            }
-            hr = rows_pool(pa, rows, s);
-        }
+        if (hr == hipSuccess) hr = pool_items(batch->items, batch->nitems, rows, d, a, out, s);
     }
     launch_status(e, hr, "encoder_forward");
     return finish(ctx, e);

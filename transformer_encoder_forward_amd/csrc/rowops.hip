@@ -272,20 +272,25 @@ __global__ __launch_bounds__(256) void gated_act_kernel(ActArgs a) {
 __global__ __launch_bounds__(256) void mean_pool_kernel(PoolArgs a) {
     __shared__ float part[4][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint32_t j = blockIdx.x * 64 + lane, i = blockIdx.y;
-    const AttnItemK it = a.items[i];
-    const uint32_t L = it.na + it.nb;
-    float s = 0.0f;
-    if (j < a.d) {
-        for (uint32_t t = wave; t < L; t += 4) {
-            const uint32_t r = t < it.na ? it.r0a + t : it.r0b + (t - it.na);
-            s += a.a[(size_t)r * a.d + j];
+    const uint32_t j = blockIdx.x * 64 + lane;
+    // items beyond the grid's y extent (65 535) are taken in grid-stride order
+    for (uint32_t i = blockIdx.y; i < a.nitems; i += gridDim.y) {
+        const AttnItemK it = a.items[i];
+        const uint32_t L = it.na + it.nb;
+        float s = 0.0f;
+        if (j < a.d) {
+            for (uint32_t t = wave; t < L; t += 4) {
+                const uint32_t r = t < it.na ? it.r0a + t : it.r0b + (t - it.na);
+                s += a.a[(size_t)r * a.d + j];
+            }
         }
+        part[wave][lane] = s;
+        __syncthreads();
+        if (wave == 0 && j < a.d)
+            a.out[(size_t)i * a.d + j] =
+                (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / (float)L;
+        __syncthreads();
     }
-    part[wave][lane] = s;
-    __syncthreads();
-    if (wave == 0 && j < a.d)
-        a.out[(size_t)i * a.d + j] = (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / (float)L;
 }
 
 }  // namespace
@@ -369,7 +374,8 @@ hipError_t launch_gated_act(const ActArgs &a, bool f16, hipStream_t s) {
 
 hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s) {
     if (!a.nitems || !a.d) return hipSuccess;
-    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 63) / 64, a.nitems), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 63) / 64, a.nitems < 65535u ? a.nitems : 65535u), dim3(256),
+                       0, s, a);
     return hipGetLastError();
 }
 
