@@ -1,6 +1,7 @@
 // Launchers of the flash attention.
 //
-// f16 path: the kernel template in attn_impl.h (mask fast path, lazy rescale).
+// f16 path: hd 128 in attn_f16d_kernel (K/V by direct global -> LDS loads), hd 64
+// in the attn_kernel template (mask fast path, lazy rescale).
 // f32 path: the kernel below, the same S^T = K Q^T / O^T = V^T P^T scheme in its
 // plain form: with 64-cycle FP32 MFMAs the softmax VALU work is hidden anyway,
 // and the plain form keeps the register count at 128 (4 waves per SIMD).
@@ -207,9 +208,17 @@ hipError_t launch_attn_f32(const AttnArgs &a0, uint32_t hd, hipStream_t s) {
     return hipGetLastError();
 }
 
+// hd 128 takes the direct-to-LDS kernel: blocks of 256 queries (8 waves, one
+// block per CU) stage each K/V block once for twice the queries, when the
+// launch still has two such blocks per CU and there is no window (with a
+// window, a block's first key depends on its query tile, so the tile size
+// must not change between launches of the same item); else 128 queries.
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s) {
     if (hd == 64) return attn::launch<64, true, 4, 4, true>(a, s);
-    return attn::launch<128, true, 4, 2, true>(a, s);
+    uint32_t t256 = 0;
+    for (uint32_t i = 0; i < a.nitems; i++) t256 += (a.items[i].na + a.items[i].nb + 255) / 256;
+    if (!a.window && t256 * a.nq >= 512) return attn::launch_f16d<8, 1>(a, s);
+    return attn::launch_f16d<4, 2>(a, s);
 }
 
 }  // namespace enc

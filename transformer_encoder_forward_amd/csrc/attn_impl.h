@@ -290,6 +290,198 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_kernel(AttnArgs a) {
     }
 }
 
+// f16 flash attention at head dim 128 with K/V staged by direct global -> LDS
+// loads.  Same tiling and softmax as attn_kernel<128, true, ..> (transposed
+// scores, a lane per query, lazy rescale, full-block mask fast path); what
+// changes is how K and V reach the MFMAs:
+//  - a three-stage LDS ring of (K, V) key blocks, each 32 keys x 256 bytes, is
+//    filled by global_load_lds_dwordx4 two blocks ahead, with no registers or
+//    LDS writes spent on staging and one barrier per block;
+//  - V stays row-major (key x channel) and the O^T = V^T P^T operand is read
+//    with the transposing ds_read_b64_tr_b16: within each 16-lane group, lane i
+//    gets channel C0 + i of four consecutive keys;
+//  - K row t keeps 16-byte chunk c at position c ^ (t & 15), V row t at
+//    c ^ 4 (t & 3), so fragment reads hit distinct bank groups;
+//  - the softmax scale is folded into one FMA per score (p = exp2(s c - m)),
+//    and the per-lane partial row sums are combined across the two lane halves
+//    once, at the end.
+// Keys past the item (in the last block) load a clamped, finite row and are
+// masked.  Requires hd = 128 and nq*hd, ld, offsets as attention_items checks.
+template <int NW, int MINW>
+__global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
+    constexpr int HD = 128, QT = 32 * NW, NS = 3;
+    constexpr int TBYTES = KB * HD * 2;          // one K or V block: 8 KB
+    constexpr int SBYTES = 2 * TBYTES;           // a stage: K then V
+    constexpr int NI = TBYTES / 1024 / NW;       // load instructions per wave per tile
+    constexpr int NDMA = 2 * NI;                 // per wave per stage
+    static_assert(TBYTES / 1024 % NW == 0, "waves");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SBYTES];
+
+    const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
+    ItemCtx c;
+    locate<QT>(a, tile, c);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int kvh = head / a.group;
+    const _Float16 *P = reinterpret_cast<const _Float16 *>(a.qkv);
+    const int W = (int)a.window;
+
+    const int tq = c.q_lo + wave * 32 + li;
+    const bool qvalid = tq < c.q_hi;
+    const int wq0 = c.q_lo + wave * 32, wq1 = min(wq0 + 32, c.q_hi);
+
+    f16x8 qf[HD / 16];
+    {
+        const _Float16 *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col + head * HD + 64 * hf;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) qf[j] = qvalid ? *reinterpret_cast<const f16x8 *>(qp + 8 * j) : f16x8{};
+    }
+
+    // loads: instruction q of this wave covers keys 4 (wave NI + q) .. +3 of the
+    // block; lane l takes key + l/16 and LDS position l % 16 of that key row
+    const int kl = lane >> 4, pl = lane & 15;
+    auto dma = [&](int b) {
+        const int kb = c.k_lo + b * KB;
+        uint8_t *buf = smem + (b % NS) * SBYTES;
+#pragma unroll
+        for (int q = 0; q < NI; q++) {
+            const int ti = 4 * (wave * NI + q) + kl;
+            const int t = min(kb + ti, c.k_hi - 1);
+            const _Float16 *row = P + (size_t)row_of(c.it, t) * a.ld + kvh * HD;
+            dma16(row + a.k_col + 8 * (pl ^ (ti & 15)), buf + (wave * NI + q) * 1024);
+            dma16(row + a.v_col + 8 * (pl ^ (4 * (ti & 3))), buf + TBYTES + (wave * NI + q) * 1024);
+        }
+    };
+
+    // fragment addresses within a stage: K (key li, chunk 8 hf + j); V^T
+    // transposed reads for channel block dblk, key group s2 and half e8
+    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t krow = lds0 + (uint32_t)li * 256u;
+    const int g = lane >> 4, src = lane & 15;
+    const uint32_t vrow = lds0 + TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
+    const int vc0 = 2 * (g & 1) + ((src & 3) >> 1);   // chunk within a 32-channel block
+    const int vsw = 4 * (src >> 2);                   // row & 3 == src / 4 for every read
+
+    f32x16 o[HD / 32];
+#pragma unroll
+    for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
+    float m_run = -INFINITY, l_lane = 0.0f;
+
+    const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
+    if (nblk > 0) dma(0);
+    if (nblk > 1) dma(1);
+    for (int b = 0; b < nblk; b++) {
+        // block b landed (own loads; block b+1's may still fly), then everyone's;
+        // after this barrier no wave reads block b-1's buffer, which takes b+2
+        if (b + 1 < nblk)
+            vm_wait<NDMA>();
+        else
+            vm_wait<0>();
+        block_barrier();
+        if (b + 2 < nblk) dma(b + 2);
+        const int kb = c.k_lo + b * KB;
+        const bool active = wq0 < wq1 && (!W || (kb <= wq1 - 1 + W && kb + KB - 1 >= wq0 - W));
+        if (!active) continue;
+        const uint32_t sb = (uint32_t)((b % NS) * SBYTES);
+
+        // LDS reads in flight stay within the 15 the counter holds: K (8) and
+        // the first half of V for key group 0 (4), then the rest of group 0
+        // during the scores, then group 1 during the first P V products
+        u32x4 kf[HD / 16];
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) kf[j] = ds_read16(krow + sb + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16));
+        u32x2 vf[HD / 32][2][2];
+        auto vread = [&](int d, int s2) {
+#pragma unroll
+            for (int e8 = 0; e8 < 2; e8++)
+                vf[d][s2][e8] = ds_read8_tr16(vrow + sb + (uint32_t)((16 * s2 + 8 * e8) * 256) +
+                                              (uint32_t)(((4 * d + vc0) ^ vsw) * 16));
+        };
+        vread(0, 0);
+        vread(1, 0);
+        lgkm_wait_n<4>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) ready(kf[j]);
+        vread(2, 0);
+        vread(3, 0);
+
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; r++) s[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s, 0, 0, 0);
+
+        const bool full = wq1 - wq0 == 32 && kb + KB <= c.k_hi &&
+                          (!W || (wq1 - 1 - kb <= W && kb + KB - 1 - wq0 <= W));
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                const bool vis = qvalid && key < c.k_hi && (!W || abs(tq - key) <= W);
+                s[r] = vis ? s[r] : -INFINITY;
+            }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; r++) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2;
+        const float m_new = fmaxf(m_run, mx);
+        if (__any(m_new > m_run)) {
+            const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.0f : m_new));
+            l_lane *= alpha;
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            pv[r] = exp2f(fmaf(s[r], a.scale_log2, -m_use));
+            l_lane += pv[r];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+            lgkm_wait_n<0>();
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][s2][0]);
+                ready(vf[d][s2][1]);
+            }
+            if (s2 == 0)
+#pragma unroll
+                for (int d = 0; d < HD / 32; d++) vread(d, 1);
+            f16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) pb[e] = (_Float16)pv[8 * s2 + e];
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                const u32x4 vv = {vf[d][s2][0][0], vf[d][s2][0][1], vf[d][s2][1][0], vf[d][s2][1][1]};
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb, o[d], 0, 0, 0);
+            }
+        }
+    }
+    const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
+    if (qvalid) {
+        const float inv = 1.0f / l_run;
+        _Float16 *out = reinterpret_cast<_Float16 *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int ch = 32 * d + 8 * q + 4 * hf;
+                f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
+                           (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
+                *reinterpret_cast<f16x4 *>(out + ch) = v;
+            }
+    }
+}
+
 // Tiles of the launch for QT queries per block (fills tile0, ntiles).
 inline uint32_t plan_tiles(AttnArgs &a, int QT) {
     uint32_t tiles = 0;
@@ -299,6 +491,14 @@ inline uint32_t plan_tiles(AttnArgs &a, int QT) {
     }
     a.ntiles = tiles;
     return tiles;
+}
+
+template <int NW, int MINW>
+hipError_t launch_f16d(AttnArgs a, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(a, 32 * NW);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((attn_f16d_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
 }
 
 template <int HD, bool F16, int NW, int MINW, bool OPT>

@@ -55,4 +55,61 @@ __device__ __forceinline__ void st4h(_Float16 *p, f32x4 v) {
     *reinterpret_cast<f16x4 *>(p) = h;
 }
 
+// ---- LDS staging by direct global -> LDS loads, and LDS reads the compiler
+// does not track.  A global_load_lds_dwordx4 writes 64 lanes x 16 bytes to 1 KB
+// of consecutive LDS from the wave-uniform address it is given.  The compiler
+// would wait for every such load in flight before any LDS read it can see, so
+// kernels that keep loads in flight across their reads issue those reads in
+// inline assembly and wait for them with explicit counters.
+#define ENC_GLOBAL(p) ((const void __attribute__((address_space(1))) *)(p))
+#define ENC_SHARED(p) ((void __attribute__((address_space(3))) *)(p))
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)ENC_SHARED(const_cast<void *>(p));
+}
+
+__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(ENC_GLOBAL(src), ENC_SHARED(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+// Transposing 64-bit read of 16-bit data: within each group of 16 lanes, lane i
+// receives element i % 4 of the four 64-bit rows addressed by lanes i/4 + 4e,
+// e = 0..3 (the layout measured on gfx950).
+__device__ __forceinline__ u32x2 ds_read8_tr16(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+// Wait until at most N LDS reads (of this wave) are in flight.  The registers
+// the reads filled are then passed through empty asm statements (see `ready`):
+// volatile asm keeps its order, so no use of them moves above the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait_n() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ void ready(T &v) {
+    asm volatile("" : "+v"(v));
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits
+    // [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8] at maximum)
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 }  // namespace enc

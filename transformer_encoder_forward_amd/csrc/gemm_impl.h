@@ -726,35 +726,9 @@ __device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
 // owns k in [32h, 32h + 32), k-step kk the 8 values at 32h + 8kk.  Requires
 // K % 64 == 0.  Rows past n and columns past m load clamped (finite) rows and
 // are never stored.
-#define ENC_GLOBAL(p) ((const void __attribute__((address_space(1))) *)(p))
-#define ENC_SHARED(p) ((void __attribute__((address_space(3))) *)(p))
-
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)ENC_SHARED(const_cast<void *>(p));
-}
-
-__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3, u32x4 &b0, u32x4 &b1) {
     asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1) : "n"(N));
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits
-    // [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8] at maximum)
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
 }
 
 template <bool GATED>
