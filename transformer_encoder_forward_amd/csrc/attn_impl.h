@@ -482,6 +482,224 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
     }
 }
 
+// The same attention without a window, software-pipelined within each wave:
+// iteration b computes the scores of key block b+1 (eight dependent MFMAs)
+// next to the softmax of block b (VALU), which do not depend on each other, so
+// the matrix core and the vector ALU of one wave can work at the same time;
+// then P V of block b.  Four LDS stages: block b+3 is loaded while block b+1's
+// K and block b's V are read.  Keys past the item occur only in the last block
+// and are masked there; rows past the item's queries are computed on clamped
+// data and never stored.  The cross-half row max uses v_permlane32_swap; the
+// query loads land before the staging loads start, so no wait for them sits
+// inside the loop.
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int NW, int MINW>
+__global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
+    constexpr int HD = 128, QT = 32 * NW, NS = 4;
+    constexpr int TBYTES = KB * HD * 2;
+    constexpr int SBYTES = 2 * TBYTES;
+    constexpr int NI = TBYTES / 1024 / NW;
+    constexpr int NDMA = 2 * NI;
+    static_assert(TBYTES / 1024 % NW == 0, "waves");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SBYTES];
+
+    const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
+    ItemCtx c;
+    locate<QT>(a, tile, c);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int kvh = head / a.group;
+    const _Float16 *P = reinterpret_cast<const _Float16 *>(a.qkv);
+
+    const int tq = c.q_lo + wave * 32 + li;
+    const bool qvalid = tq < c.q_hi;
+    const bool wactive = c.q_lo + wave * 32 < c.q_hi;  // waves without queries only join the barriers
+
+    f16x8 qf[HD / 16];
+    {
+        const _Float16 *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col + head * HD + 64 * hf;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) qf[j] = *reinterpret_cast<const f16x8 *>(qp + 8 * j);
+        // land q before the staging loads start, so that no wait for them is
+        // placed inside the loop (it would also wait for every block in flight)
+        vm_wait<0>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) ready(qf[j]);
+    }
+
+    const int kl = lane >> 4, pl = lane & 15;
+    auto dma = [&](int b) {
+        const int kb = c.k_lo + b * KB;
+        uint8_t *buf = smem + (b % NS) * SBYTES;
+#pragma unroll
+        for (int q = 0; q < NI; q++) {
+            const int ti = 4 * (wave * NI + q) + kl;
+            const int t = min(kb + ti, c.k_hi - 1);
+            const _Float16 *row = P + (size_t)row_of(c.it, t) * a.ld + kvh * HD;
+            dma16(row + a.k_col + 8 * (pl ^ (ti & 15)), buf + (wave * NI + q) * 1024);
+            dma16(row + a.v_col + 8 * (pl ^ (4 * (ti & 3))), buf + TBYTES + (wave * NI + q) * 1024);
+        }
+    };
+
+    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t krow = lds0 + (uint32_t)li * 256u;
+    const int g = lane >> 4, src = lane & 15;
+    const uint32_t vrow = lds0 + TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
+    const int vc0 = 2 * (g & 1) + ((src & 3) >> 1);
+    const int vsw = 4 * (src >> 2);
+
+    u32x4 kf[HD / 16];
+    auto kread = [&](uint32_t sb) {
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) kf[j] = ds_read16(krow + sb + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16));
+    };
+    u32x2 vf[HD / 32][2][2];
+    auto vread = [&](uint32_t sb, int d, int s2) {
+#pragma unroll
+        for (int e8 = 0; e8 < 2; e8++)
+            vf[d][s2][e8] = ds_read8_tr16(vrow + sb + (uint32_t)((16 * s2 + 8 * e8) * 256) +
+                                          (uint32_t)(((4 * d + vc0) ^ vsw) * 16));
+    };
+
+    f32x16 o[HD / 32];
+#pragma unroll
+    for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
+    float m_run = -INFINITY, l_lane = 0.0f;
+    const float cs = a.scale_log2;
+
+    const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
+    if (nblk > 0) dma(0);
+    if (nblk > 1) dma(1);
+    if (nblk > 2) dma(2);
+    if (nblk > 2)
+        vm_wait<2 * NDMA>();
+    else if (nblk > 1)
+        vm_wait<NDMA>();
+    else
+        vm_wait<0>();
+    block_barrier();
+    f32x16 s_cur;
+#pragma unroll
+    for (int r = 0; r < 16; r++) s_cur[r] = 0.0f;
+    if (wactive && nblk > 0) {
+        kread(0);
+        lgkm_wait_n<0>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) {
+            ready(kf[j]);
+            s_cur = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_cur, 0, 0, 0);
+        }
+    }
+    for (int b = 0; b < nblk; b++) {
+        // block b+1 landed (own loads; b+2's may fly), then everyone's; after
+        // the barrier nobody reads block b-1's buffer, which takes block b+3
+        if (b + 2 < nblk)
+            vm_wait<NDMA>();
+        else
+            vm_wait<0>();
+        block_barrier();
+        if (b + 3 < nblk) dma(b + 3);
+        if (!wactive) continue;
+        const int kb = c.k_lo + b * KB;
+        const uint32_t sb = (uint32_t)((b % NS) * SBYTES), sn = (uint32_t)(((b + 1) % NS) * SBYTES);
+        if (kb + KB > c.k_hi) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                s_cur[r] = key < c.k_hi ? s_cur[r] : -INFINITY;
+            }
+        }
+        // reads: block b+1's K (8; on the last block a stale buffer, unused) and
+        // the first half of block b's V group 0 (4): 12 in flight at most
+        kread(sn);
+        vread(sb, 0, 0);
+        vread(sb, 1, 0);
+        lgkm_wait_n<4>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) ready(kf[j]);
+        vread(sb, 2, 0);
+        vread(sb, 3, 0);
+
+        // scores of block b+1 (a dependent chain of MFMAs) and the softmax of
+        // block b (VALU) are independent: the scheduler overlaps them
+        f32x16 s_nx;
+#pragma unroll
+        for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++)
+            s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
+        float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
+                         fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
+                             fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
+        const float m_new = fmaxf(m_run, max_halves(mx) * cs);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+        // 2^x as the bare v_exp_f32: results below 2^-126 flush to 0, far
+        // below anything a row sum of at least 1 can register
+        float pv[16], rs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], cs, -m_use));
+            rs += pv[r];
+        }
+        f16x8 pb[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+            for (int e = 0; e < 8; e++) pb[s2][e] = (_Float16)pv[8 * s2 + e];
+
+        // the output and the row sum follow the new max only when it grew
+        if (__any(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_lane *= alpha;
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+        }
+        m_run = m_new;
+        l_lane += rs;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++) {
+            lgkm_wait_n<0>();
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][s2][0]);
+                ready(vf[d][s2][1]);
+            }
+            if (s2 == 0)
+#pragma unroll
+                for (int d = 0; d < HD / 32; d++) vread(sb, d, 1);
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                const u32x4 vv = {vf[d][s2][0][0], vf[d][s2][0][1], vf[d][s2][1][0], vf[d][s2][1][1]};
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[s2], o[d], 0, 0, 0);
+            }
+        }
+        s_cur = s_nx;
+    }
+    const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
+    if (qvalid) {
+        const float inv = 1.0f / l_run;
+        _Float16 *out = reinterpret_cast<_Float16 *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int ch = 32 * d + 8 * q + 4 * hf;
+                f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
+                           (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
+                *reinterpret_cast<f16x4 *>(out + ch) = v;
+            }
+    }
+}
+
 // Tiles of the launch for QT queries per block (fills tile0, ntiles).
 inline uint32_t plan_tiles(AttnArgs &a, int QT) {
     uint32_t tiles = 0;
@@ -498,6 +716,14 @@ hipError_t launch_f16d(AttnArgs a, hipStream_t s) {
     const uint32_t tiles = plan_tiles(a, 32 * NW);
     if (!tiles) return hipSuccess;
     hipLaunchKernelGGL((attn_f16d_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int NW, int MINW>
+hipError_t launch_f16p(AttnArgs a, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(a, 32 * NW);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((attn_f16p_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
