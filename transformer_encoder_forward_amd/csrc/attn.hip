@@ -4,7 +4,8 @@
 // in the attn_kernel template (mask fast path, lazy rescale).
 // f32 path: the kernel below, the same S^T = K Q^T / O^T = V^T P^T scheme in its
 // plain form: with 64-cycle FP32 MFMAs the softmax VALU work is hidden anyway,
-// and the plain form keeps the register count at 128 (4 waves per SIMD).
+// and the plain form keeps the register count at 128 (4 waves per SIMD).  V is
+// staged transposed, so the P V operand comes in 16-byte reads.
 // What both compute: egemma2.rs (cortiq-engine 0.8.39), module doc "Attention"
 // and `att_plan`; zimage.rs (cortiq-engine 0.7.6), module doc and `PFa`.
 #include <math.h>
@@ -51,7 +52,9 @@ __device__ __forceinline__ bool block_active(int q0, int q1, int kb, int k_hi, u
 }
 
 // Online-softmax update of one lane's 16 scores (query = lane%32).  s holds
-// raw dot products; masked keys become -inf.  Returns p in place.
+// raw dot products; masked keys become -inf.  Returns p in place.  2^x is the
+// bare v_exp_f32 (results below 2^-126 flush to 0, far below anything a row
+// sum of at least 1 registers).
 __device__ __forceinline__ float softmax_step(float (&sv)[16], float &m_run, float &l_run) {
     float mx = -INFINITY;
 #pragma unroll
@@ -59,11 +62,11 @@ __device__ __forceinline__ float softmax_step(float (&sv)[16], float &m_run, flo
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float rs = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; r++) {
-        sv[r] = exp2f(sv[r] - m_use);
+        sv[r] = __builtin_amdgcn_exp2f(sv[r] - m_use);
         rs += sv[r];
     }
     rs += __shfl_xor(rs, 32, 64);
@@ -76,11 +79,12 @@ __device__ __forceinline__ float softmax_step(float (&sv)[16], float &m_run, flo
 
 template <int HD>
 __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
-    constexpr int LDK = HD + 4, LDV = HD + 8;
+    constexpr int LDK = HD + 4;
+    constexpr int LDT = KB + 4;                // V^T rows: 32 keys + pad
     constexpr int NQ4 = HD / 8;                // float4 of q per lane (hd/2 floats)
     constexpr int NLD = KB * HD / 4 / 256;     // float4 of K (and of V) per thread per block
     __shared__ __attribute__((aligned(16))) float Ks[2][KB][LDK];
-    __shared__ __attribute__((aligned(16))) float Vs[2][KB][LDV];
+    __shared__ __attribute__((aligned(16))) float Vs[2][HD][LDT];  // V transposed
 
     const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
     ItemCtx c;
@@ -125,7 +129,8 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
         for (int i = 0; i < NLD; i++) {
             const int f = tid + 256 * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
             st4(&Ks[buf][key][ch], rk[i]);
-            st4(&Vs[buf][key][ch], rv[i]);
+#pragma unroll
+            for (int e = 0; e < 4; e++) Vs[buf][ch + e][key] = rv[i][e];
         }
     };
 
@@ -169,14 +174,18 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
             for (int d = 0; d < HD / 32; d++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) o[d][r] *= alpha;
-            // O^T[d][q] += V^T[d][key] P^T[key][q]; step r pairs lane halves' keys
+            // O^T[d][q] += V^T[d][key] P^T[key][q]; step r pairs lane halves'
+            // keys 8(r/4) + 4 hf + r%4, so the keys of steps 4g..4g+3 are four
+            // consecutive floats of a V^T row: one 16-byte read per 4 MFMAs
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float *vr = &Vs[buf][8 * (r >> 2) + 4 * hf + (r & 3)][li];
+            for (int g4 = 0; g4 < 4; g4++)
 #pragma unroll
-                for (int d = 0; d < HD / 32; d++)
-                    o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vr[32 * d], sv[r], o[d], 0, 0, 0);
-            }
+                for (int d = 0; d < HD / 32; d++) {
+                    const f32x4 v4 = ld4(&Vs[buf][32 * d + li][8 * g4 + 4 * hf]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++)
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(v4[e], sv[4 * g4 + e], o[d], 0, 0, 0);
+                }
         }
         if (b + 1 < nblk) sstore(buf ^ 1);
         __syncthreads();
