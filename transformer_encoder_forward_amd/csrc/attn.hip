@@ -17,21 +17,21 @@ namespace enc {
 namespace f32path {
 
 constexpr int KB = 32;   // keys per block
-constexpr int kQT = 128;  // queries per block (4 waves x 32)
 
 struct ItemCtx {
     AttnItemK it;
     int L, q_lo, q_hi, k_lo, k_hi;
 };
 
+template <int QT>
 __device__ __forceinline__ void locate(const AttnArgs &a, uint32_t tile, ItemCtx &c) {
     uint32_t sel = 0;
     for (uint32_t i = 1; i < a.nitems; i++)
         if (tile >= a.items[i].tile0) sel = i;
     c.it = a.items[sel];
     c.L = (int)(c.it.na + c.it.nb);
-    c.q_lo = (int)(tile - c.it.tile0) * kQT;
-    c.q_hi = min(c.q_lo + kQT, c.L);
+    c.q_lo = (int)(tile - c.it.tile0) * QT;
+    c.q_hi = min(c.q_lo + QT, c.L);
     c.k_lo = 0;
     c.k_hi = c.L;
     if (a.window) {
@@ -77,18 +77,19 @@ __device__ __forceinline__ float softmax_step(float (&sv)[16], float &m_run, flo
 
 // ------------------------------------------------------------------ f32 path
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
+template <int HD, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
+    constexpr int NT = 64 * NW, QT = 32 * NW;
     constexpr int LDK = HD + 4;
     constexpr int LDT = KB + 4;                // V^T rows: 32 keys + pad
     constexpr int NQ4 = HD / 8;                // float4 of q per lane (hd/2 floats)
-    constexpr int NLD = KB * HD / 4 / 256;     // float4 of K (and of V) per thread per block
+    constexpr int NLD = KB * HD / 4 / NT;      // float4 of K (and of V) per thread per block
     __shared__ __attribute__((aligned(16))) float Ks[2][KB][LDK];
     __shared__ __attribute__((aligned(16))) float Vs[2][HD][LDT];  // V transposed
 
     const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
     ItemCtx c;
-    locate(a, tile, c);
+    locate<QT>(a, tile, c);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hf = lane >> 5;
     const int kvh = head / a.group;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
     auto gload = [&](int kb) {
 #pragma unroll
         for (int i = 0; i < NLD; i++) {
-            const int f = tid + 256 * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
+            const int f = tid + NT * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
             const int t = kb + key;
             if (t < c.k_hi) {
                 const float *base = P + (size_t)row_of(c.it, t) * a.ld + kvh * HD + ch;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NLD; i++) {
-            const int f = tid + 256 * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
+            const int f = tid + NT * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
             st4(&Ks[buf][key][ch], rk[i]);
 #pragma unroll
             for (int e = 0; e < 4; e++) Vs[buf][ch + e][key] = rv[i][e];
@@ -206,15 +207,19 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace f32path
 
-hipError_t launch_attn_f32(const AttnArgs &a0, uint32_t hd, hipStream_t s) {
-    AttnArgs a = a0;
-    const uint32_t tiles = attn::plan_tiles(a, f32path::kQT);
+template <int HD, int NW>
+hipError_t launch_f32(AttnArgs a, hipStream_t s) {
+    const uint32_t tiles = attn::plan_tiles(a, 32 * NW);
     if (!tiles) return hipSuccess;
-    if (hd == 64)
-        hipLaunchKernelGGL(f32path::attn_f32_kernel<64>, dim3(tiles * a.nq), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(f32path::attn_f32_kernel<128>, dim3(tiles * a.nq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((f32path::attn_f32_kernel<HD, NW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
+}
+
+// 128 queries per block (four waves; blocks of one wave were measured slower
+// even where 128-query blocks leave CUs idle).
+hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s) {
+    if (hd == 64) return launch_f32<64, 4>(a, s);
+    return launch_f32<128, 4>(a, s);
 }
 
 // hd 128 takes the direct-to-LDS kernels.  Without a window: the pipelined
