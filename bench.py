@@ -80,7 +80,7 @@ def main():
     db = M.DeviceBatch(w, dev)
     x = torch.from_numpy(w.x).to(dev)
     out = torch.empty((M.out_rows(w), cfg["d"]), dtype=torch.float32, device=dev)
-    ws = dm.workspace(w.rows, dev)
+    ws = dm.workspace(db, dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] {args.workload}: rows={w.rows} items={len(w.items)} layers={cfg['layers']} "

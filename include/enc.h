@@ -155,10 +155,24 @@ typedef struct {
     float scale;
     uint32_t window;        /* 0 = full bidirectional */
     uint32_t rows;          /* panel rows (bound for the items) */
+    void *ws;               /* (dev) scratch for key splits, 256-byte aligned, or NULL */
+    size_t ws_bytes;        /* at least enc_attention_workspace_bytes() when ws != NULL */
 } enc_attn_desc;
 
+/* Key splits (ENC_F32, windowless items): an item too short to occupy the GPU
+ * with its query tiles alone is cut into key chunks whose partial softmax
+ * results (running max, sum and unnormalised output, f32) go to ws and are
+ * merged by a second kernel in a fixed order: the same softmax, regrouped.
+ * Whether and how an item is split depends only on its length, nq, the path
+ * and the window, so a packed batch gives the same bits as its items alone.
+ * With ws == NULL nothing is split.  A ws smaller than needed is ENC_ESHAPE. */
 ENC_API enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_item *items,
                            uint32_t nitems, enc_stream stream);
+
+/* Bytes of ws attention_items uses for these items (0: nothing is split).
+ * Host only; reads only the geometry fields of desc. */
+ENC_API size_t enc_attention_workspace_bytes(const enc_attn_desc *desc, const enc_item *items,
+                                             uint32_t nitems);
 
 /* ------------------------------------------------------------------ row ops */
 /* One wavefront per row (or per row and head); f32 statistics.  Geometry:
@@ -292,8 +306,9 @@ typedef struct {
     float final_eps;
 } enc_model;
 
-/* Workspace bytes encoder_forward / encoder_layer_forward need for `rows`. */
-ENC_API size_t enc_workspace_bytes(const enc_model *model, uint32_t rows);
+/* Workspace bytes encoder_forward / encoder_layer_forward need for this batch
+ * (its rows, and its items for the attention key splits).  0 on null input. */
+ENC_API size_t enc_workspace_bytes(const enc_model *model, const enc_batch *batch);
 
 /* One layer in place on h (dev, f32 [rows][d]), computing its own pre-norm. */
 ENC_API enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_batch *batch,

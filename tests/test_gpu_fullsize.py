@@ -147,7 +147,7 @@ def run(w, x=None, layers=None):
     db = M.DeviceBatch(w, DEV)
     X = torch.from_numpy(np.ascontiguousarray(w.x if x is None else x)).to(DEV)
     out = torch.empty((M.out_rows(w), w.cfg["d"]), dtype=torch.float32, device=DEV)
-    ws = dm.workspace(w.rows, DEV)
+    ws = dm.workspace(db, DEV)
     M.encoder_forward(dm, db, X, out, ws)
     torch.cuda.synchronize()
     return out

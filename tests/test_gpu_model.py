@@ -27,7 +27,7 @@ def run(w, layers=None, x=None):
     db = M.DeviceBatch(w, DEV)
     X = torch.from_numpy(np.ascontiguousarray(w.x if x is None else x)).to(DEV)
     out = torch.empty((M.out_rows(w), w.cfg["d"]), dtype=torch.float32, device=DEV)
-    ws = dm.workspace(w.rows, DEV)
+    ws = dm.workspace(db, DEV)
     M.encoder_forward(dm, db, X, out, ws)
     torch.cuda.synchronize()
     return out
@@ -78,7 +78,7 @@ def test_fused_chain_equals_layer_by_layer(name, kw):
     dm = M.DeviceModel(w, DEV)
     db = M.DeviceBatch(w, DEV)
     h = torch.from_numpy(w.x.copy()).to(DEV)
-    ws = dm.workspace(w.rows, DEV)
+    ws = dm.workspace(db, DEV)
     for li in range(w.cfg["layers"]):
         M.encoder_layer_forward(dm, li, db, h, ws)
     torch.cuda.synchronize()

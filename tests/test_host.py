@@ -150,7 +150,7 @@ def test_check_model_accepts_workloads(name, kw):
     w, m, b, keep = _fake_model(name, **kw)
     st, msg = B.check_model(m, b)
     assert st == B.ENC_OK, msg
-    assert B.lib().enc_workspace_bytes(C.byref(m), w.rows) > 0
+    assert B.lib().enc_workspace_bytes(C.byref(m), C.byref(b)) > 0
 
 
 def test_check_model_rejects():
@@ -173,12 +173,73 @@ def test_check_model_rejects():
 
 def test_workspace_grows_with_rows():
     w, m, b, keep = _fake_model("gemma_text_f32", lengths=[5, 7])
-    a = B.lib().enc_workspace_bytes(C.byref(m), 1000)
-    c = B.lib().enc_workspace_bytes(C.byref(m), 2000)
+    b.rows = 1000
+    a = B.lib().enc_workspace_bytes(C.byref(m), C.byref(b))
+    b.rows = 2000
+    c = B.lib().enc_workspace_bytes(C.byref(m), C.byref(b))
     assert c > a > 0 and a % 256 == 0
     # A, panel, attention out, T, m, H in f32 at d 512, ff 2048, 8x64 heads
     per_row = 4 * (512 + 1536 + 512 + 512 + 2048 + 512)
     assert a >= 1000 * per_row
+
+
+def _up256(v):
+    return (v + 255) // 256 * 256
+
+
+def _split_bytes(records, hd):
+    return _up256(records * hd * 4) + _up256(records * 8) if records else 0
+
+
+def test_attention_key_split_workspace_rule():
+    """Key splits: windowless f32 items whose 128-query tiles times heads stay
+    under 768 blocks are cut into min(8, 768 // blocks, L // 128) chunks of whole
+    32-key blocks; one record (hd + 2 floats) per chunk, item row and head."""
+    def ws(items, nq=12, hd=64, window=0, path=B.ENC_F32):
+        d = B.attention_desc(None, None, nq, nq, hd, 0.125, window, ld=3 * nq * hd,
+                             ldo=nq * hd, path=path, rows=1 << 20)
+        return B.attention_workspace_bytes(d, items)
+    # 1024 rows, 12 heads: 96 blocks -> 8 chunks of 128 keys
+    assert ws([[(0, 1024)]]) == _split_bytes(8 * 1024 * 12, 64)
+    # 1000 rows: min(8, 8, 7) = 7 -> chunk ceil(1000/7) = 143 -> 160 -> 7 chunks
+    assert ws([[(0, 1000)]]) == _split_bytes(7 * 1000 * 12, 64)
+    # 30 heads of 128 at 1056 rows: 9 tiles x 30 = 270 blocks -> 2 chunks
+    assert ws([[(0, 1056)]], nq=30, hd=128) == _split_bytes(2 * 1056 * 30, 128)
+    # no split: a window, the f16 path, short items, items that fill the GPU alone
+    assert ws([[(0, 1024)]], window=512) == 0
+    assert ws([[(0, 1024)]], path=B.ENC_I8F16) == 0
+    assert ws([[(0, 255)]]) == 0
+    assert ws([[(0, 8192)]]) == 0
+    # items are planned one by one and their records add up (same launch)
+    assert ws([[(0, 1024)], [(1024, 1024)], [(2048, 100)]]) == _split_bytes(2 * 8 * 1024 * 12, 64)
+
+
+def test_attention_workspace_checked():
+    d = B.attention_desc(None, None, 12, 12, 64, 0.125, 0, ld=3 * 768, ldo=768, rows=1024)
+    d.qkv = d.out = 0x10000
+    items = B.make_items([[(0, 1024)]])
+    need = B.attention_workspace_bytes(d, [[(0, 1024)]])
+    msg = C.create_string_buffer(256)
+    d.ws, d.ws_bytes = 0x100000, need - 1
+    assert B.lib().enc_check_attention(C.byref(d), items, 1, msg, 256) == B.ENC_ESHAPE
+    d.ws_bytes = need
+    assert B.lib().enc_check_attention(C.byref(d), items, 1, msg, 256) == B.ENC_OK
+    d.ws = 0x100010
+    assert B.lib().enc_check_attention(C.byref(d), items, 1, msg, 256) == B.ENC_EUNSUPPORTED
+    d.ws, d.ws_bytes = None, 0  # no workspace: nothing is split, always valid
+    assert B.lib().enc_check_attention(C.byref(d), items, 1, msg, 256) == B.ENC_OK
+
+
+def test_model_workspace_holds_key_splits():
+    w, m, b, keep = _fake_model("vit_layer_f32")
+    small = B.lib().enc_workspace_bytes(C.byref(m), C.byref(b))  # 64 rows: no split
+    items = B.make_items([[(0, 1024)]])
+    b.rows, b.items, b.nitems = 1024, items, 1
+    big = B.lib().enc_workspace_bytes(C.byref(m), C.byref(b))
+    # vit_layer_f32: 2 heads of 64 -> 16 blocks -> 8 chunks of 128 keys
+    # A, attention out, T, H at d 128; the panel (384); the GELU hidden (512)
+    dense = _up256(1024 * 128 * 4) * 4 + _up256(1024 * 384 * 4) + _up256(1024 * 512 * 4)
+    assert big == dense + _split_bytes(8 * 1024 * 2, 64) > small
 
 
 # --------------------------------------------------- tables vs the oracle

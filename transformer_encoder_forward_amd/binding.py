@@ -28,7 +28,8 @@ EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attenti
            "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
            "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
-           "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak"]
+           "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak",
+           "enc_attention_workspace_bytes"]
 CLASS_NAMES = ["gemm", "attn", "rows"]
 
 
@@ -65,7 +66,8 @@ class AttnDesc(C.Structure):
                 ("q_col", C.c_uint32), ("k_col", C.c_uint32), ("v_col", C.c_uint32),
                 ("out", C.c_void_p), ("ldo", C.c_uint32), ("nq", C.c_uint32),
                 ("nkv", C.c_uint32), ("hd", C.c_uint32), ("scale", C.c_float),
-                ("window", C.c_uint32), ("rows", C.c_uint32)]
+                ("window", C.c_uint32), ("rows", C.c_uint32), ("ws", C.c_void_p),
+                ("ws_bytes", C.c_size_t)]
 
 
 class NormDesc(C.Structure):
@@ -154,8 +156,10 @@ def lib():
     L.enc_qk_norm_rope.argtypes = [P, C.POINTER(QkDesc), P]
     L.enc_gated_act.argtypes = [P, C.POINTER(ActDesc), P]
     L.enc_mean_pool.argtypes = [P, C.c_uint32, C.c_uint32, P, C.POINTER(Item), C.c_uint32, P, P]
-    L.enc_workspace_bytes.argtypes = [C.POINTER(Model), C.c_uint32]
+    L.enc_workspace_bytes.argtypes = [C.POINTER(Model), C.POINTER(Batch)]
     L.enc_workspace_bytes.restype = C.c_size_t
+    L.enc_attention_workspace_bytes.argtypes = [C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32]
+    L.enc_attention_workspace_bytes.restype = C.c_size_t
     L.encoder_layer_forward.argtypes = [P, C.POINTER(Layer), C.POINTER(Batch), P, P, C.c_size_t, P]
     L.encoder_forward.argtypes = [P, C.POINTER(Model), C.POINTER(Batch), P, P, P, C.c_size_t, P]
     L.enc_check_gemm.argtypes = [C.POINTER(GemmDesc), C.POINTER(GemmItem), C.c_uint32,
@@ -254,10 +258,8 @@ def gemm_items(x, y, w, items, path=ENC_F32, row_scale=None, bias=None, alpha=1.
     ctx.check(lib().gemm_items(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
 
 
-def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_col=0,
-                    k_col=None, v_col=None, ldo=None, path=ENC_F32, rows=None, ctx=None,
-                    stream=None):
-    ctx = ctx or context()
+def attention_desc(qkv, out, nq, nkv, hd, scale, window=0, ld=None, q_col=0, k_col=None,
+                   v_col=None, ldo=None, path=ENC_F32, rows=None):
     d = AttnDesc()
     d.path = path
     d.qkv = _ptr(qkv)
@@ -271,6 +273,29 @@ def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_co
     d.scale = scale
     d.window = window
     d.rows = rows if rows is not None else qkv.shape[0]
+    return d
+
+
+def attention_workspace_bytes(desc, items):
+    return lib().enc_attention_workspace_bytes(C.byref(desc), make_items(items), len(items))
+
+
+def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_col=0,
+                    k_col=None, v_col=None, ldo=None, path=ENC_F32, rows=None, ws="auto",
+                    ctx=None, stream=None):
+    """ws: "auto" (a torch buffer of the size the key splits need), None (no
+    split) or a uint8 device tensor."""
+    ctx = ctx or context()
+    d = attention_desc(qkv, out, nq, nkv, hd, scale, window, ld, q_col, k_col, v_col, ldo, path,
+                       rows)
+    if isinstance(ws, str):
+        import torch
+        n = attention_workspace_bytes(d, items)
+        ws = torch.empty(n, dtype=torch.uint8, device=qkv.device) if n else None
+        if ws is not None and stream is not None and hasattr(stream, "cuda_stream"):
+            ws.record_stream(stream)
+    if ws is not None:
+        d.ws, d.ws_bytes = ws.data_ptr(), ws.numel()
     arr = make_items(items)
     ctx.check(lib().attention_items(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
 

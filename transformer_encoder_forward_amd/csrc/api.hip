@@ -264,6 +264,64 @@ enc_status check_items(Err &e, const char *who, const enc_item *items, uint32_t 
     return ENC_OK;
 }
 
+// Key split of one item.  An item whose q-tiles alone would leave most CUs
+// idle is cut into nsplit key chunks (multiples of the 32-key block); each
+// (q-tile, chunk) block writes a partial softmax, merged afterwards in a fixed
+// order.  The plan depends only on the item's own length and the launch-wide
+// geometry (path, heads, window), never on the other items, so a packed batch
+// and its items run alone give the same bits.  f32 path, windowless items only.
+constexpr uint32_t kAttnQT = 128;      // queries per f32 attention block
+constexpr uint32_t kSplitTarget = 768; // blocks an item alone should reach
+constexpr uint32_t kSplitMinKeys = 128;
+constexpr uint32_t kSplitMax = 8;
+
+struct KvSplit {
+    uint32_t n, chunk;
+};
+
+KvSplit kv_split(const enc_attn_desc *d, uint32_t L) {
+    if (d->path != ENC_F32 || d->window || L < 2 * kSplitMinKeys) return {1, L};
+    const uint32_t blocks = (L + kAttnQT - 1) / kAttnQT * d->nq;
+    const uint32_t s = std::min({kSplitMax, kSplitTarget / blocks, L / kSplitMinKeys});
+    if (s < 2) return {1, L};
+    const uint32_t chunk = ((L + s - 1) / s + 31) / 32 * 32;
+    return {(L + chunk - 1) / chunk, chunk};
+}
+
+// Items in launch order (longest first: their tiles carry the most key blocks).
+std::vector<uint32_t> attn_order(const enc_item *items, uint32_t n) {
+    std::vector<uint32_t> order;
+    for (uint32_t i = 0; i < n; i++)
+        if (item_len(items[i])) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](uint32_t a, uint32_t b) { return item_len(items[a]) > item_len(items[b]); });
+    return order;
+}
+
+// Partial-result records (one per split, item row and head) of the largest
+// launch; launches run in stream order and reuse the same workspace.
+uint64_t attn_records(const enc_attn_desc *d, const enc_item *items, uint32_t n) {
+    const std::vector<uint32_t> order = attn_order(items, n);
+    uint64_t most = 0;
+    for (size_t c0 = 0; c0 < order.size(); c0 += kMaxAttnItems) {
+        uint64_t r = 0;
+        for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++) {
+            const uint32_t L = item_len(items[order[c]]);
+            const KvSplit k = kv_split(d, L);
+            if (k.n > 1) r += (uint64_t)k.n * L * d->nq;
+        }
+        most = std::max(most, r);
+    }
+    return most;
+}
+
+size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+size_t attn_ws_bytes(const enc_attn_desc *d, const enc_item *items, uint32_t n) {
+    const uint64_t r = attn_records(d, items, n);
+    return r ? up256(r * d->hd * 4) + up256(r * 8) : 0;
+}
+
 enc_status check_attn(Err &e, const enc_attn_desc *d, const enc_item *items, uint32_t n) {
     if (!d) return e.set(ENC_EINVAL, "attention_items: null descriptor");
     if (d->path != ENC_F32 && d->path != ENC_I8F16)
@@ -284,16 +342,23 @@ enc_status check_attn(Err &e, const enc_attn_desc *d, const enc_item *items, uin
         return e.set(ENC_EUNSUPPORTED, "attention_items: panel/output must be 16-byte aligned");
     if (!(d->scale == d->scale) || std::isinf(d->scale))
         return e.set(ENC_EINVAL, "attention_items: scale is not finite");
-    return check_items(e, "attention_items", items, n, d->rows);
+    if (check_items(e, "attention_items", items, n, d->rows) != ENC_OK) return e.st;
+    if (d->ws) {
+        if (!aligned(d->ws, 256))
+            return e.set(ENC_EUNSUPPORTED, "attention_items: workspace must be 256-byte aligned");
+        const size_t need = attn_ws_bytes(d, items, n);
+        if (d->ws_bytes < need)
+            return e.set(ENC_ESHAPE, "attention_items: workspace of %zu bytes, %zu needed",
+                         (size_t)d->ws_bytes, need);
+    }
+    return ENC_OK;
 }
 
 hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t n, hipStream_t s) {
-    // longest items first (their tiles carry the most key blocks)
-    std::vector<uint32_t> order;
-    for (uint32_t i = 0; i < n; i++)
-        if (item_len(items[i])) order.push_back(i);
-    std::stable_sort(order.begin(), order.end(),
-                     [&](uint32_t a, uint32_t b) { return item_len(items[a]) > item_len(items[b]); });
+    const std::vector<uint32_t> order = attn_order(items, n);
+    const uint64_t records = d->ws ? attn_records(d, items, n) : 0;
+    float *part_o = (float *)d->ws;
+    float *part_ml = records ? (float *)((char *)d->ws + up256(records * d->hd * 4)) : nullptr;
     for (size_t c0 = 0; c0 < order.size(); c0 += kMaxAttnItems) {
         AttnArgs a;
         memset(&a, 0, sizeof a);
@@ -308,22 +373,52 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         a.group = d->nq / d->nkv;
         a.scale_log2 = (float)((double)d->scale * 1.4426950408889634);
         a.window = d->window;
-        uint32_t k = 0;
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+        CombineArgs cb;
+        memset(&cb, 0, sizeof cb);
+        cb.part_o = part_o;
+        cb.part_ml = part_ml;
+        cb.out = d->out;
+        cb.ldo = d->ldo;
+        cb.nq = d->nq;
+        cb.hd = d->hd;
+        uint32_t k = 0, part = 0;
+        double pairs = 0;
         for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++, k++) {
             const enc_item &it = items[order[c]];
-            a.items[k].r0a = it.r[0].r0;
-            a.items[k].na = it.r[0].n;
-            a.items[k].r0b = it.nr > 1 ? it.r[1].r0 : 0;
-            a.items[k].nb = it.nr > 1 ? it.r[1].n : 0;
+            AttnItemK &ik = a.items[k];
+            ik.r0a = it.r[0].r0;
+            ik.na = it.r[0].n;
+            ik.r0b = it.nr > 1 ? it.r[1].r0 : 0;
+            ik.nb = it.nr > 1 ? it.r[1].n : 0;
+            const uint32_t L = item_len(it);
+            const KvSplit ks = records ? kv_split(d, L) : KvSplit{1, L};
+            ik.nsplit = ks.n;
+            ik.chunk = ks.chunk;
+            if (ks.n > 1) {
+                ik.part0 = part;
+                part += ks.n * L * d->nq;
+                cb.items[cb.nitems] = ik;
+                cb.row0[cb.nitems + 1] = cb.row0[cb.nitems] + L;
+                cb.nitems++;
+            }
+            pairs += visible_pairs(L, d->window);
         }
         a.nitems = k;
-        double pairs = 0;
-        for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++)
-            pairs += visible_pairs(item_len(items[order[c]]), d->window);
         hipError_t h = prof_launch(ENC_CLASS_ATTN, s, 4.0 * d->hd * d->nq * pairs, 0.0, [&] {
             return d->path == ENC_I8F16 ? launch_attn_f16(a, d->hd, s) : launch_attn_f32(a, d->hd, s);
         });
         if (h != hipSuccess) return h;
+        if (cb.nitems) {
+            // bytes: every partial (hd + 2 floats) read once, the merged rows written once
+            const double rec = (double)part, esz = d->path == ENC_I8F16 ? 2 : 4;
+            const double bytes = rec * (d->hd + 2) * 4 + (double)cb.row0[cb.nitems] * d->nq * d->hd * esz;
+            h = prof_launch(ENC_CLASS_ATTN, s, 0.0, bytes, [&] {
+                return launch_attn_combine(cb, d->path == ENC_I8F16, s);
+            });
+            if (h != hipSuccess) return h;
+        }
     }
     return hipSuccess;
 }
@@ -441,14 +536,33 @@ hipError_t pool_items(const enc_item *items, uint32_t nitems, uint32_t rows, uin
 }
 
 struct WsPlan {
-    size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0, total = 0;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, total = 0;
+    size_t part_bytes = 0;
 };
 
-size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+// The attention descriptor of one layer over the batch's panel.
+enc_attn_desc layer_attn_desc(const enc_layer &L, uint32_t rows) {
+    const uint32_t qw = L.nq * L.hd, kw = L.nkv * L.hd;
+    enc_attn_desc a{};
+    a.path = L.path;
+    a.ld = qw + 2 * kw;
+    a.q_col = 0;
+    a.k_col = qw;
+    a.v_col = qw + kw;
+    a.ldo = qw;
+    a.nq = L.nq;
+    a.nkv = L.nkv;
+    a.hd = L.hd;
+    a.scale = L.attn_scale;
+    a.window = L.window;
+    a.rows = rows;
+    return a;
+}
 
-WsPlan plan_ws(const enc_model *M, uint32_t rows) {
+WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
     WsPlan p;
-    size_t a = 0, panel = 0, att = 0, t = 0, gu = 0, m = 0, h = 0;
+    const uint32_t rows = B->rows;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0;
     for (uint32_t l = 0; l < M->nlayers; l++) {
         const enc_layer &L = M->layers[l];
         const size_t esz = L.path == ENC_I8F16 ? 2 : 4;
@@ -456,6 +570,8 @@ WsPlan plan_ws(const enc_model *M, uint32_t rows) {
         panel = std::max(panel, (size_t)rows * (L.nq + 2 * L.nkv) * L.hd * esz);
         att = std::max(att, (size_t)rows * L.nq * L.hd * esz);
         t = std::max(t, (size_t)rows * L.d * 4);
+        const enc_attn_desc ad = layer_attn_desc(L, rows);
+        part = std::max(part, attn_ws_bytes(&ad, B->items, B->nitems));
         m = std::max(m, (size_t)rows * L.ff * (L.mlp == ENC_MLP_GELU_TANH ? 4 : esz));
         h = std::max(h, (size_t)rows * L.d * 4);
     }
@@ -464,7 +580,8 @@ WsPlan plan_ws(const enc_model *M, uint32_t rows) {
     p.panel = off; off += up256(panel);
     p.att = off; off += up256(att);
     p.t = off; off += up256(t);
-    p.gu = off; off += up256(gu);
+    p.part = off; off += up256(part);
+    p.part_bytes = up256(part);
     p.m = off; off += up256(m);
     p.h = off; off += up256(h);  // residual stream (out holds it when final is NONE)
     p.total = off;
@@ -532,15 +649,17 @@ enc_status check_model(Err &e, const enc_model *M, const enc_batch *B) {
 
 struct Bufs {
     void *a, *panel, *att;
-    float *t, *gu;
+    float *t;
+    void *part;
+    size_t part_bytes;
     void *m;
     float *h;
 };
 
 Bufs carve(void *ws, const WsPlan &p) {
     char *b = (char *)ws;
-    return Bufs{b + p.a, b + p.panel, b + p.att, (float *)(b + p.t), (float *)(b + p.gu), b + p.m,
-                (float *)(b + p.h)};
+    return Bufs{b + p.a, b + p.panel, b + p.att, (float *)(b + p.t), p.part_bytes ? b + p.part : nullptr,
+                p.part_bytes, b + p.m, (float *)(b + p.h)};
 }
 
 #define TRY(expr)                                                                               \
@@ -588,21 +707,11 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
         TRY(rows_qk(q, i8, s));
     }
     {
-        enc_attn_desc a{};
-        a.path = L.path;
+        enc_attn_desc a = layer_attn_desc(L, rows);
         a.qkv = b.panel;
-        a.ld = ld;
-        a.q_col = 0;
-        a.k_col = qw;
-        a.v_col = qw + kw;
         a.out = b.att;
-        a.ldo = qw;
-        a.nq = L.nq;
-        a.nkv = L.nkv;
-        a.hd = hd;
-        a.scale = L.attn_scale;
-        a.window = L.window;
-        a.rows = rows;
+        a.ws = b.part;
+        a.ws_bytes = b.part_bytes;
         TRY(run_attention(&a, B->items, B->nitems, s));
     }
     // output projection: sandwich -> T; pre-LN -> h += att Wo^T + bo
@@ -872,9 +981,15 @@ enc_status enc_mfma_peak(enc_ctx *ctx, uint32_t path, uint32_t blocks, uint32_t 
     return finish(ctx, e);
 }
 
-size_t enc_workspace_bytes(const enc_model *model, uint32_t rows) {
-    if (!model || (model->nlayers && !model->layers)) return 0;
-    return plan_ws(model, rows).total;
+size_t enc_workspace_bytes(const enc_model *model, const enc_batch *batch) {
+    if (!model || (model->nlayers && !model->layers) || !batch || (batch->nitems && !batch->items))
+        return 0;
+    return plan_ws(model, batch).total;
+}
+
+size_t enc_attention_workspace_bytes(const enc_attn_desc *desc, const enc_item *items, uint32_t nitems) {
+    if (!desc || (nitems && !items)) return 0;
+    return attn_ws_bytes(desc, items, nitems);
 }
 
 enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_batch *batch, float *h,
@@ -888,7 +1003,7 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
     }
     enc_model M{1, layer, ENC_FINAL_NONE, nullptr, nullptr, 0.0f};
     if (check_model(e, &M, batch) != ENC_OK) return finish(ctx, e);
-    const WsPlan p = plan_ws(&M, batch->rows);
+    const WsPlan p = plan_ws(&M, batch);
     if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(h, 16)) {
         e.set(ENC_EINVAL, "encoder_layer_forward: workspace needs %zu bytes, 256-byte aligned",
               p.total);
@@ -917,7 +1032,7 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
         e.set(ENC_EINVAL, "encoder_forward: no layers");
         return finish(ctx, e);
     }
-    const WsPlan p = plan_ws(model, batch->rows);
+    const WsPlan p = plan_ws(model, batch);
     if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(x, 16) || !aligned(out, 16)) {
         e.set(ENC_EINVAL, "encoder_forward: workspace needs %zu bytes, 256-byte aligned", p.total);
         return finish(ctx, e);

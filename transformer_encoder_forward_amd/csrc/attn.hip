@@ -10,6 +10,8 @@
 // and `att_plan`; zimage.rs (cortiq-engine 0.7.6), module doc and `PFa`.
 #include <math.h>
 
+#include <algorithm>
+
 #include "attn_impl.h"
 
 namespace enc {
@@ -23,18 +25,25 @@ struct ItemCtx {
     int L, q_lo, q_hi, k_lo, k_hi;
 };
 
+// Item, query range and key range of a block.  A key-split item's tiles are
+// (q-tile, split) pairs, split fastest; split s sees keys [s*chunk, (s+1)*chunk).
 template <int QT>
-__device__ __forceinline__ void locate(const AttnArgs &a, uint32_t tile, ItemCtx &c) {
+__device__ __forceinline__ void locate(const AttnArgs &a, uint32_t tile, ItemCtx &c, int &split) {
     uint32_t sel = 0;
     for (uint32_t i = 1; i < a.nitems; i++)
         if (tile >= a.items[i].tile0) sel = i;
     c.it = a.items[sel];
     c.L = (int)(c.it.na + c.it.nb);
-    c.q_lo = (int)(tile - c.it.tile0) * QT;
+    const uint32_t local = tile - c.it.tile0;
+    split = (int)(local % c.it.nsplit);
+    c.q_lo = (int)(local / c.it.nsplit) * QT;
     c.q_hi = min(c.q_lo + QT, c.L);
     c.k_lo = 0;
     c.k_hi = c.L;
-    if (a.window) {
+    if (c.it.nsplit > 1) {
+        c.k_lo = split * (int)c.it.chunk;
+        c.k_hi = min(c.L, c.k_lo + (int)c.it.chunk);
+    } else if (a.window) {
         c.k_lo = max(0, c.q_lo - (int)a.window);
         c.k_hi = min(c.L, c.q_hi + (int)a.window);
     }
@@ -89,7 +98,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
 
     const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
     ItemCtx c;
-    locate<QT>(a, tile, c);
+    int split;
+    locate<QT>(a, tile, c, split);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hf = lane >> 5;
     const int kvh = head / a.group;
@@ -191,17 +201,77 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
         if (b + 1 < nblk) sstore(buf ^ 1);
         __syncthreads();
     }
-    if (qvalid) {
-        const float inv = 1.0f / l_run;
-        float *out = reinterpret_cast<float *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+    if (!qvalid) return;
+    if (c.it.nsplit > 1) {
+        // partial result of this key split: unnormalised O, running max and sum
+        const size_t rec = c.it.part0 + ((size_t)split * c.L + tq) * a.nq + head;
+        float *po = a.part_o + rec * HD;
 #pragma unroll
         for (int d = 0; d < HD / 32; d++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                f32x4 v = {o[d][4 * q] * inv, o[d][4 * q + 1] * inv, o[d][4 * q + 2] * inv,
-                           o[d][4 * q + 3] * inv};
-                st4(out + 32 * d + 8 * q + 4 * hf, v);
+                f32x4 v = {o[d][4 * q], o[d][4 * q + 1], o[d][4 * q + 2], o[d][4 * q + 3]};
+                st4(po + 32 * d + 8 * q + 4 * hf, v);
             }
+        if (hf == 0) {
+            a.part_ml[2 * rec] = m_run;
+            a.part_ml[2 * rec + 1] = l_run;
+        }
+        return;
+    }
+    const float inv = 1.0f / l_run;
+    float *out = reinterpret_cast<float *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+#pragma unroll
+    for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            f32x4 v = {o[d][4 * q] * inv, o[d][4 * q + 1] * inv, o[d][4 * q + 2] * inv,
+                       o[d][4 * q + 3] * inv};
+            st4(out + 32 * d + 8 * q + 4 * hf, v);
+        }
+}
+
+// Merge of the key splits: for item row t and head h with partials
+// (o_s, m_s, l_s), s = 0..S-1 in increasing order,
+//   out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s,
+// the same softmax as one pass over all keys.  A thread owns 4 channels of one
+// (row, head); the order over s is fixed, so the result is deterministic.
+template <bool F16>
+__global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
+    const uint32_t c4 = a.hd / 4;
+    const uint64_t total = (uint64_t)a.row0[a.nitems] * a.nq * c4;
+    for (uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+         g += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t ch = (uint32_t)(g % c4);
+        const uint64_t rh = g / c4;
+        const uint32_t head = (uint32_t)(rh % a.nq), rt = (uint32_t)(rh / a.nq);
+        uint32_t sel = 0;
+        for (uint32_t i = 1; i < a.nitems; i++)
+            if (rt >= a.row0[i]) sel = i;
+        const AttnItemK &it = a.items[sel];
+        const uint32_t t = rt - a.row0[sel], L = it.na + it.nb, S = it.nsplit;
+        float M = -INFINITY;
+        for (uint32_t s = 0; s < S; s++)
+            M = fmaxf(M, a.part_ml[2 * (it.part0 + ((size_t)s * L + t) * a.nq + head)]);
+        const float Mu = (M == -INFINITY) ? 0.0f : M;
+        float lsum = 0.0f;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (uint32_t s = 0; s < S; s++) {
+            const size_t rec = it.part0 + ((size_t)s * L + t) * a.nq + head;
+            const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * rec] - Mu);
+            lsum += w * a.part_ml[2 * rec + 1];
+            const f32x4 v = ld4(a.part_o + rec * a.hd + 4 * ch);
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] += w * v[e];
+        }
+        const float inv = 1.0f / lsum;
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[e] *= inv;
+        const size_t off = (size_t)row_of(it, (int)t) * a.ldo + head * a.hd + 4 * ch;
+        if (F16)
+            st4h(reinterpret_cast<_Float16 *>(a.out) + off, acc);
+        else
+            st4(reinterpret_cast<float *>(a.out) + off, acc);
     }
 }
 
@@ -228,6 +298,17 @@ hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s) {
 // per CU, else 128.  With a window, a block's first key depends on its query
 // tile, so the tile size must not change between launches of the same item:
 // always 128 queries.  Every choice sums each query's keys in the same order.
+hipError_t launch_attn_combine(const CombineArgs &a, bool f16_out, hipStream_t s) {
+    const uint64_t total = (uint64_t)a.row0[a.nitems] * a.nq * (a.hd / 4);
+    if (!total) return hipSuccess;
+    const uint32_t blocks = (uint32_t)std::min<uint64_t>((total + 255) / 256, 8192);
+    if (f16_out)
+        hipLaunchKernelGGL(f32path::attn_combine_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(f32path::attn_combine_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s) {
     if (hd == 64) return attn::launch<64, true, 4, 4, true>(a, s);
     if (a.window) return attn::launch_f16d<4, 2>(a, s);

@@ -700,12 +700,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
     }
 }
 
-// Tiles of the launch for QT queries per block (fills tile0, ntiles).
+// Tiles of the launch for QT queries per block (fills tile0, ntiles): q-tiles
+// times key splits per item.  Only the f32 kernel reads the split fields; the
+// host gives every item of an f16 launch nsplit = 1.
 inline uint32_t plan_tiles(AttnArgs &a, int QT) {
     uint32_t tiles = 0;
     for (uint32_t i = 0; i < a.nitems; i++) {
         a.items[i].tile0 = tiles;
-        tiles += (a.items[i].na + a.items[i].nb + QT - 1) / QT;
+        tiles += (a.items[i].na + a.items[i].nb + QT - 1) / QT * a.items[i].nsplit;
     }
     a.ntiles = tiles;
     return tiles;

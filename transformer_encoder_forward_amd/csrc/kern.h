@@ -31,7 +31,11 @@ struct GemmArgs {
 
 struct AttnItemK {
     uint32_t r0a, na, r0b, nb;  // ranges (nb = 0 for one range)
-    uint32_t tile0;             // first q-tile of this item in the launch
+    uint32_t tile0;             // first tile of this item in the launch
+    // key split (f32 path): nsplit chunks of `chunk` keys; the item's tiles are
+    // (q-tile, split) pairs, split fastest.  Partial results of split s, item
+    // row t, head h sit at record part0 + (s * L + t) * nq + h.
+    uint32_t nsplit, chunk, part0;
 };
 
 struct AttnArgs {
@@ -42,6 +46,17 @@ struct AttnArgs {
     float scale_log2;       // scale * log2(e): the softmax runs in base 2
     uint32_t window;
     uint32_t nitems, ntiles;
+    float *part_o;   // [records][hd] unnormalised outputs of split items
+    float *part_ml;  // [records][2] running max (base 2) and sum
+    AttnItemK items[kMaxAttnItems];
+};
+
+// Merge of the key-split partial results into the attention output.
+struct CombineArgs {
+    const float *part_o, *part_ml;
+    void *out;
+    uint32_t ldo, nq, hd, nitems;
+    uint32_t row0[kMaxAttnItems + 1];  // prefix of item lengths over the split items
     AttnItemK items[kMaxAttnItems];
 };
 
@@ -90,6 +105,7 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s);
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s);
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s);
+hipError_t launch_attn_combine(const CombineArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_rms_norm(const NormArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_layer_norm(const NormArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_add_norm(const AddNormArgs &a, bool f16_out, hipStream_t s);

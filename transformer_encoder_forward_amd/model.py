@@ -62,11 +62,11 @@ class DeviceModel:
                 self.keep.append(dev)
                 setattr(self.model, n, dev.data_ptr())
 
-    def workspace_bytes(self, rows):
-        return B.lib().enc_workspace_bytes(C.byref(self.model), rows)
+    def workspace_bytes(self, batch: "DeviceBatch"):
+        return B.lib().enc_workspace_bytes(C.byref(self.model), C.byref(batch.batch))
 
-    def workspace(self, rows, device="cuda"):
-        return torch.empty(self.workspace_bytes(rows), dtype=torch.uint8, device=device)
+    def workspace(self, batch: "DeviceBatch", device="cuda"):
+        return torch.empty(self.workspace_bytes(batch), dtype=torch.uint8, device=device)
 
 
 class DeviceBatch:
