@@ -108,7 +108,8 @@ def test_gemm_packed_rows_bit_identical():
 @pytest.mark.parametrize("path,act,n,ff,d", [
     (B.ENC_F32, "gelu", 1000, 2048, 512), (B.ENC_F32, "gelu", 37, 200, 128),
     (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64),
-    (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192)])
+    (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192),
+    (B.ENC_I8F16, "silu", 77, 160, 80)])
 def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
     bit for bit, and == the oracle within tolerance."""
@@ -165,9 +166,11 @@ def test_gemm_i8f16_integer_exact(n, m, k):
     assert np.array_equal(host(Y), ref)
 
 
-# shapes that take the 256 x 256 direct-to-LDS kernel (K % 64 == 0, >= 200 tiles):
-# one K stage, exactly the LDS ring, ring wrap-around; ragged rows and columns
-@pytest.mark.parametrize("n,m,k", [(520, 17000, 64), (520, 17000, 192), (513, 17000, 320)])
+# shapes that take the direct-to-LDS kernel (K % 64 == 0): 256 x 256 tiles (>= 128
+# of them) and 128 x 256 tiles (fewer); one K stage, exactly the LDS ring, ring
+# wrap-around; ragged rows and columns
+@pytest.mark.parametrize("n,m,k", [(520, 17000, 64), (520, 17000, 192), (513, 17000, 320),
+                                   (130, 1000, 64), (257, 3000, 192), (1, 300, 320)])
 def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
     say(f"gemm i8f16 wide integer n={n} m={m} k={k}")
     rng = np.random.default_rng(n + m + k)
@@ -183,7 +186,7 @@ def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
 
 def test_gemm_i8f16_kernel_choice_bit_identical():
     """Rows computed in a launch of 256 x 256 tiles and in small launches of
-    128 x 128 tiles give the same bits (one K order for every int8 kernel)."""
+    128 x 256 tiles give the same bits (one K order for every int8 kernel)."""
     rng = np.random.default_rng(77)
     n, m, k = 520, 17000, 256
     x = rng.normal(0, 1, (n, k)).astype(np.float16)

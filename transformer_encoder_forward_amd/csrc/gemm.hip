@@ -3,7 +3,8 @@
 // The tile shape is chosen per launch from the problem size.  f32: large
 // problems take 128 x 128 tiles, small ones (too few 128 x 128 tiles to fill
 // the 256 CUs twice over) take 64 x 64 tiles.  int8 x f16: large problems take
-// the 256 x 256 kernel fed by direct global -> LDS loads, the rest 128 x 128.
+// the kernel fed by direct global -> LDS loads (256 x 256 tiles, or 128 x 256
+// when there are few of those), and K % 64 != 0 the register-staged 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
 // K order, so an output element is summed in the same order whatever tile it
 // falls in: the choice never changes a result bit, and packed and separate
@@ -37,23 +38,30 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
 
 namespace {
 
-// The direct-to-LDS kernel (256 x 256 tiles, one block per CU) needs K % 64 == 0
-// and enough tiles to occupy most CUs; otherwise 128 x 128 tiles, two blocks
-// per CU.  Both sum in the same K order.
+// The direct-to-LDS kernel needs K % 64 == 0.  256 x 256 tiles (8 waves of
+// 128 x 64, one block per CU) when the launch has at least 128 of them; fewer
+// (the output projections of a 1056-row DiT batch: 75 tiles) take 128 x 256
+// tiles (8 waves of 64 x 64), which measured 10-40% faster there.  Otherwise
+// the register-staged 128 x 128 kernel.  All sum in the same K order.
 bool k64(const GemmArgs &a) {
     for (uint32_t i = 0; i < a.nitems; i++)
         if (a.items[i].k % 64) return false;
     return true;
 }
 
-constexpr uint32_t kWideTiles = 200;
+constexpr uint32_t kWideTiles = 128;
 
 }  // namespace
 
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
-    if (k64(a) && tiles_of(a, 256, gated ? 128 : 256) >= kWideTiles)
-        return gated ? gemm::launch_q8d<true>(a, s) : gemm::launch_q8d<false>(a, s);
+    if (k64(a)) {
+        if (tiles_of(a, 256, gated ? 128 : 256) >= kWideTiles)
+            return gated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
+                         : gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
+        return gated ? gemm::launch_q8d<128, 256, 2, 4, 1, true>(a, s)
+                     : gemm::launch_q8d<128, 256, 2, 4, 1, false>(a, s);
+    }
     if (gated) return gemm::launch_gated<128, 128, 64, 2, true, 2>(a, s);
     return gemm::launch<128, 128, 64, 2, 2, true, 2>(a, s);
 }

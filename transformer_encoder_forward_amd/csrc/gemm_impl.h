@@ -705,11 +705,14 @@ __device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
 // ---------------------------------------------------------------------------
 // int8 x f16 GEMM fed by direct global -> LDS loads (global_load_lds_dwordx4).
 //
-// 256 x 256 block tile, 8 waves as 2 x 4, each wave 128 x 64 outputs (4 x 2
-// accumulator blocks), W kept as int8 in LDS and widened per fragment.  Three
-// LDS stages of 64 K each (48 KB): the loads of stage s+3 are issued as soon
-// as every wave has finished reading stage s, so two stages of loads are in
-// flight while one is computed, and no register holds staged data.
+// BM x BN block tile, WGM x WGN waves, each wave (BM/WGM) x (BN/WGN) outputs
+// (FM x FN accumulator blocks of 32 x 32), W kept as int8 in LDS and widened
+// per fragment.  Three LDS stages of 64 K each: the loads of stage s+3 are
+// issued as soon as every wave has finished reading stage s, so two stages of
+// loads are in flight while one is computed, and no register holds staged
+// data.  The large-problem instantiation is 256 x 256 with 8 waves (128 x 64
+// each, one block per CU, 48 KB per stage); 128-row tiles serve launches with
+// too few 256-row tiles to spread over the CUs.
 //
 // A load instruction writes 64 lanes x 16 bytes to 1 KB of consecutive LDS, so
 // the LDS tiles are swizzled instead of padded: X row r (128 bytes = 8 chunks
@@ -720,22 +723,31 @@ __device__ __forceinline__ f16x8 widen8(uint32_t w0, uint32_t w1) {
 // The compiler cannot tell LDS reads apart from the in-flight LDS-bound loads
 // and would wait for all of them before every read, so the fragment reads are
 // issued as ds_read_b128 in inline assembly and their completion is awaited
-// explicitly (lgkmcnt), tying the fragment registers to the wait.
+// explicitly (lgkmcnt), each fragment register then passed through an empty
+// asm statement so that no use moves above the wait.
 //
 // Same K order as gemm_kernel<.., 64, .., true, ..>: stage 64, lane half h
 // owns k in [32h, 32h + 32), k-step kk the 8 values at 32h + 8kk.  Requires
 // K % 64 == 0.  Rows past n and columns past m load clamped (finite) rows and
-// are never stored.
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4 &a0, u32x4 &a1, u32x4 &a2, u32x4 &a3, u32x4 &b0, u32x4 &b1) {
-    asm volatile("s_waitcnt lgkmcnt(%6)" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3), "+v"(b0), "+v"(b1) : "n"(N));
+// are never stored.  Gated: each wave column holds 32 gate and 32 up rows of
+// the same 32 output columns (BN / WGN == 64).
+template <int FM, int FN>
+__device__ __forceinline__ void frag_ready(u32x4 (&a)[FM], u32x4 (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; i++) ready(a[i]);
+#pragma unroll
+    for (int j = 0; j < FN; j++) ready(b[j]);
 }
 
-template <bool GATED>
-__global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
-    constexpr int BM = 256, BN = 256, WGN = 4, BK = 64, FM = 4, FN = 2, NS = 3;
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs a) {
+    constexpr int NW = WGM * WGN, BK = 64, NS = 3;
+    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
     constexpr int A_BYTES = BM * BK * 2, S_BYTES = A_BYTES + BN * BK;
-    constexpr int NDMA = 6;  // load instructions per wave per stage (4 X + 2 W)
+    constexpr int AL = A_BYTES / 1024 / NW, BL = BN * BK / 1024 / NW;  // loads per wave per stage
+    constexpr int NDMA = AL + BL;
+    static_assert(AL >= 1 && BL >= 1 && AL * 1024 * NW == A_BYTES && BL * 1024 * NW == BN * BK, "loads");
+    static_assert(FM >= 1 && FN >= 1 && (!GATED || BN / WGN == 64), "tile");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
 
     TileCtx t;
@@ -758,17 +770,19 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
     const int li = lane & 31, hf = lane >> 5;
     const int wr = wave / WGN, wc = wave % WGN;
 
-    // sources of this lane's load instructions (k offset added per stage)
-    const _Float16 *asrc[4];
+    // sources of this lane's load instructions (k offset added per stage):
+    // X load q of this wave covers tile rows 8 (AL wave + q) .. + 7, W load q
+    // covers W rows 16 (BL wave + q) .. + 15
+    const _Float16 *asrc[AL];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-        const int r = 8 * (4 * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+    for (int q = 0; q < AL; q++) {
+        const int r = 8 * (AL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
         asrc[q] = X + (size_t)min(t.row0 + r, n - 1) * t.it.ldx + 8 * c;
     }
-    const int8_t *bsrc[2];
+    const int8_t *bsrc[BL];
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-        const int r = 16 * (2 * wave + q) + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+    for (int q = 0; q < BL; q++) {
+        const int r = 16 * (BL * wave + q) + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
         const int8_t *w = wg;
         int col = t.col0 + r;
         if constexpr (GATED) {
@@ -781,20 +795,21 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
         uint8_t *buf = smem + (s % NS) * S_BYTES;
         const int k0 = s * BK;
 #pragma unroll
-        for (int q = 0; q < 4; q++)
-            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(asrc[q] + k0), ENC_SHARED(buf + (4 * wave + q) * 1024), 16,
+        for (int q = 0; q < AL; q++)
+            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(asrc[q] + k0), ENC_SHARED(buf + (AL * wave + q) * 1024), 16,
                                              0, 0);
 #pragma unroll
-        for (int q = 0; q < 2; q++)
+        for (int q = 0; q < BL; q++)
             __builtin_amdgcn_global_load_lds(ENC_GLOBAL(bsrc[q] + k0),
-                                             ENC_SHARED(buf + A_BYTES + (2 * wave + q) * 1024), 16, 0, 0);
+                                             ENC_SHARED(buf + A_BYTES + (BL * wave + q) * 1024), 16, 0, 0);
     };
 
-    // fragment addresses: X row wr*128 + 32 i + li, chunk 4 hf + kk; W row
-    // wc*64 + 32 j + li, chunk 2 hf + p (p = kk / 2, one read per two k-steps)
+    // fragment addresses: X row wr*(BM/WGM) + 32 i + li, chunk 4 hf + kk; W
+    // row wc*(BN/WGN) + 32 j + li, chunk 2 hf + p (p = kk / 2, one read per two
+    // k-steps)
     const uint32_t lds0 = lds_offset(smem);
-    const uint32_t arow = lds0 + (uint32_t)(wr * 128 + li) * 128u;
-    const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * 64 + li) * 64u;
+    const uint32_t arow = lds0 + (uint32_t)(wr * (BM / WGM) + li) * 128u;
+    const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * (BN / WGN) + li) * 64u;
     const int sa = (li >> 1) & 7, sb = (li >> 2) & 3;
     uint32_t asw[4], bsw[2];
 #pragma unroll
@@ -846,14 +861,17 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
     for (int s = 0; s < nst; s++) {
         const int b = s % NS;
         read_a(fa1, b, 1);
-        lgkm_wait<4>(fa0[0], fa0[1], fa0[2], fa0[3], fb0[0], fb0[1]);
+        lgkm_wait_n<FM>();  // fa0, fb0 landed (fa1 may still be in flight)
+        frag_ready(fa0, fb0);
         mma(fa0, fb0, 0);
         read_a(fa0, b, 2);
         read_b(fb1, b, 1);
-        lgkm_wait<6>(fa1[0], fa1[1], fa1[2], fa1[3], fb0[0], fb0[1]);
+        lgkm_wait_n<FM + FN>();  // fa1 landed
+        frag_ready(fa1, fb0);
         mma(fa1, fb0, 1);
         read_a(fa1, b, 3);
-        lgkm_wait<4>(fa0[0], fa0[1], fa0[2], fa0[3], fb1[0], fb1[1]);
+        lgkm_wait_n<FM>();  // fa0, fb1 landed
+        frag_ready(fa0, fb1);
         mma(fa0, fb1, 0);
         // stage s+1 landed (own loads), own reads of buffer b done; after the
         // barrier every wave's are, so b takes stage s+3
@@ -861,7 +879,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
             vm_wait<NDMA>();
         else
             vm_wait<0>();
-        lgkm_wait<0>(fa1[0], fa1[1], fa1[2], fa1[3], fb1[0], fb1[1]);
+        lgkm_wait_n<0>();
+        frag_ready(fa1, fb1);
         block_barrier();
         if (s + 3 < nst) dma(s + 3);
         if (s + 1 < nst) {
@@ -876,7 +895,8 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                store_block<true>(a, t, acc[i][j], t.row0 + wr * 128 + i * 32, t.col0 + wc * 64 + j * 32, lane);
+                store_block<true>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
+                                  lane);
     } else {
         const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
         const int c = t.col0 + wc * 32 + li;
@@ -886,7 +906,7 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    const int row = t.row0 + wr * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                     if (row >= n) continue;
                     const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
                     const float v = (gelu ? gelu_tanh(g) : silu(g)) * u;
@@ -900,11 +920,11 @@ __global__ __launch_bounds__(512, 1) void gemm_q8d_kernel(GemmArgs a) {
     }
 }
 
-template <bool GATED>
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
 hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
-    const uint32_t tiles = plan_tiles(g, 256, GATED ? 128 : 256);
+    const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_q8d_kernel<GATED>), dim3(tiles), dim3(512), 0, s, g);
+    hipLaunchKernelGGL((gemm_q8d_kernel<BM, BN, WGM, WGN, MINB, GATED>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
     return hipGetLastError();
 }
 
