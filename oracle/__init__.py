@@ -56,6 +56,7 @@ _LAYER_PTRS_S = ["sq", "sk", "sv", "so", "s_gate", "s_up", "s_down"]
 _LAYER_PTRS_B = ["bq", "bk", "bv", "bo", "b_up", "b_down"]
 _LAYER_PTRS_N = ["norm1_w", "norm1_b", "norm2_w", "norm2_b", "post_attn_w", "post_ff_w",
                  "q_norm_w", "k_norm_w"]
+_LAYER_PTRS_PLE = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
 
 
 class Layer(C.Structure):
@@ -65,7 +66,10 @@ class Layer(C.Structure):
                 + [(n, C.POINTER(C.c_float)) for n in _LAYER_PTRS_F]
                 + [(n, C.POINTER(C.c_int8)) for n in _LAYER_PTRS_Q]
                 + [(n, C.POINTER(C.c_float)) for n in _LAYER_PTRS_S + _LAYER_PTRS_B
-                   + _LAYER_PTRS_N])
+                   + _LAYER_PTRS_N]
+                + [("v_norm", C.c_int32), ("n_ple", C.c_int32), ("scalar", C.c_double),
+                   ("ple_scale", C.c_double)]
+                + [(n, C.POINTER(C.c_float)) for n in _LAYER_PTRS_PLE])
 
 
 class Model(C.Structure):
@@ -224,12 +228,24 @@ def attention(items, q, k, v, nq, nkv, hd, scale, window, rows=None, query_rows=
 # ----------------------------------------------------------------------- forward
 
 def _layer_struct(cfg, t, keep):
+    """A layer from the workload config and the layer's dict; per-layer values
+    (window, rope_base, scalar) in the dict override the config's."""
     L = Layer()
-    for n in ("block", "path", "mlp", "d", "nq", "nkv", "hd", "ff", "window", "rope_sections"):
+    for n in ("block", "path", "mlp", "d", "nq", "nkv", "hd", "ff", "rope_sections"):
         setattr(L, n, int(cfg[n]))
+    L.window = int(t.get("window", cfg["window"]))
     L.eps = cfg["eps"]
     L.attn_scale = cfg["attn_scale"]
-    L.rope_base = cfg["rope_base"]
+    L.rope_base = float(t.get("rope_base", cfg["rope_base"]))
+    L.v_norm = 1 if cfg.get("v_norm") else 0
+    L.scalar = float(t.get("scalar", 1.0))
+    L.n_ple = int(cfg.get("n_ple", 0))
+    L.ple_scale = float(cfg.get("ple_scale", 1.0))
+    for n in _LAYER_PTRS_PLE:
+        if t.get(n) is not None:
+            a, p = _f(t[n])
+            keep.append(a)
+            setattr(L, n, p)
     for fn, qn, sn in zip(_LAYER_PTRS_F, _LAYER_PTRS_Q, _LAYER_PTRS_S):
         if fn not in t:
             continue

@@ -387,6 +387,17 @@ typedef struct {
      * post_ff; q_norm/k_norm per head. */
     const float *norm1_w, *norm1_b, *norm2_w, *norm2_b;
     const float *post_attn_w, *post_ff_w, *q_norm_w, *k_norm_w;
+    /* text-encoder options of [EG] `LayerSpec` / `TextSpec` (sandwich block):
+     * v_norm: weightless RMS of every v head ([EG] `Prog::qkv`, "v norm");
+     * scalar: the layer's last residual update is H = (H + .) * scalar
+     *   ([EG] `Prog::add_norm` "H = (H + rms(T)·w)·post", post = the layer
+     *   scalar); 0 is read as 1;
+     * n_ple > 0: the per-layer-input branch ([EG] `TextGpu::forward`, "per-layer
+     *   input") with ple_in, ple_gate [n_ple][d], ple_proj [d][n_ple], the
+     *   model-wide ple_in_norm_w [n_ple] and this layer's ple_post_w [d]. */
+    int32_t v_norm, n_ple;
+    double scalar, ple_scale;
+    const float *ple_in, *ple_gate, *ple_proj, *ple_in_norm_w, *ple_post_w;
 } or_layer;
 
 typedef struct {
@@ -429,10 +440,13 @@ static void maybe_f16(int on, double *v, int64_t n)
  * Pre-LN block ([VE] `encode_image_gpu`, step 3):
  *   A = LN(H; norm1);  q|k|v = A W^T + b;  att = attention
  *   H += att Wo^T + bo;  A = LN(H; norm2);  H += gelu_tanh(A Wu^T + bu) Wd^T + bd
+ * Options of the sandwich block: v_norm right after the q/k norm + RoPE; the
+ * per-layer-input branch after the FFN, reading X0 (the forward's input rows);
+ * the layer scalar multiplying H after the layer's last residual add.
  * `f16_sites` rounds to binary16 exactly where the int8 path stores half; 0
  * gives the pure-f64 diagnostic. */
 static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_item *items,
-                          const int32_t *pos, double *H, int f16_sites)
+                          const int32_t *pos, double *H, const double *X0, int f16_sites)
 {
     int d = L->d, hd = L->hd, nq = L->nq, nkv = L->nkv, ff = L->ff;
     int qw = nq * hd, kw = nkv * hd;
@@ -463,6 +477,11 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
         or_qk_norm_rope(rows, nkv, hd, K, L->k_norm_w, L->eps, L->rope_sections, pos, L->rope_base);
         maybe_f16(r16, Q, rows * qw);
         maybe_f16(r16, K, rows * kw);
+        if (L->v_norm) {
+            /* every v head of every row is one hd-wide row of V */
+            or_rms_norm(rows * nkv, hd, V, NULL, L->eps, V);
+            maybe_f16(r16, V, rows * kw);
+        }
     }
     or_attention(nitems, items, nq, nkv, hd, Q, qw, K, kw, V, kw, Att, qw, L->attn_scale, L->window);
     maybe_f16(r16, Att, rows * qw);
@@ -491,10 +510,36 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
     }
     maybe_f16(r16, U, rows * ff);
     project(L, rows, ff, d, U, L->w_down, L->q_down, L->s_down, L->b_down, T);
+    const double scalar = L->scalar == 0.0 ? 1.0 : L->scalar;
     if (L->block == OR_SANDWICH)
         or_rms_norm(rows, d, T, L->post_ff_w, L->eps, T);
     for (int64_t i = 0; i < rows * d; i++)
         H[i] += T[i];
+    if (L->n_ple > 0) {
+        /* per-layer input ([EG] `TextGpu::forward`, after the FFN):
+         *   P = rms(ple_scale * (X0 ple_in^T); ple_in_norm)   ("Y = rms(pre·X)·w")
+         *   Z = gelu_tanh(H ple_gate^T) * P
+         *   H = (H + rms(Z ple_proj^T; ple_post)) * scalar */
+        int np = L->n_ple;
+        double *P = (double *)malloc(sizeof(double) * rows * np);
+        double *Z = (double *)malloc(sizeof(double) * rows * np);
+        or_linear(rows, d, np, X0, L->ple_in, NULL, P);
+        for (int64_t i = 0; i < rows * np; i++)
+            P[i] *= L->ple_scale;
+        or_rms_norm(rows, np, P, L->ple_in_norm_w, L->eps, P);
+        or_linear(rows, d, np, H, L->ple_gate, NULL, Z);
+        for (int64_t i = 0; i < rows * np; i++)
+            Z[i] = or_gelu_tanh(Z[i]) * P[i];
+        or_linear(rows, np, d, Z, L->ple_proj, NULL, T);
+        or_rms_norm(rows, d, T, L->ple_post_w, L->eps, T);
+        for (int64_t i = 0; i < rows * d; i++)
+            H[i] += T[i];
+        free(P);
+        free(Z);
+    }
+    if (scalar != 1.0)
+        for (int64_t i = 0; i < rows * d; i++)
+            H[i] *= scalar;
 
     free(A); free(Q); free(K); free(V); free(Att); free(T); free(G); free(U);
 }
@@ -517,7 +562,7 @@ OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, cons
     double *H = (double *)malloc(sizeof(double) * rows * d);
     memcpy(H, x, sizeof(double) * rows * d);
     for (int l = 0; l < M->nlayers; l++)
-        layer_forward(&M->layers[l], rows, nitems, items, pos, H, f16_sites);
+        layer_forward(&M->layers[l], rows, nitems, items, pos, H, x, f16_sites);
     if (M->final_kind == OR_FINAL_NONE) {
         memcpy(out, H, sizeof(double) * rows * d);
     } else if (M->final_kind == OR_FINAL_LN) {

@@ -268,22 +268,31 @@ def test_attention_closed_forms(oracle):
 def _zero_layer_weights(w):
     for t in w.layers:
         for n in list(t):
-            if n.startswith(("w", "b", "q_")) and n not in ("q_norm_w",):
+            if (n.startswith(("w", "b", "q_")) and n not in ("q_norm_w", "window")) or \
+                    n in ("ple_in", "ple_gate", "ple_proj"):
                 t[n] = np.zeros_like(t[n])
     return w
 
 
-@pytest.mark.parametrize("name", ["vit_layer_f32", "gemma_text_f32", "zimage_dit_1056"])
+@pytest.mark.parametrize("name", ["vit_layer_f32", "gemma_text_f32", "zimage_dit_1056",
+                                  "gemma_text_ple_f32"])
 def test_zero_weights_layer_is_identity(oracle, name):
+    """All projection weights zero: every residual update adds rms(0) = 0, so the
+    layer is the identity, times the layer scalar where there is one."""
     kw = dict(layers=2)
-    if name == "gemma_text_f32":
+    if name.startswith("gemma_text"):
         kw["lengths"] = [5, 9]
     if name == "zimage_dit_1056":
         kw.update(grid=2, ncap=2, overrides=dict(d=256, nq=2, nkv=2, ff=512))
     w = _zero_layer_weights(wl.make(name, **kw))
     w.cfg["final"] = wl.FINAL_NONE
     out = oracle.forward(w, f16_sites=False)
-    assert np.array_equal(out, w.x.astype(np.float64))
+    ref = w.x.astype(np.float64)
+    for t in w.layers:
+        ref = ref * t.get("scalar", 1.0)
+    assert np.array_equal(out, ref)
+    if name == "gemma_text_ple_f32":
+        assert not np.array_equal(ref, w.x.astype(np.float64)), "the scalars must act"
 
 
 def test_pre_ln_layer_matches_torch_encoder_layer(oracle):
@@ -314,11 +323,14 @@ def test_pre_ln_layer_matches_torch_encoder_layer(oracle):
     assert np.abs(out - ref).max() / np.abs(ref).max() < 1e-13
 
 
-def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16):
-    """Composition of torch f64 library ops in the sandwich order (independent check)."""
+def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None):
+    """Composition of torch f64 library ops in the sandwich order (independent check).
+    GQA by repeating each kv head over its query group; the text-encoder options
+    (v-norm, per-layer window, per-layer input from x0, layer scalar) as written
+    on the page."""
     F = torch.nn.functional
     T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
-    eps, hd, nq = c["eps"], c["hd"], c["nq"]
+    eps, hd, nq, nkv = c["eps"], c["hd"], c["nq"], c["nkv"]
     r16 = (lambda a: a.to(torch.float16).to(torch.float64)) if f16 else (lambda a: a)
     H = T(x)
     d = H.shape[1]
@@ -332,8 +344,8 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16):
     q, k, v = r16(lin(A, "wq")), r16(lin(A, "wk")), r16(lin(A, "wv"))
     cos, sin = pos_cos_sin
 
-    def qk(z, wn):
-        z = z.view(z.shape[0], nq, hd)
+    def qk(z, wn, nh):
+        z = z.view(z.shape[0], nh, hd)
         z = F.rms_norm(z, (hd,), T(wn), eps)
         S = hd // c["rope_sections"]
         parts = []
@@ -342,19 +354,21 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16):
             cs, sn = cos[s][:, None, :], sin[s][:, None, :]
             a, b = zz[..., :S // 2], zz[..., S // 2:]
             parts += [a * cs - b * sn, b * cs + a * sn]
-        return r16(torch.cat(parts, -1).reshape(z.shape[0], nq * hd))
+        return r16(torch.cat(parts, -1).reshape(z.shape[0], nh * hd))
 
-    q, k = qk(q, t["q_norm_w"]), qk(k, t["k_norm_w"])
+    q, k = qk(q, t["q_norm_w"], nq), qk(k, t["k_norm_w"], nkv)
+    if c.get("v_norm"):
+        v = r16(F.rms_norm(v.view(-1, nkv, hd), (hd,), None, eps).reshape(v.shape[0], nkv * hd))
     att = torch.zeros_like(q)
+    W = t.get("window", c["window"])
     for rr in items:
         idx = torch.cat([torch.arange(r0, r0 + n) for r0, n in rr])
         L = len(idx)
         i = torch.arange(L)
-        W = c["window"]
         mask = (i[:, None] - i[None, :]).abs() <= W if W else torch.ones(L, L, dtype=torch.bool)
         qh = q[idx].view(L, nq, hd).transpose(0, 1)
-        kh = k[idx].view(L, nq, hd).transpose(0, 1)
-        vh = v[idx].view(L, nq, hd).transpose(0, 1)
+        kh = k[idx].view(L, nkv, hd).transpose(0, 1).repeat_interleave(nq // nkv, 0)
+        vh = v[idx].view(L, nkv, hd).transpose(0, 1).repeat_interleave(nq // nkv, 0)
         o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=c["attn_scale"])
         att[idx] = o.transpose(0, 1).reshape(L, nq * hd)
     att = r16(att)
@@ -364,7 +378,12 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16):
     act = F.gelu(g, approximate="tanh") if c["mlp"] == wl.MLP_GELU_GATED else F.silu(g)
     m = r16(act * u)
     H = H + F.rms_norm(lin(m, "w_down"), (d,), T(t["post_ff_w"]), eps)
-    return H.numpy()
+    if c.get("n_ple"):
+        P = F.rms_norm(c["ple_scale"] * (T(x0) @ T(t["ple_in"]).T), (c["n_ple"],),
+                       T(t["ple_in_norm_w"]), eps)
+        Z = F.gelu(H @ T(t["ple_gate"]).T, approximate="tanh") * P
+        H = H + F.rms_norm(Z @ T(t["ple_proj"]).T, (d,), T(t["ple_post_w"]), eps)
+    return (H * t.get("scalar", 1.0)).numpy()
 
 
 def _angles(pos, sections, hd, base):
@@ -399,6 +418,31 @@ def test_sandwich_layer_matches_torch_composition(oracle, name, kw):
         out64 = oracle.forward(w, f16_sites=False)
         ref64 = _torch_sandwich_layer(c, w.layers[0], w.x, ang, w.items, False)
         assert np.abs(out64 - ref64).max() / np.abs(ref64).max() < 1e-12
+
+
+def test_text_encoder_options_match_torch_composition(oracle):
+    """GQA (8 q / 2 kv heads), v-norm, a windowed then a global layer with their
+    own RoPE bases, layer scalars and the per-layer input, two layers deep."""
+    w = wl.make("gemma_text_ple_f32", layers=2, lengths=[9, 30, 4],
+                overrides=dict(window=6, global_every=2, n_ple=64))
+    w.cfg["final"] = wl.FINAL_NONE
+    c = w.cfg
+    assert [t["window"] for t in w.layers] == [6, 0]
+    assert w.layers[0]["rope_base"] != w.layers[1]["rope_base"]
+    pos = oracle.positions(w.rows, w.items, w.grids, 1)
+    H = w.x
+    for t in w.layers:
+        H = _torch_sandwich_layer(c, t, H, _angles(pos, 1, c["hd"], t["rope_base"]), w.items,
+                                  False, x0=w.x)
+    out = oracle.forward(w)
+    assert np.abs(out - H).max() / np.abs(H).max() < 1e-12
+    # each option changes the result (none of them is silently dropped)
+    for key, val in (("v_norm", False), ("n_ple", 0)):
+        ov = dict(window=6, global_every=2, n_ple=64)
+        ov[key] = val
+        w2 = wl.make("gemma_text_ple_f32", layers=2, lengths=[9, 30, 4], overrides=ov)
+        w2.cfg["final"] = wl.FINAL_NONE
+        assert np.abs(oracle.forward(w2) - out).max() > 1e-3 * np.abs(out).max(), key
 
 
 def test_packed_equals_separate_forward(oracle):

@@ -1,6 +1,6 @@
 """Synthetic workloads of the packed encoder forward: shapes, items and seeded tensors.
 
-Five workloads, each the shape of one of the encoders on the reference pages,
+Six workloads, each the shape of one of the encoders on the reference pages,
 with random weights (no trained checkpoint is available):
 
   vit_layer_f32        one pre-LN ViT layer: 64 tokens, d 128, 2x64 heads, MLP 512
@@ -14,6 +14,9 @@ with random weights (no trained checkpoint is available):
                        2-D RoPE over a 32x32 grid + 32 caption rows, SwiGLU 10240
   zimage_dit_cfg_8448  the same stack at a 64x64 grid + 128 caption rows as a CFG
                        batch-2 program: rows [img0|img1|cap0|cap1]
+  gemma_text_ple_f32   the text encoder's full layer spec on the gemma_text_f32 batch:
+                       8 q / 2 kv heads, v-norm, 5 windowed : 1 global layers with
+                       RoPE bases 1e4 / 1e6, layer scalars, per-layer input (256 wide)
 
 Only draws and shapes live here; the forward itself is computed by the HIP
 library (and, independently, by the oracle).
@@ -45,6 +48,17 @@ CONFIGS = {
         hd=64, ff=2048, layers=24, window=512, rope_sections=1, final=FINAL_RMS_MEANPOOL,
         eps=1e-6, attn_scale=1.0, rope_base=10000.0, x_scale=math.sqrt(512.0), biases=False,
         nseq=16, len_lo=32, len_hi=2048),
+    # the same packed batch (lengths drawn from the stream of workload 2) through
+    # the full option set of the text encoder's layer spec: GQA, v-norm, a
+    # sliding/global window pattern with one RoPE table per kind, layer scalars
+    # and the per-layer-input branch
+    "gemma_text_ple_f32": dict(
+        num=6, block=BLOCK_SANDWICH, path=PATH_F32, mlp=MLP_GELU_GATED, d=512, nq=8, nkv=2,
+        hd=64, ff=2048, layers=24, window=512, global_every=6, rope_sections=1,
+        final=FINAL_RMS_MEANPOOL, eps=1e-6, attn_scale=1.0, rope_base=10000.0,
+        rope_base_global=1000000.0, x_scale=math.sqrt(512.0), biases=False, nseq=16, len_lo=32,
+        len_hi=2048, len_stream=2, v_norm=True, layer_scalar=True, n_ple=256,
+        ple_scale=1.0 / math.sqrt(2.0)),
     "lfm2_vit_f32": dict(
         num=3, block=BLOCK_PRE_LN, path=PATH_F32, mlp=MLP_GELU, d=768, nq=12, nkv=12, hd=64,
         ff=3072, layers=16, window=0, rope_sections=0, final=FINAL_LN, eps=1e-6,
@@ -144,6 +158,24 @@ def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
             t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
         for name in ("q_norm_w", "k_norm_w"):
             t[name] = _normal(seed, f"L{li}.{name}", (hd,), 0.02, 1.0)
+    # per-layer values: every global_every-th layer attends globally (window 0)
+    # with its own RoPE base; the rest keep the config's window and base
+    ge = cfg.get("global_every", 0)
+    if ge and (li + 1) % ge == 0:
+        t["window"] = 0
+        t["rope_base"] = cfg["rope_base_global"]
+    else:
+        t["window"] = cfg["window"]
+        t["rope_base"] = cfg["rope_base"]
+    if cfg.get("layer_scalar"):
+        t["scalar"] = float(1.0 + 0.05 * synth.normal_np(synth.tensor_key(seed, f"L{li}.scalar"), 0, 1)[0])
+    if cfg.get("n_ple"):
+        np_ = cfg["n_ple"]
+        t["ple_in"] = _normal(seed, f"L{li}.ple_in", (np_, d), 0.02)
+        t["ple_gate"] = _normal(seed, f"L{li}.ple_gate", (np_, d), 0.02)
+        t["ple_proj"] = _normal(seed, f"L{li}.ple_proj", (d, np_), 0.02)
+        t["ple_in_norm_w"] = _normal(seed, "ple_in_norm_w", (np_,), 0.02, 1.0)  # model-wide
+        t["ple_post_w"] = _normal(seed, f"L{li}.ple_post_w", (d,), 0.02, 1.0)
     return t
 
 
@@ -169,7 +201,7 @@ def layout(cfg: dict, lengths=None, grid=None, ncap=None, cfg_pair=None):
         if "lengths" in cfg:
             lengths = cfg["lengths"]
         else:
-            k = synth.tensor_key(MASTER_SEED + cfg["num"], "lengths")
+            k = synth.tensor_key(MASTER_SEED + cfg.get("len_stream", cfg["num"]), "lengths")
             lengths = [int(v) for v in synth.ints_np(k, cfg["nseq"], cfg["len_lo"], cfg["len_hi"])]
     items, r = [], 0
     for n in lengths:
@@ -215,12 +247,17 @@ def gemm_flops(w: Workload) -> float:
     c = w.cfg
     d, q, kv, ff = c["d"], c["nq"] * c["hd"], c["nkv"] * c["hd"], c["ff"]
     per_row = d * (q + 2 * kv) + q * d + ff * d * (1 if c["mlp"] == MLP_GELU else 2) + ff * d
+    per_row += 3 * c.get("n_ple", 0) * d  # per-layer input: ple_in, ple_gate, ple_proj
     return 2.0 * per_row * w.rows * c["layers"]
 
 
-def visible_pairs(w: Workload) -> int:
+def layer_windows(w: Workload) -> list:
+    return [int(t.get("window", w.cfg["window"])) for t in w.layers]
+
+
+def visible_pairs(w: Workload, window=None) -> int:
     """Sum over items of the (query, key) pairs the attention mask lets through."""
-    W = w.cfg["window"]
+    W = w.cfg["window"] if window is None else window
     tot = 0
     for rr in w.items:
         L = sum(n for _, n in rr)
@@ -235,4 +272,5 @@ def visible_pairs(w: Workload) -> int:
 def attn_flops(w: Workload) -> float:
     """Algorithmic attention flops: 4*hd per visible pair per head per layer."""
     c = w.cfg
-    return 4.0 * c["hd"] * c["nq"] * visible_pairs(w) * c["layers"]
+    pairs = {W: visible_pairs(w, W) for W in set(layer_windows(w))}
+    return 4.0 * c["hd"] * c["nq"] * sum(pairs[W] for W in layer_windows(w))
