@@ -176,7 +176,10 @@ def main():
         "tokens_per_s_per_layer": round(w.rows / (ms * 1e-3 / cfg["layers"]), 1),
         "config": {"workload": args.workload, "rows": w.rows, "items": len(w.items),
                    "layers": cfg["layers"], "d": cfg["d"], "heads": f"{cfg['nq']}x{cfg['hd']}",
-                   "ff": cfg["ff"], "window": cfg["window"],
+                   "kv_heads": cfg["nkv"], "ff": cfg["ff"], "window": cfg["window"],
+                   **({"global_every": cfg["global_every"]} if cfg.get("global_every") else {}),
+                   **({"v_norm": True} if cfg.get("v_norm") else {}),
+                   **({"n_ple": cfg["n_ple"]} if cfg.get("n_ple") else {}),
                    "gemm_gflop": round(gflop / 1e9, 2), "attn_gflop": round(aflop / 1e9, 2),
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "GEMM class: gemm_kernel + gemm_gated_kernel ("

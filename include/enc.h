@@ -178,10 +178,11 @@ ENC_API size_t enc_attention_workspace_bytes(const enc_attn_desc *desc, const en
 /* One wavefront per row (or per row and head); f32 statistics.  Geometry:
  * d % 4 == 0 and d <= 4096; strides multiples of 4 (f32) or 8 (f16). */
 
-/* RMSNorm y = x * w / sqrt(mean(x^2) + eps), gain multiplying directly ([EG]
- * `Prog::rms`).  LayerNorm y = (x - mean) / sqrt(var + eps) * w + b, population
- * variance ([VE] `VitGpuOps::layernorm`; b may be NULL).  Output f32, or f16
- * with ENC_Y_F16.  rows = 0 is a no-op (the pointers may then be NULL). */
+/* RMSNorm y = rms(pre x) w = pre x w / sqrt(mean((pre x)^2) + eps), gain
+ * multiplying directly ([EG] `Prog::rms`, "Y = rms(pre·X)·w").  LayerNorm
+ * y = (x - mean) / sqrt(var + eps) * w + b, population variance ([VE]
+ * `VitGpuOps::layernorm`; b may be NULL; pre must be 0 or 1).  Output f32, or
+ * f16 with ENC_Y_F16.  rows = 0 is a no-op (the pointers may then be NULL). */
 typedef struct {
     uint32_t rows, d;
     const float *x;   /* (dev) [rows][ldx] */
@@ -192,13 +193,14 @@ typedef struct {
     void *y;          /* (dev) [rows][ldy]; may equal x for an f32 output */
     uint32_t ldy;
     uint32_t flags;   /* ENC_Y_F16 */
+    float pre;        /* RMSNorm input prescale; 0 is read as 1 */
 } enc_norm_desc;
 ENC_API enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *desc, enc_stream stream);
 ENC_API enc_status enc_layer_norm(enc_ctx *ctx, const enc_norm_desc *desc, enc_stream stream);
 
 /* Post-norm residual fused with the next pre-norm ([EG] `Prog::add_norm`
  * "H = (H + rms(T)·w)·post; then A = rms(H)·w2"; [ZI] `Enc::rowop`):
- *   h += rms(t) * w_post;   then, when w_next != NULL, a = rms(h) * w_next.
+ *   h = (h + rms(t) * w_post) * post;   then, when w_next != NULL, a = rms(h) * w_next.
  * h, t f32 [rows][d] (dense); a f32 or f16 (ENC_Y_F16) [rows][d]. */
 typedef struct {
     uint32_t rows, d;
@@ -209,6 +211,7 @@ typedef struct {
     float eps;
     void *a;              /* (dev) next block input; unused when w_next == NULL */
     uint32_t flags;       /* ENC_Y_F16 */
+    float post;           /* the layer scalar; 0 is read as 1 */
 } enc_add_norm_desc;
 ENC_API enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *desc, enc_stream stream);
 
@@ -219,7 +222,10 @@ ENC_API enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *desc, enc
  *   and i < S/2, with (c, sn) = (cos, sin)[r][s*S/2 + i]:
  *     x[sS+i] <- x[sS+i] c - x[sS+i+S/2] sn;  x[sS+i+S/2] <- x[sS+i+S/2] c + x[sS+i] sn
  * sections = 0 skips the rotation.  cos/sin: (dev) f32 [rows][hd/2], built by
- * enc_rope_table.  The panel is f32 (ENC_F32) or f16 (ENC_I8F16, math in f32). */
+ * enc_rope_table.  With v_norm, every v head (columns v_col + g*hd) is also
+ * replaced by x / sqrt(mean(x^2) + eps), without gain or rotation ([EG]
+ * `Prog::qkv`: "q/k norm + RoPE, v norm"; the prep takes no v weight).  The
+ * panel is f32 (ENC_F32) or f16 (ENC_I8F16, math in f32). */
 typedef struct {
     uint32_t path;
     void *panel;          /* (dev) [rows][ld] */
@@ -228,6 +234,7 @@ typedef struct {
     float eps;
     const float *cos, *sin;           /* (dev) [rows][hd/2] */
     uint32_t sections;                /* 0, 1 or 2 */
+    uint32_t v_col, v_norm;           /* v block column; 1 = norm the v heads too */
 } enc_qk_desc;
 ENC_API enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *desc, enc_stream stream);
 
@@ -283,15 +290,39 @@ typedef struct {
     const float *bq, *bk, *bv, *bo, *b_up, *b_down;
     const float *norm1_w, *norm1_b, *norm2_w, *norm2_b;
     const float *post_attn_w, *post_ff_w, *q_norm_w, *k_norm_w;
+    /* Options of the text encoder's layer spec ([EG] `LayerSpec`; sandwich block,
+     * zero-initialised = off):
+     *  v_norm      weightless RMS of every v head after the projection;
+     *  rope_table  which of the batch's RoPE tables the layer rotates with
+     *              ([EG] `LayerSpec.rope`: one table per RoPE kind);
+     *  scalar      the layer's last residual update is H = (H + .) * scalar
+     *              ([EG] `add_norm(.., l.scalar)`); 0 is read as 1;
+     *  n_ple       width of the per-layer-input branch ([EG] `TextGpu::forward`,
+     *              after the FFN; f32 path, multiple of 64; 0 = none):
+     *                P = rms(ple_scale * (X0 ple_in^T); ple_in_norm_w)
+     *                Z = gelu_tanh(H ple_gate^T) * P
+     *                H = (H + rms(Z ple_proj^T; ple_post_w)) * scalar
+     *              with X0 the forward's input rows (enc_batch.ple_x). */
+    uint32_t v_norm, rope_table;
+    float scalar;
+    uint32_t n_ple;
+    float ple_scale;
+    const float *ple_in, *ple_gate, *ple_proj; /* [n_ple][d], [n_ple][d], [d][n_ple] */
+    const float *ple_in_norm_w, *ple_post_w;   /* [n_ple], [d] */
 } enc_layer;
 
-/* The packed batch: `rows` rows, `nitems` disjoint items covering them, and
- * the RoPE tables (dev, f32 [rows][hd/2], NULL when no layer rotates). */
+/* The packed batch: `rows` rows, `nitems` disjoint items covering them, the
+ * RoPE tables (dev, f32 [rows][hd/2] each; a layer rotates with table
+ * rope_table; NULL where no layer uses it) and, for layers with a per-layer
+ * input, the rows X0 that branch projects (dev, f32 [rows][d]; encoder_forward
+ * takes its x when NULL, encoder_layer_forward needs it). */
+#define ENC_MAX_ROPE_TABLES 4
 typedef struct {
     uint32_t rows;
     const enc_item *items; /* (host) */
     uint32_t nitems;
-    const float *rope_cos, *rope_sin;
+    const float *rope_cos[ENC_MAX_ROPE_TABLES], *rope_sin[ENC_MAX_ROPE_TABLES];
+    const float *ple_x;
 } enc_batch;
 
 /* All layers share d, path and block kind.  final: NONE -> out = H [rows][d];

@@ -153,12 +153,15 @@ def run(w, x=None, layers=None):
     return out
 
 
-def test_text_encoder_full_batch_shortest_sequences():
+@pytest.mark.parametrize("name", ["gemma_text_f32", "gemma_text_ple_f32"])
+def test_text_encoder_full_batch_shortest_sequences(name):
     """The benchmark batch (16 sequences, 16 057 rows, 24 layers, pooled output):
     the pooled rows of the three shortest sequences against the oracle run on
     each sequence alone (packed == separate is pinned in the oracle), and the GPU
-    packed result against the GPU run of each sequence alone, bit for bit."""
-    w = wl.make("gemma_text_f32")
+    packed result against the GPU run of each sequence alone, bit for bit.  Also
+    with every text-encoder option on (GQA, v-norm, window pattern, two RoPE
+    tables, layer scalars, per-layer input)."""
+    w = wl.make(name)
     say(f"full text encoder: rows {w.rows}, layers {w.cfg['layers']}")
     pooled = host(run(w))
     assert np.isfinite(pooled).all()

@@ -46,6 +46,10 @@ CASES = [
     ("zimage_dit_1056", dict(layers=2, grid=8, ncap=8, overrides=DIT_SMALL)),
     ("zimage_dit_1056", dict(layers=1, grid=4, ncap=4)),
     ("zimage_dit_cfg_8448", dict(layers=2, grid=6, ncap=5, overrides=DIT_SMALL)),
+    # GQA 8:2, v-norm, windowed / global layers with their own RoPE tables, layer
+    # scalars, per-layer input
+    ("gemma_text_ple_f32", dict(layers=3, lengths=[600, 37, 1100, 5, 130],
+                                overrides=dict(global_every=2))),
 ]
 
 
@@ -68,6 +72,7 @@ def test_forward_vs_oracle(name, kw):
     ("gemma_text_f32", dict(layers=3, lengths=[300, 77, 700])),
     ("lfm2_vit_f32", dict(layers=2, overrides=dict(), lengths=[200])),
     ("zimage_dit_cfg_8448", dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)),
+    ("gemma_text_ple_f32", dict(layers=3, lengths=[300, 77, 700], overrides=dict(global_every=2))),
 ])
 def test_fused_chain_equals_layer_by_layer(name, kw):
     """encoder_forward (each layer's last row op writes the next pre-norm) gives
@@ -78,6 +83,8 @@ def test_fused_chain_equals_layer_by_layer(name, kw):
     dm = M.DeviceModel(w, DEV)
     db = M.DeviceBatch(w, DEV)
     h = torch.from_numpy(w.x.copy()).to(DEV)
+    x0 = torch.from_numpy(w.x.copy()).to(DEV)
+    db.batch.ple_x = x0.data_ptr()  # the rows the per-layer inputs project
     ws = dm.workspace(db, DEV)
     for li in range(w.cfg["layers"]):
         M.encoder_layer_forward(dm, li, db, h, ws)
@@ -85,13 +92,15 @@ def test_fused_chain_equals_layer_by_layer(name, kw):
     assert torch.equal(fused, h)
 
 
-def test_packed_equals_separate_stack():
+@pytest.mark.parametrize("name", ["gemma_text_f32", "gemma_text_ple_f32"])
+def test_packed_equals_separate_stack(name):
     lengths = [513, 40, 1030]
-    w = wl.make("gemma_text_f32", layers=2, lengths=lengths)
+    kw = dict(overrides=dict(global_every=2)) if name == "gemma_text_ple_f32" else {}
+    w = wl.make(name, layers=2, lengths=lengths, **kw)
     packed = run(w)
     r = 0
     for i, n in enumerate(lengths):
-        ws_ = wl.make("gemma_text_f32", layers=2, lengths=[n])
+        ws_ = wl.make(name, layers=2, lengths=[n], **kw)
         alone = run(ws_, x=w.x[r:r + n])
         assert torch.equal(alone[0], packed[i]), f"sequence {i}"
         r += n

@@ -451,6 +451,58 @@ def test_qk_norm_rope(hd, sections, f16):
     assert np.array_equal(got[:, (nq + nkv) * hd:], pp[:, (nq + nkv) * hd:])  # v untouched
 
 
+def test_rms_norm_prescale_and_add_norm_scalar():
+    """rms(pre x) w (the per-layer input's norm) and h = (h + rms(t) w) post (the
+    layer scalar) against the oracle's norms; pre = post = 1 is bit-identical to
+    the plain calls."""
+    rng = np.random.default_rng(5)
+    n, d = 300, 512
+    x = rng.normal(0, 3, (n, d)).astype(np.float32)
+    w = (1 + 0.02 * rng.normal(0, 1, d)).astype(np.float32)
+    y = torch.empty((n, d), dtype=torch.float32, device=DEV)
+    B.rms_norm(to_dev(x), to_dev(w), 1e-6, y, pre=0.7071)
+    ref = O.rms_norm(x.astype(np.float64) * np.float64(np.float32(0.7071)), w, 1e-6)
+    assert row_rel_err(host(y), ref) <= TOL_F32
+    y1 = torch.empty_like(y)
+    B.rms_norm(to_dev(x), to_dev(w), 1e-6, y1, pre=1.0)
+    y0 = torch.empty_like(y)
+    B.rms_norm(to_dev(x), to_dev(w), 1e-6, y0)
+    assert torch.equal(y1, y0)
+    h = rng.normal(0, 20, (n, d)).astype(np.float32)
+    t = rng.normal(0, 1, (n, d)).astype(np.float32)
+    H = to_dev(h)
+    B.add_norm(H, to_dev(t), to_dev(w), 1e-6, post=0.93)
+    ref = (h.astype(np.float64) + O.rms_norm(t, w, 1e-6)) * np.float64(np.float32(0.93))
+    assert row_rel_err(host(H), ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("hd,f16", [(64, False), (128, True)])
+def test_qk_norm_rope_with_v_norm(hd, f16):
+    """With v_norm the v heads are RMS-normed without gain and not rotated; q and
+    k get exactly the bits they get without it."""
+    rng = np.random.default_rng(hd)
+    rows, nq, nkv = 200, 8, 2
+    ld = (nq + 2 * nkv) * hd
+    p = rng.normal(0, 2, (rows, ld)).astype(np.float16 if f16 else np.float32)
+    qw = (1 + 0.02 * rng.normal(0, 1, hd)).astype(np.float32)
+    kw = (1 + 0.02 * rng.normal(0, 1, hd)).astype(np.float32)
+    pos = O.positions(rows, [[(0, rows)]], [0], 1)
+    th = pos.astype(np.float64) * 10000.0 ** (-2.0 * np.arange(hd // 2) / hd)
+    cos, sin = to_dev(np.cos(th).astype(np.float32)), to_dev(np.sin(th).astype(np.float32))
+    path = B.ENC_I8F16 if f16 else B.ENC_F32
+    P1, P2 = to_dev(p), to_dev(p)
+    B.qk_norm_rope(P1, nq, nkv, hd, to_dev(qw), to_dev(kw), 1e-6, cos, sin, 1, path=path, v_norm=True)
+    B.qk_norm_rope(P2, nq, nkv, hd, to_dev(qw), to_dev(kw), 1e-6, cos, sin, 1, path=path)
+    vc = (nq + nkv) * hd
+    assert torch.equal(P1[:, :vc], P2[:, :vc])
+    assert torch.equal(P2[:, vc:], to_dev(p)[:, vc:])  # untouched without v_norm
+    v = p[:, vc:].astype(np.float64).reshape(rows * nkv, hd)
+    ref = O.rms_norm(v, None, 1e-6).reshape(rows, nkv * hd)
+    if f16:
+        ref = np.vectorize(O.round_f16)(ref)
+    assert row_rel_err(host(P1)[:, vc:], ref) <= (TOL_I8F16 if f16 else TOL_F32)
+
+
 @pytest.mark.parametrize("kind,f16", [(B.ENC_ACT_GELU_TANH_GATED, False), (B.ENC_ACT_SWIGLU, True),
                                       (B.ENC_ACT_SWIGLU, False)])
 def test_gated_act(kind, f16):

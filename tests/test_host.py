@@ -132,6 +132,14 @@ def _fake_model(name, **kw):
             if key in w.layers[li] or (w.cfg["path"] == 1 and key in wl.weight_shapes(w.cfg)):
                 setattr(L, n, p)
                 p += 0x100000
+        L.window = int(w.layers[li].get("window", w.cfg["window"]))
+        L.v_norm = 1 if w.cfg.get("v_norm") else 0
+        L.scalar = float(w.layers[li].get("scalar", 0.0))
+        L.n_ple, L.ple_scale = int(w.cfg.get("n_ple", 0)), float(w.cfg.get("ple_scale", 1.0))
+        if L.n_ple:
+            for n in B._LAYER_PLE_PTRS:
+                setattr(L, n, p)
+                p += 0x100000
     m = B.Model()
     m.nlayers, m.layers, m.final_kind = 2, layers, w.cfg["final"]
     m.final_w = 0x7000000 if w.final_w is not None else None
@@ -139,7 +147,7 @@ def _fake_model(name, **kw):
     items = B.make_items(w.items)
     b = B.Batch()
     b.rows, b.items, b.nitems = w.rows, items, len(w.items)
-    b.rope_cos = b.rope_sin = 0x8000000 if w.cfg["rope_sections"] else None
+    b.rope_cos[0] = b.rope_sin[0] = 0x8000000 if w.cfg["rope_sections"] else None
     return w, m, b, (layers, items)
 
 
@@ -158,9 +166,9 @@ def test_check_model_rejects():
     b.rows = 13  # items cover 12
     assert B.check_model(m, b)[0] == B.ENC_ESHAPE
     b.rows = 12
-    b.rope_cos = None
+    b.rope_cos[0] = None
     assert B.check_model(m, b)[0] == B.ENC_EINVAL
-    b.rope_cos = 0x8000000
+    b.rope_cos[0] = 0x8000000
     m.layers[1].hd = 96
     assert B.check_model(m, b)[0] == B.ENC_EUNSUPPORTED
     m.layers[1].hd = 64
@@ -169,6 +177,37 @@ def test_check_model_rejects():
     m.layers[1].d = 512
     m.layers[0].q_norm_w = None
     assert B.check_model(m, b)[0] == B.ENC_EINVAL
+
+
+def test_check_model_text_encoder_options():
+    w, m, b, keep = _fake_model("gemma_text_ple_f32", lengths=[5, 7])
+    st, msg = B.check_model(m, b)
+    assert st == B.ENC_OK, msg
+    base = B.lib().enc_workspace_bytes(C.byref(m), C.byref(b))
+    # the branch's two [rows][n_ple] f32 buffers
+    assert base >= 2 * 12 * 256 * 4
+    L = m.layers[1]
+    L.rope_table = 1                      # no second table in the batch
+    assert B.check_model(m, b)[0] == B.ENC_EINVAL
+    b.rope_cos[1] = b.rope_sin[1] = 0x9000000
+    assert B.check_model(m, b)[0] == B.ENC_OK
+    L.rope_table = B.MAX_ROPE_TABLES
+    assert B.check_model(m, b)[0] == B.ENC_EINVAL
+    L.rope_table = 0
+    L.n_ple = 96                          # not a multiple of 64
+    assert B.check_model(m, b)[0] == B.ENC_EUNSUPPORTED
+    L.n_ple = 256
+    L.ple_gate = None
+    assert B.check_model(m, b)[0] == B.ENC_EINVAL
+    L.ple_gate = 0x6000000
+    L.scalar = float("nan")
+    assert B.check_model(m, b)[0] == B.ENC_EINVAL
+    L.scalar = 1.0
+    L.path = m.layers[0].path = 1         # per-layer input on the int8 path
+    assert B.check_model(m, b)[0] != B.ENC_OK
+    w2, m2, b2, keep2 = _fake_model("vit_layer_f32")
+    m2.layers[0].v_norm = 1               # a sandwich option on a pre-LN layer
+    assert B.check_model(m2, b2)[0] == B.ENC_EUNSUPPORTED
 
 
 def test_workspace_grows_with_rows():

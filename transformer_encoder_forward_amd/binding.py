@@ -73,13 +73,13 @@ class AttnDesc(C.Structure):
 class NormDesc(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("d", C.c_uint32), ("x", C.c_void_p), ("ldx", C.c_uint32),
                 ("w", C.c_void_p), ("b", C.c_void_p), ("eps", C.c_float), ("y", C.c_void_p),
-                ("ldy", C.c_uint32), ("flags", C.c_uint32)]
+                ("ldy", C.c_uint32), ("flags", C.c_uint32), ("pre", C.c_float)]
 
 
 class AddNormDesc(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("d", C.c_uint32), ("h", C.c_void_p), ("t", C.c_void_p),
                 ("w_post", C.c_void_p), ("w_next", C.c_void_p), ("eps", C.c_float),
-                ("a", C.c_void_p), ("flags", C.c_uint32)]
+                ("a", C.c_void_p), ("flags", C.c_uint32), ("post", C.c_float)]
 
 
 class QkDesc(C.Structure):
@@ -87,7 +87,8 @@ class QkDesc(C.Structure):
                 ("ld", C.c_uint32), ("q_col", C.c_uint32), ("k_col", C.c_uint32),
                 ("nq", C.c_uint32), ("nkv", C.c_uint32), ("hd", C.c_uint32),
                 ("q_norm_w", C.c_void_p), ("k_norm_w", C.c_void_p), ("eps", C.c_float),
-                ("cos", C.c_void_p), ("sin", C.c_void_p), ("sections", C.c_uint32)]
+                ("cos", C.c_void_p), ("sin", C.c_void_p), ("sections", C.c_uint32),
+                ("v_col", C.c_uint32), ("v_norm", C.c_uint32)]
 
 
 class ActDesc(C.Structure):
@@ -104,10 +105,16 @@ _LAYER_PTRS = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
                "post_attn_w", "post_ff_w", "q_norm_w", "k_norm_w"]
 
 
+_LAYER_PLE_PTRS = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
+
+
 class Layer(C.Structure):
     _fields_ = ([(n, C.c_uint32) for n in _LAYER_U32]
                 + [("eps", C.c_float), ("attn_scale", C.c_float)]
-                + [(n, C.c_void_p) for n in _LAYER_PTRS])
+                + [(n, C.c_void_p) for n in _LAYER_PTRS]
+                + [("v_norm", C.c_uint32), ("rope_table", C.c_uint32), ("scalar", C.c_float),
+                   ("n_ple", C.c_uint32), ("ple_scale", C.c_float)]
+                + [(n, C.c_void_p) for n in _LAYER_PLE_PTRS])
 
 
 class ProfStat(C.Structure):
@@ -115,9 +122,13 @@ class ProfStat(C.Structure):
                 ("bytes", C.c_double)]
 
 
+MAX_ROPE_TABLES = 4
+
+
 class Batch(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("items", C.POINTER(Item)), ("nitems", C.c_uint32),
-                ("rope_cos", C.c_void_p), ("rope_sin", C.c_void_p)]
+                ("rope_cos", C.c_void_p * MAX_ROPE_TABLES), ("rope_sin", C.c_void_p * MAX_ROPE_TABLES),
+                ("ple_x", C.c_void_p)]
 
 
 class Model(C.Structure):
@@ -300,9 +311,10 @@ def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_co
     ctx.check(lib().attention_items(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
 
 
-def _norm(fn, x, w, b, eps, y, f16, ctx, stream):
+def _norm(fn, x, w, b, eps, y, f16, ctx, stream, pre=1.0):
     ctx = ctx or context()
     d = NormDesc()
+    d.pre = pre
     d.rows, d.d = x.shape[0], x.shape[1]
     d.x, d.ldx = _ptr(x), x.stride(0)
     d.w, d.b = _ptr(w), _ptr(b)
@@ -312,17 +324,18 @@ def _norm(fn, x, w, b, eps, y, f16, ctx, stream):
     ctx.check(fn(ctx.h, C.byref(d), _stream(stream)))
 
 
-def rms_norm(x, w, eps, y, f16=False, ctx=None, stream=None):
-    _norm(lib().enc_rms_norm, x, w, None, eps, y, f16, ctx, stream)
+def rms_norm(x, w, eps, y, f16=False, pre=1.0, ctx=None, stream=None):
+    _norm(lib().enc_rms_norm, x, w, None, eps, y, f16, ctx, stream, pre)
 
 
 def layer_norm(x, w, b, eps, y, f16=False, ctx=None, stream=None):
     _norm(lib().enc_layer_norm, x, w, b, eps, y, f16, ctx, stream)
 
 
-def add_norm(h, t, w_post, eps, w_next=None, a=None, f16=False, ctx=None, stream=None):
+def add_norm(h, t, w_post, eps, w_next=None, a=None, f16=False, post=1.0, ctx=None, stream=None):
     ctx = ctx or context()
     d = AddNormDesc()
+    d.post = post
     d.rows, d.d = h.shape[0], h.shape[1]
     d.h, d.t, d.w_post, d.w_next, d.a = _ptr(h), _ptr(t), _ptr(w_post), _ptr(w_next), _ptr(a)
     d.eps = eps
@@ -331,7 +344,7 @@ def add_norm(h, t, w_post, eps, w_next=None, a=None, f16=False, ctx=None, stream
 
 
 def qk_norm_rope(panel, nq, nkv, hd, q_norm_w, k_norm_w, eps, cos, sin, sections, q_col=0,
-                 k_col=None, path=ENC_F32, ctx=None, stream=None):
+                 k_col=None, path=ENC_F32, v_col=None, v_norm=False, ctx=None, stream=None):
     ctx = ctx or context()
     d = QkDesc()
     d.path = path
@@ -344,6 +357,8 @@ def qk_norm_rope(panel, nq, nkv, hd, q_norm_w, k_norm_w, eps, cos, sin, sections
     d.eps = eps
     d.cos, d.sin = _ptr(cos), _ptr(sin)
     d.sections = sections
+    d.v_col = v_col if v_col is not None else d.k_col + nkv * hd
+    d.v_norm = 1 if v_norm else 0
     ctx.check(lib().enc_qk_norm_rope(ctx.h, C.byref(d), _stream(stream)))
 
 

@@ -436,6 +436,7 @@ enc_status check_norm(Err &e, const char *who, const enc_norm_desc *d) {
     if (d->ldx % 4 || d->ldy % 4 || !aligned(d->x, 16) || !aligned(d->y, 16) || !aligned(d->w, 16) ||
         (d->b && !aligned(d->b, 16)))
         return e.set(ENC_EUNSUPPORTED, "%s: pointers 16-byte aligned, strides multiples of 4", who);
+    if (!std::isfinite(d->pre)) return e.set(ENC_EINVAL, "%s: pre is not finite", who);
     return ENC_OK;
 }
 
@@ -449,6 +450,7 @@ enc_status check_add_norm(Err &e, const enc_add_norm_desc *d) {
     if (!aligned(d->h, 16) || !aligned(d->t, 16) || !aligned(d->w_post, 16) ||
         (d->w_next && (!aligned(d->w_next, 16) || !aligned(d->a, 16))))
         return e.set(ENC_EUNSUPPORTED, "enc_add_norm: pointers must be 16-byte aligned");
+    if (!std::isfinite(d->post)) return e.set(ENC_EINVAL, "enc_add_norm: post is not finite");
     return ENC_OK;
 }
 
@@ -461,8 +463,13 @@ enc_status check_qk(Err &e, const enc_qk_desc *d) {
         return e.set(ENC_EUNSUPPORTED, "enc_qk_norm_rope: head dim %u (64 or 128)", d->hd);
     if (d->sections > 2) return e.set(ENC_EINVAL, "enc_qk_norm_rope: sections %u", d->sections);
     if (d->sections && (!d->cos || !d->sin)) return e.set(ENC_EINVAL, "enc_qk_norm_rope: null cos/sin");
-    if (d->q_col + d->nq * d->hd > d->ld || d->k_col + d->nkv * d->hd > d->ld)
+    if (d->q_col + d->nq * d->hd > d->ld || d->k_col + d->nkv * d->hd > d->ld ||
+        (d->v_norm && d->v_col + d->nkv * d->hd > d->ld))
         return e.set(ENC_ESHAPE, "enc_qk_norm_rope: heads do not fit the panel width");
+    if (d->v_norm > 1) return e.set(ENC_EINVAL, "enc_qk_norm_rope: v_norm %u", d->v_norm);
+    if (d->ld % 8 || d->q_col % 8 || d->k_col % 8 || d->v_col % 8 || !aligned(d->panel, 16))
+        return e.set(ENC_EUNSUPPORTED,
+                     "enc_qk_norm_rope: panel 16-byte aligned, stride and columns multiples of 8");
     if ((uint64_t)d->rows * (d->nq + d->nkv) >= (1ull << 32) / 4)
         return e.set(ENC_ESHAPE, "enc_qk_norm_rope: too many rows");
     return ENC_OK;
@@ -536,7 +543,7 @@ hipError_t pool_items(const enc_item *items, uint32_t nitems, uint32_t rows, uin
 }
 
 struct WsPlan {
-    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, total = 0;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, pin = 0, z = 0, total = 0;
     size_t part_bytes = 0;
 };
 
@@ -562,7 +569,7 @@ enc_attn_desc layer_attn_desc(const enc_layer &L, uint32_t rows) {
 WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
     WsPlan p;
     const uint32_t rows = B->rows;
-    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, ple = 0;
     for (uint32_t l = 0; l < M->nlayers; l++) {
         const enc_layer &L = M->layers[l];
         const size_t esz = L.path == ENC_I8F16 ? 2 : 4;
@@ -574,6 +581,7 @@ WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
         part = std::max(part, attn_ws_bytes(&ad, B->items, B->nitems));
         m = std::max(m, (size_t)rows * L.ff * (L.mlp == ENC_MLP_GELU_TANH ? 4 : esz));
         h = std::max(h, (size_t)rows * L.d * 4);
+        ple = std::max(ple, (size_t)rows * L.n_ple * 4);
     }
     size_t off = 0;
     p.a = off; off += up256(a);
@@ -584,6 +592,8 @@ WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
     p.part_bytes = up256(part);
     p.m = off; off += up256(m);
     p.h = off; off += up256(h);  // residual stream (out holds it when final is NONE)
+    p.pin = off; off += up256(ple);  // per-layer input: normed projection of X0
+    p.z = off; off += up256(ple);    // and its gate
     p.total = off;
     return p;
 }
@@ -613,7 +623,21 @@ enc_status check_layer(Err &e, uint32_t l, const enc_layer &L, const enc_layer &
             return e.set(ENC_EINVAL, "layer %u: sandwich block needs post/q/k norm weights", l);
         if (L.mlp == ENC_MLP_GELU_TANH)
             return e.set(ENC_EUNSUPPORTED, "layer %u: sandwich block takes a gated MLP", l);
+        if (L.v_norm > 1) return e.set(ENC_EINVAL, "layer %u: v_norm %u", l, L.v_norm);
+        if (L.rope_table >= ENC_MAX_ROPE_TABLES)
+            return e.set(ENC_EINVAL, "layer %u: rope_table %u", l, L.rope_table);
+        if (!std::isfinite(L.scalar)) return e.set(ENC_EINVAL, "layer %u: scalar not finite", l);
+        if (L.n_ple) {
+            if (L.path != ENC_F32)
+                return e.set(ENC_EUNSUPPORTED, "layer %u: the per-layer input runs the f32 path", l);
+            if (L.n_ple % 64) return e.set(ENC_EUNSUPPORTED, "layer %u: n_ple %u (multiple of 64)", l, L.n_ple);
+            if (!L.ple_in || !L.ple_gate || !L.ple_proj || !L.ple_in_norm_w || !L.ple_post_w)
+                return e.set(ENC_EINVAL, "layer %u: per-layer input needs its weights", l);
+            if (!std::isfinite(L.ple_scale)) return e.set(ENC_EINVAL, "layer %u: ple_scale not finite", l);
+        }
     } else {
+        if (L.v_norm || L.n_ple || (L.scalar != 0.0f && L.scalar != 1.0f) || L.rope_table)
+            return e.set(ENC_EUNSUPPORTED, "layer %u: v-norm, per-layer input and scalar are sandwich options", l);
         if (L.path == ENC_I8F16) return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block runs the f32 path", l);
         if (L.mlp != ENC_MLP_GELU_TANH)
             return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block takes the GELU MLP", l);
@@ -641,9 +665,11 @@ enc_status check_model(Err &e, const enc_model *M, const enc_batch *B) {
         for (uint32_t i = 0; i < B->nitems; i++)
             if (!item_len(B->items[i]))
                 return e.set(ENC_EINVAL, "item %u is empty: its mean pool is undefined", i);
-    bool rope = false;
-    for (uint32_t l = 0; l < M->nlayers; l++) rope |= M->layers[l].rope_sections != 0;
-    if (rope && (!B->rope_cos || !B->rope_sin)) return e.set(ENC_EINVAL, "RoPE layers need cos/sin tables");
+    for (uint32_t l = 0; l < M->nlayers; l++) {
+        const enc_layer &L = M->layers[l];
+        if (L.rope_sections && (!B->rope_cos[L.rope_table] || !B->rope_sin[L.rope_table]))
+            return e.set(ENC_EINVAL, "layer %u: RoPE table %u missing", l, L.rope_table);
+    }
     return ENC_OK;
 }
 
@@ -653,13 +679,13 @@ struct Bufs {
     void *part;
     size_t part_bytes;
     void *m;
-    float *h;
+    float *h, *pin, *z;
 };
 
 Bufs carve(void *ws, const WsPlan &p) {
     char *b = (char *)ws;
     return Bufs{b + p.a, b + p.panel, b + p.att, (float *)(b + p.t), p.part_bytes ? b + p.part : nullptr,
-                p.part_bytes, b + p.m, (float *)(b + p.h)};
+                p.part_bytes, b + p.m, (float *)(b + p.h), (float *)(b + p.pin), (float *)(b + p.z)};
 }
 
 #define TRY(expr)                                                                               \
@@ -674,10 +700,42 @@ hipError_t pre_norm(const enc_layer &L, uint32_t rows, const float *h, void *a, 
     return L.block == ENC_SANDWICH_RMS ? rows_rms(n, f16, s) : rows_ln(n, f16, s);
 }
 
+// The final RMS of a sandwich f32 stack is the last row op's next-norm output
+// (same eps), as the pages fuse it.
+bool fused_final(const enc_model *M) {
+    const enc_layer &L0 = M->layers[0], &Ll = M->layers[M->nlayers - 1];
+    return M->final_kind == ENC_FINAL_RMS_MEANPOOL && L0.block == ENC_SANDWICH_RMS && L0.path == ENC_F32 &&
+           M->final_eps == Ll.eps;
+}
+
+// Per-layer input of a text layer, up to its projection T = Z ple_proj^T:
+// P = rms(ple_scale * X0 ple_in^T; ple_in_norm), Z = gelu_tanh(H ple_gate^T) * P.
+hipError_t run_ple(const enc_layer &L, uint32_t rows, const float *x0, const float *h, const Bufs &b,
+                   hipStream_t s) {
+    const uint32_t d = L.d, np = L.n_ple;
+    auto proj = [&](const float *x, uint32_t k, const float *w, uint32_t m, float *y) {
+        enc_gemm_desc g{};
+        g.path = ENC_F32;
+        g.x = x;
+        g.y = y;
+        g.w[0] = w;
+        g.alpha = 1.0f;
+        enc_gemm_item it{rows, m, k, k, m, 0, 0, 0};
+        return run_gemm(&g, &it, 1, s);
+    };
+    TRY(proj(x0, d, L.ple_in, np, b.pin));
+    NormArgs n{rows, np, np, np, b.pin, L.ple_in_norm_w, nullptr, L.eps, b.pin, L.ple_scale};
+    TRY(rows_rms(n, false, s));
+    TRY(proj(h, d, L.ple_gate, np, b.z));
+    ActArgs act{ENC_ACT_GELU_TANH_GATED, rows, np, np, np, np, b.z, b.pin, b.z};
+    TRY(rows_act(act, false, s));
+    return proj(b.z, np, L.ple_proj, d, b.t);
+}
+
 // One layer on h.  On entry, for the sandwich block, A holds rms(h; norm1)
 // (pre-LN computes its own LN).  On exit the last row op has written
 // A = rms(h; w_next) when w_next != NULL (sandwich only).
-hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Bufs &b,
+hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, float *h, const Bufs &b,
                      const float *w_next, hipStream_t s) {
     const uint32_t rows = B->rows, d = L.d, hd = L.hd;
     const uint32_t qw = L.nq * hd, kw = L.nkv * hd, ld = qw + 2 * kw;
@@ -703,7 +761,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
     }
     if (sandwich) {
         QkArgs q{b.panel, rows, ld, 0, qw, L.nq, L.nkv, hd, L.rope_sections, L.q_norm_w, L.k_norm_w,
-                 L.eps, B->rope_cos, B->rope_sin};
+                 L.eps, B->rope_cos[L.rope_table], B->rope_sin[L.rope_table], qw + kw, L.v_norm};
         TRY(rows_qk(q, i8, s));
     }
     {
@@ -776,8 +834,17 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, float *h, const Buf
         TRY(run_gemm(&g, &it, 1, s));
     }
     if (sandwich) {
-        AddNormArgs an{rows, d, h, b.t, L.post_ff_w, w_next, L.eps, b.a};
-        TRY(rows_add_norm(an, i8, s));
+        const float scalar = L.scalar == 0.0f ? 1.0f : L.scalar;
+        if (!L.n_ple) {
+            AddNormArgs an{rows, d, h, b.t, L.post_ff_w, w_next, L.eps, b.a, scalar};
+            TRY(rows_add_norm(an, i8, s));
+        } else {
+            AddNormArgs an{rows, d, h, b.t, L.post_ff_w, nullptr, L.eps, nullptr, 1.0f};
+            TRY(rows_add_norm(an, false, s));
+            TRY(run_ple(L, rows, x0, h, b, s));
+            AddNormArgs pn{rows, d, h, b.t, L.ple_post_w, w_next, L.eps, b.a, scalar};
+            TRY(rows_add_norm(pn, false, s));
+        }
     }
     return hipSuccess;
 }
@@ -897,7 +964,8 @@ enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *d, enc_stream stream)
     if (!ctx) return ENC_EINVAL;
     CtxScope cs(ctx);
     if (check_norm(e, "enc_rms_norm", d) == ENC_OK) {
-        NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, nullptr, d->eps, d->y};
+        NormArgs n{d->rows, d->d, d->ldx, d->ldy, d->x, d->w, nullptr, d->eps, d->y,
+                   d->pre == 0.0f ? 1.0f : d->pre};
         launch_status(e, rows_rms(n, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_rms_norm");
     }
     return finish(ctx, e);
@@ -919,7 +987,8 @@ enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *d, enc_stream str
     if (!ctx) return ENC_EINVAL;
     CtxScope cs(ctx);
     if (check_add_norm(e, d) == ENC_OK) {
-        AddNormArgs a{d->rows, d->d, d->h, d->t, d->w_post, d->w_next, d->eps, d->a};
+        AddNormArgs a{d->rows, d->d, d->h, d->t, d->w_post, d->w_next, d->eps, d->a,
+                      d->post == 0.0f ? 1.0f : d->post};
         launch_status(e, rows_add_norm(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_add_norm");
     }
     return finish(ctx, e);
@@ -931,7 +1000,7 @@ enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *d, enc_stream strea
     CtxScope cs(ctx);
     if (check_qk(e, d) == ENC_OK) {
         QkArgs q{d->panel, d->rows, d->ld, d->q_col, d->k_col, d->nq, d->nkv, d->hd, d->sections,
-                 d->q_norm_w, d->k_norm_w, d->eps, d->cos, d->sin};
+                 d->q_norm_w, d->k_norm_w, d->eps, d->cos, d->sin, d->v_col, d->v_norm ? 1u : 0u};
         launch_status(e, rows_qk(q, d->path == ENC_I8F16, (hipStream_t)stream), "enc_qk_norm_rope");
     }
     return finish(ctx, e);
@@ -1003,6 +1072,10 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
     }
     enc_model M{1, layer, ENC_FINAL_NONE, nullptr, nullptr, 0.0f};
     if (check_model(e, &M, batch) != ENC_OK) return finish(ctx, e);
+    if (layer->n_ple && (!batch->ple_x || batch->ple_x == h)) {
+        e.set(ENC_EINVAL, "encoder_layer_forward: the per-layer input needs batch ple_x (not h)");
+        return finish(ctx, e);
+    }
     const WsPlan p = plan_ws(&M, batch);
     if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(h, 16)) {
         e.set(ENC_EINVAL, "encoder_layer_forward: workspace needs %zu bytes, 256-byte aligned",
@@ -1013,7 +1086,7 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
     hipStream_t s = (hipStream_t)stream;
     hipError_t hr = hipSuccess;
     if (layer->block == ENC_SANDWICH_RMS) hr = pre_norm(*layer, batch->rows, h, b.a, s);
-    if (hr == hipSuccess) hr = run_layer(*layer, batch, h, b, nullptr, s);
+    if (hr == hipSuccess) hr = run_layer(*layer, batch, batch->ple_x, h, b, nullptr, s);
     launch_status(e, hr, "encoder_layer_forward");
     return finish(ctx, e);
 }
@@ -1042,6 +1115,13 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
     const Bufs b = carve(ws, p);
     hipStream_t s = (hipStream_t)stream;
     float *h = model->final_kind == ENC_FINAL_NONE ? out : b.h;
+    const float *x0 = batch->ple_x ? batch->ple_x : x;  // rows the per-layer inputs project
+    bool ple = false;
+    for (uint32_t l = 0; l < model->nlayers; l++) ple |= model->layers[l].n_ple != 0;
+    if (ple && x0 == h) {
+        e.set(ENC_EINVAL, "encoder_forward: the per-layer input reads x in every layer; out must not alias it");
+        return finish(ctx, e);
+    }
     hipError_t hr = hipSuccess;
     if (h != x) hr = hipMemcpyAsync(h, x, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s);
     if (hr == hipSuccess && L0.block == ENC_SANDWICH_RMS) hr = pre_norm(L0, rows, h, b.a, s);
@@ -1049,17 +1129,17 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
         const float *w_next = nullptr;
         if (l + 1 < model->nlayers)
             w_next = model->layers[l + 1].norm1_w;
-        else if (model->final_kind == ENC_FINAL_RMS_MEANPOOL && L0.block == ENC_SANDWICH_RMS &&
-                 L0.path == ENC_F32)
+        else if (fused_final(model))
             w_next = model->final_w;  // the final RMS (f32) written by the last row op
-        hr = run_layer(model->layers[l], batch, h, b, L0.block == ENC_SANDWICH_RMS ? w_next : nullptr, s);
+        hr = run_layer(model->layers[l], batch, x0, h, b, L0.block == ENC_SANDWICH_RMS ? w_next : nullptr,
+                       s);
     }
     if (hr == hipSuccess && model->final_kind == ENC_FINAL_LN) {
         NormArgs n{rows, d, d, d, h, model->final_w, model->final_b, model->final_eps, out};
         hr = rows_ln(n, false, s);
     } else if (hr == hipSuccess && model->final_kind == ENC_FINAL_RMS_MEANPOOL) {
         float *a = (float *)b.t;  // f32 rows of rms(H; final_w)
-        if (L0.block == ENC_SANDWICH_RMS && L0.path == ENC_F32) {
+        if (fused_final(model)) {
             a = (float *)b.a;
         } else {
             NormArgs n{rows, d, d, d, h, model->final_w, nullptr, model->final_eps, a};

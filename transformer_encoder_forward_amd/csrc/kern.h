@@ -67,6 +67,7 @@ struct NormArgs {
     const float *b;
     float eps;
     void *y;
+    float pre = 1.0f;  // RMSNorm of pre * x (1 = plain)
 };
 
 struct AddNormArgs {
@@ -77,6 +78,7 @@ struct AddNormArgs {
     const float *w_next;
     float eps;
     void *a;
+    float post = 1.0f;  // h = (h + rms(t) w_post) * post
 };
 
 struct QkArgs {
@@ -85,6 +87,7 @@ struct QkArgs {
     const float *qw, *kw;
     float eps;
     const float *cos, *sin;
+    uint32_t v_col = 0, v_norm = 0;  // v_norm: weightless RMS of the nkv v heads too
 };
 
 struct ActArgs {

@@ -89,6 +89,8 @@ __global__ __launch_bounds__(256) void rms_norm_kernel(NormArgs a) {
     if (row >= (int)a.rows) return;
     Row<NV> r;
     load_row(r, a.x + (size_t)row * a.ldx, a.d, lane);
+#pragma unroll
+    for (int i = 0; i < NV; i++) r.v[i] *= a.pre;  // exact when pre == 1
     const float inv = rms_inv(r, a.d, a.eps);
     Row<NV> y = rms_apply(r, inv, a.w, a.d, lane);
     if (F16)
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
     const float inv_t = rms_inv(t, a.d, a.eps);
     const Row<NV> tn = rms_apply(t, inv_t, a.w_post, a.d, lane);
 #pragma unroll
-    for (int i = 0; i < NV; i++) h.v[i] += tn.v[i];
+    for (int i = 0; i < NV; i++) h.v[i] = (h.v[i] + tn.v[i]) * a.post;  // exact when post == 1
     store_row(h, a.h + off, false, a.d, lane);
     if (a.w_next) {
         const float inv_h = rms_inv(h, a.d, a.eps);
@@ -159,7 +161,8 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
     }
 }
 
-// One wave per row over all of its nq q heads and nkv k heads.  A head is held
+// One wave per row over all of its nq q heads and nkv k heads (and, with
+// v_norm, its nkv v heads: weightless RMS, no rotation).  A head is held
 // by LH = hd / VE lanes, each owning VE consecutive channels (one 16-byte
 // vector: 4 f32 or 8 f16), so a wave covers 64 / LH heads per pass with fully
 // coalesced loads.  The per-head RMS is a butterfly inside the LH-lane group;
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     const int lane = threadIdx.x & 63;
     if (row >= a.rows) return;
     const int hsub = lane / LH, c0 = (lane % LH) * VE;
-    const uint32_t heads = a.nq + a.nkv;
+    const uint32_t heads = a.nq + a.nkv + (a.v_norm ? a.nkv : 0);
     const int S = a.sections ? HD / (int)a.sections : HD, half = S / 2;
     const int s_idx = c0 / S, i0 = c0 % S;
     const bool first = i0 < half;
@@ -193,8 +196,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     for (uint32_t h0 = 0; h0 < heads; h0 += HP) {
         const uint32_t hh = h0 + hsub;
         const bool valid = hh < heads;
-        const bool isq = hh < a.nq;
-        const uint32_t col = isq ? a.q_col + hh * HD : a.k_col + (hh - a.nq) * HD;
+        const bool isq = hh < a.nq, isv = hh >= a.nq + a.nkv;
+        const uint32_t col = isq ? a.q_col + hh * HD
+                                 : isv ? a.v_col + (hh - a.nq - a.nkv) * HD : a.k_col + (hh - a.nq) * HD;
         const float *w = isq ? a.qw : a.kw;
         float x[VE];
         if (valid) {
@@ -220,8 +224,10 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
         const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
         if (valid) {
 #pragma unroll
-            for (int e = 0; e < VE; e++) x[e] = x[e] * inv * w[c0 + e];
+            for (int e = 0; e < VE; e++) x[e] = isv ? x[e] * inv : x[e] * inv * w[c0 + e];
         }
+        // the v heads come last: a pass of them is wave-uniform in isv except
+        // for its k/v boundary, where the rotated value of a v lane is dropped
         if (a.sections) {
             float y[VE];
 #pragma unroll
@@ -229,8 +235,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
                 const float xp = __shfl_xor(x[e], pmask, 64);
                 y[e] = first ? x[e] * cs[e] - xp * sn[e] : x[e] * cs[e] + xp * sn[e];
             }
+            if (!isv)
 #pragma unroll
-            for (int e = 0; e < VE; e++) x[e] = y[e];
+                for (int e = 0; e < VE; e++) x[e] = y[e];
         }
         if (valid) {
             if (F16) {

@@ -18,6 +18,19 @@ _F32_NAMES = ["bq", "bk", "bv", "bo", "b_up", "b_down", "norm1_w", "norm1_b", "n
               "norm2_b", "post_attn_w", "post_ff_w", "q_norm_w", "k_norm_w",
               "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down"]
 _W_NAMES = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
+_PLE_NAMES = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
+
+
+def rope_bases(w: wl.Workload) -> list:
+    """Distinct RoPE bases of the layers, in order of first use: table i of the
+    batch holds base i."""
+    bases = []
+    for t in w.layers:
+        b = float(t.get("rope_base", w.cfg["rope_base"]))
+        if b not in bases:
+            bases.append(b)
+    assert len(bases) <= B.MAX_ROPE_TABLES
+    return bases
 
 
 class DeviceModel:
@@ -28,13 +41,20 @@ class DeviceModel:
         self.nlayers = nl
         self.layers = (B.Layer * max(1, nl))()
         shapes = wl.weight_shapes(cfg)
+        bases = rope_bases(w)
         for li in range(nl):
             t = w.layers[li]
             L = self.layers[li]
             for n in B._LAYER_U32:
                 setattr(L, n, int(cfg[n]))
+            L.window = int(t.get("window", cfg["window"]))
             L.eps = cfg["eps"]
             L.attn_scale = cfg["attn_scale"]
+            L.v_norm = 1 if cfg.get("v_norm") else 0
+            L.rope_table = bases.index(float(t.get("rope_base", cfg["rope_base"])))
+            L.scalar = float(t.get("scalar", 1.0))
+            L.n_ple = int(cfg.get("n_ple", 0))
+            L.ple_scale = float(cfg.get("ple_scale", 1.0))
             for n in _W_NAMES:
                 if n not in shapes:
                     continue
@@ -45,7 +65,7 @@ class DeviceModel:
                     dev = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
                 self.keep.append(dev)
                 setattr(L, n, dev.data_ptr())
-            for n in _F32_NAMES:
+            for n in _F32_NAMES + _PLE_NAMES:
                 if t.get(n) is not None:
                     dev = torch.from_numpy(np.ascontiguousarray(t[n], np.float32)).to(device)
                     self.keep.append(dev)
@@ -81,13 +101,16 @@ class DeviceBatch:
         self.batch.nitems = len(w.items)
         self.cos = self.sin = None
         sec = cfg["rope_sections"]
+        self.tables = []
         if sec:
             self.pos = B.positions(w.rows, w.items, w.grids, sec)
-            cos, sin = B.rope_table(self.pos, cfg["hd"], sec, cfg["rope_base"])
-            self.cos = torch.from_numpy(cos).to(device)
-            self.sin = torch.from_numpy(sin).to(device)
-            self.batch.rope_cos = self.cos.data_ptr()
-            self.batch.rope_sin = self.sin.data_ptr()
+            for i, base in enumerate(rope_bases(w)):
+                cos, sin = B.rope_table(self.pos, cfg["hd"], sec, base)
+                cos, sin = torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device)
+                self.tables.append((cos, sin))
+                self.batch.rope_cos[i] = cos.data_ptr()
+                self.batch.rope_sin[i] = sin.data_ptr()
+            self.cos, self.sin = self.tables[0]
 
 
 def encoder_forward(model: DeviceModel, batch: DeviceBatch, x, out, ws, ctx=None, stream=None):
