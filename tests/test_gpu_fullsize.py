@@ -188,6 +188,15 @@ def test_vit_encoder_full_stack_vs_oracle():
     assert err <= TOL_F32
 
 
+def test_vision_tower_full_stack_vs_oracle():
+    """The vision tower whole: five images (2176 rows), 16 layers; every row."""
+    w = wl.make("gemma_vision_f32")
+    got = host(run(w))
+    err = row_rel_err(got, O.forward(w))
+    say(f"full vision tower: error {err:.2e}")
+    assert err <= TOL_F32
+
+
 def test_dit_1056_full_width_layer_vs_oracle():
     """C4 at full width and rows (1056 x 3840, 30 heads of 128, SwiGLU 10240), one
     layer; every output row against the oracle with its f16 sites."""

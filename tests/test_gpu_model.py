@@ -50,6 +50,9 @@ CASES = [
     # scalars, per-layer input
     ("gemma_text_ple_f32", dict(layers=3, lengths=[600, 37, 1100, 5, 130],
                                 overrides=dict(global_every=2))),
+    # the vision tower: images of 20x20, 12x12, 9x9 and 3x3 patches (the first
+    # two take the key split)
+    ("gemma_vision_f32", dict(layers=2, lengths=[20, 12, 9, 3])),
 ]
 
 
@@ -104,6 +107,18 @@ def test_packed_equals_separate_stack(name):
         alone = run(ws_, x=w.x[r:r + n])
         assert torch.equal(alone[0], packed[i]), f"sequence {i}"
         r += n
+
+
+def test_packed_images_equal_separate():
+    """Vision tower: each packed image gets the bits of its forward alone."""
+    sides = [20, 7, 12]
+    w = wl.make("gemma_vision_f32", layers=2, lengths=sides)
+    packed = run(w)
+    r = 0
+    for i, g in enumerate(sides):
+        alone = run(wl.make("gemma_vision_f32", layers=2, lengths=[g]), x=w.x[r:r + g * g])
+        assert torch.equal(alone, packed[r:r + g * g]), f"image {i}"
+        r += g * g
 
 
 def test_cfg_pair_equals_two_singles():

@@ -401,6 +401,8 @@ def _angles(pos, sections, hd, base):
     ("gemma_text_f32", dict(lengths=[9, 30, 4], overrides=dict(window=6))),
     ("zimage_dit_1056", dict(grid=3, ncap=4, cfg_pair=True,
                              overrides=dict(d=256, nq=2, nkv=2, ff=384))),
+    # the vision tower: several images (3x3, 4x4, 2x2 grids), 2-D RoPE, no captions
+    ("gemma_vision_f32", dict(lengths=[3, 4, 2], overrides=dict(d=128, nq=2, nkv=2, ff=256))),
 ])
 def test_sandwich_layer_matches_torch_composition(oracle, name, kw):
     w = wl.make(name, layers=1, **kw)

@@ -1,6 +1,6 @@
 """Synthetic workloads of the packed encoder forward: shapes, items and seeded tensors.
 
-Six workloads, each the shape of one of the encoders on the reference pages,
+Seven workloads, each the shape of one of the encoders on the reference pages,
 with random weights (no trained checkpoint is available):
 
   vit_layer_f32        one pre-LN ViT layer: 64 tokens, d 128, 2x64 heads, MLP 512
@@ -17,6 +17,9 @@ with random weights (no trained checkpoint is available):
   gemma_text_ple_f32   the text encoder's full layer spec on the gemma_text_f32 batch:
                        8 q / 2 kv heads, v-norm, 5 windowed : 1 global layers with
                        RoPE bases 1e4 / 1e6, layer scalars, per-layer input (256 wide)
+  gemma_vision_f32     the text model's vision tower: 16 sandwich layers, d 768, 12x64
+                       heads, qk-norm + 2-D RoPE, gated GELU 3072, five images of
+                       32x32, 24x24, 16x16, 16x16 and 8x8 patches packed back to back
 
 Only draws and shapes live here; the forward itself is computed by the HIP
 library (and, independently, by the oracle).
@@ -64,6 +67,18 @@ CONFIGS = {
         ff=3072, layers=16, window=0, rope_sections=0, final=FINAL_LN, eps=1e-6,
         attn_scale=1.0 / 8.0, rope_base=10000.0, x_scale=1.0, biases=True,
         lengths=[1024]),
+    # the text model's vision tower: sandwich RMS blocks, qk-norm + 2-D RoPE
+    # (column half, row half) over several images packed back to back, hd-64
+    # flash per image with scale 1, gated GELU; H out (no final norm).  The
+    # q/k norm gains are drawn around hd^-1/4 (they carry the softmax
+    # temperature at scale 1): with gains near 1 the logits have a standard
+    # deviation of 8, attention is nearly one-hot and 16 random layers amplify
+    # f32 rounding several thousand times
+    "gemma_vision_f32": dict(
+        num=7, block=BLOCK_SANDWICH, path=PATH_F32, mlp=MLP_GELU_GATED, d=768, nq=12, nkv=12,
+        hd=64, ff=3072, layers=16, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0, rope_base=10000.0, x_scale=1.0, biases=False,
+        image_grids=[32, 24, 16, 16, 8], qk_gain=64 ** -0.25),
     "zimage_dit_1056": dict(
         num=4, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
         hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
@@ -157,7 +172,8 @@ def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
         for name in ("norm1_w", "post_attn_w", "norm2_w", "post_ff_w"):
             t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
         for name in ("q_norm_w", "k_norm_w"):
-            t[name] = _normal(seed, f"L{li}.{name}", (hd,), 0.02, 1.0)
+            g = cfg.get("qk_gain", 1.0)
+            t[name] = _normal(seed, f"L{li}.{name}", (hd,), 0.02 * g, g)
     # per-layer values: every global_every-th layer attends globally (window 0)
     # with its own RoPE base; the rest keep the config's window and base
     ge = cfg.get("global_every", 0)
@@ -182,11 +198,20 @@ def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
 def layout(cfg: dict, lengths=None, grid=None, ncap=None, cfg_pair=None):
     """(rows, items, grids) of a workload.
 
+    Images (2-D, no captions): one single-range item of G*G rows per grid side
+    in `image_grids` (or `lengths` read as grid sides), back to back.
     Sequences (1-D): `lengths` back to back, one single-range item each.
     DiT (2-D): one item = G*G image rows + ncap caption rows; the CFG pair is two
     items over rows [img0 | img1 | cap0 | cap1], each item = its image range then
     its caption range.
     """
+    if cfg["rope_sections"] == 2 and "image_grids" in cfg:
+        sides = cfg["image_grids"] if lengths is None else lengths
+        items, r = [], 0
+        for g in sides:
+            items.append([(r, g * g)])
+            r += g * g
+        return r, items, [int(g) for g in sides]
     if cfg["rope_sections"] == 2:
         g = cfg["grid"] if grid is None else grid
         nc = cfg["ncap"] if ncap is None else ncap
@@ -221,7 +246,7 @@ def make(name: str, layers=None, lengths=None, grid=None, ncap=None, cfg_pair=No
     seed = MASTER_SEED + cfg["num"]
     rows, items, grids = layout(cfg, lengths, grid, ncap, cfg_pair)
     d = cfg["d"]
-    if cfg["rope_sections"] == 2:
+    if cfg["rope_sections"] == 2 and "image_grids" not in cfg:
         # image rows are one draw shared by every item (one latent, CFG pair);
         # each item's caption rows are its own draw
         x = np.empty((rows, d), np.float32)
