@@ -57,6 +57,9 @@ _LAYER_PTRS_B = ["bq", "bk", "bv", "bo", "b_up", "b_down"]
 _LAYER_PTRS_N = ["norm1_w", "norm1_b", "norm2_w", "norm2_b", "post_attn_w", "post_ff_w",
                  "q_norm_w", "k_norm_w"]
 _LAYER_PTRS_PLE = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
+_LAYER_PTRS_MOD = ["mod_s_attn", "mod_g_attn", "mod_s_ff", "mod_g_ff"]
+_LAYER_PTRS_COL = ["col_q", "col_k", "col_v", "col_o", "col_gate", "col_up", "col_down"]
+_LAYER_GUARDS = ["guard_attn", "guard_qkv", "guard_ao", "guard_ffn", "guard_hid"]
 
 
 class Layer(C.Structure):
@@ -69,7 +72,9 @@ class Layer(C.Structure):
                    + _LAYER_PTRS_N]
                 + [("v_norm", C.c_int32), ("n_ple", C.c_int32), ("scalar", C.c_double),
                    ("ple_scale", C.c_double)]
-                + [(n, C.POINTER(C.c_float)) for n in _LAYER_PTRS_PLE])
+                + [(n, C.POINTER(C.c_float)) for n in _LAYER_PTRS_PLE + _LAYER_PTRS_MOD
+                   + _LAYER_PTRS_COL]
+                + [(n, C.c_int32) for n in _LAYER_GUARDS])
 
 
 class Model(C.Structure):
@@ -105,7 +110,7 @@ def _setup(L):
                                _D, C.c_int, _D, C.c_int, _D, C.c_int, C.c_double, C.c_int]
     L.or_attention_rows.argtypes = L.or_attention.argtypes + [_I8]
     L.or_encoder_forward.argtypes = [C.POINTER(Model), C.c_int64, C.c_int, C.POINTER(Item), _D,
-                                     _D, C.c_int]
+                                     _D, C.c_int, _D]
     for f in ("or_rms_norm", "or_layer_norm", "or_linear", "or_linear_q8", "or_positions",
               "or_qk_norm_rope", "or_attention", "or_attention_rows", "or_encoder_forward"):
         getattr(L, f).restype = None
@@ -241,11 +246,15 @@ def _layer_struct(cfg, t, keep):
     L.scalar = float(t.get("scalar", 1.0))
     L.n_ple = int(cfg.get("n_ple", 0))
     L.ple_scale = float(cfg.get("ple_scale", 1.0))
-    for n in _LAYER_PTRS_PLE:
+    for n in _LAYER_PTRS_PLE + _LAYER_PTRS_MOD + _LAYER_PTRS_COL:
         if t.get(n) is not None:
             a, p = _f(t[n])
             keep.append(a)
             setattr(L, n, p)
+    guards = t.get("guards", cfg.get("guards"))
+    if guards:
+        for n, g in zip(_LAYER_GUARDS, guards):
+            setattr(L, n, int(g))
     for fn, qn, sn in zip(_LAYER_PTRS_F, _LAYER_PTRS_Q, _LAYER_PTRS_S):
         if fn not in t:
             continue
@@ -268,8 +277,10 @@ def _layer_struct(cfg, t, keep):
     return L
 
 
-def forward(w, layers=None, f16_sites: bool = True, x=None):
-    """The oracle forward of a workload-like object (first `layers` layers)."""
+def forward(w, layers=None, f16_sites: bool = True, x=None, amax=None):
+    """The oracle forward of a workload-like object (first `layers` layers).
+    amax: an optional float64 array [layers][5] that receives the per-site
+    max |stored value| of the int8 path's half sites."""
     cfg = w.cfg
     nl = len(w.layers) if layers is None else layers
     keep = []
@@ -291,7 +302,11 @@ def forward(w, layers=None, f16_sites: bool = True, x=None):
     nout = len(w.items) if cfg["final"] == 2 else w.rows
     out = np.zeros((nout, d))
     it = _items(w.items, w.grids)
+    if amax is not None:
+        assert amax.dtype == np.float64 and amax.shape == (nl, 5) and amax.flags.c_contiguous
+        amax[:] = 0.0
     lib().or_encoder_forward(C.byref(M), w.rows, len(w.items), it, xp, out.ctypes.data_as(_D),
-                             1 if f16_sites else 0)
+                             1 if f16_sites else 0,
+                             amax.ctypes.data_as(_D) if amax is not None else None)
     del keep, fw, fb
     return out

@@ -398,6 +398,21 @@ typedef struct {
     int32_t v_norm, n_ple;
     double scalar, ple_scale;
     const float *ple_in, *ple_gate, *ple_proj, *ple_in_norm_w, *ple_post_w;
+    /* the int8 DiT block's row-op contract ([ZI] `Enc::block`, `Enc::rowop`,
+     * module doc "The chain"):
+     * mod_*: adaLN modulation [d], NULL = off ([ZI] `block`: this block's
+     *   [s_msa|g_msa|s_mlp|g_mlp]): a pre-norm output is multiplied by
+     *   (1 + s), a residual update by g (s = 0, g = 1 is the unmodulated form
+     *   of [ZI] `refine_caption`);
+     * col_*: the q8_2f column field [in] of each weight, NULL = ones:
+     *   W_eff[j][k] = rs[j] q[j][k] col[k], folded into the half input by its
+     *   producer (the row op for q/k/v and w1/w3, the attention epilogue for
+     *   the O projection, SwiGLU for w2);
+     * guard_*: [ZI] `Guards`: the half site stores x 2^-s and its consumer
+     *   multiplies 2^s back (int8 path). */
+    const float *mod_s_attn, *mod_g_attn, *mod_s_ff, *mod_g_ff;
+    const float *col_q, *col_k, *col_v, *col_o, *col_gate, *col_up, *col_down;
+    int32_t guard_attn, guard_qkv, guard_ao, guard_ffn, guard_hid;
 } or_layer;
 
 typedef struct {
@@ -408,6 +423,37 @@ typedef struct {
     const float *final_w, *final_b;
     double final_eps;
 } or_model;
+
+/* y[i][k] = x[i][k] * (1 + s[k]) (s NULL: a copy) */
+static void modulate(int64_t n, int d, const double *x, const float *s, double *y)
+{
+    for (int64_t i = 0; i < n; i++)
+        for (int k = 0; k < d; k++)
+            y[i * d + k] = x[i * d + k] * (s ? 1.0 + (double)s[k] : 1.0);
+}
+
+/* A half site of the int8 path: y = x * col[k] * 2^-guard, rounded to binary16
+ * when r16 (col NULL: ones).  The amax slot (nullable) takes max |y|. */
+static void half_site(int64_t n, int d, const double *x, const float *col, int guard, int r16,
+                      double *y, double *amax)
+{
+    const double g = ldexp(1.0, -guard);
+    for (int64_t i = 0; i < n; i++)
+        for (int k = 0; k < d; k++) {
+            double v = x[i * d + k] * (col ? (double)col[k] : 1.0) * g;
+            if (r16)
+                v = or_round_f16(v);
+            y[i * d + k] = v;
+            if (amax && fabs(v) > *amax)
+                *amax = fabs(v);
+        }
+}
+
+static void scale_all(double *v, int64_t n, double c)
+{
+    for (int64_t i = 0; i < n; i++)
+        v[i] *= c;
+}
 
 /* One projection of the layer: f32 weight (+bias) or int8 weight x row scale. */
 static void project(const or_layer *L, int64_t n, int k, int m, const double *x, const float *wf,
@@ -442,16 +488,29 @@ static void maybe_f16(int on, double *v, int64_t n)
  *   H += att Wo^T + bo;  A = LN(H; norm2);  H += gelu_tanh(A Wu^T + bu) Wd^T + bd
  * Options of the sandwich block: v_norm right after the q/k norm + RoPE; the
  * per-layer-input branch after the FFN, reading X0 (the forward's input rows);
- * the layer scalar multiplying H after the layer's last residual add.
+ * the layer scalar multiplying H after the layer's last residual add; adaLN
+ * modulation (each pre-norm output times (1 + s), each residual update times
+ * g).  On the int8 path every half site stores x col 2^-guard (the column
+ * field of the weight that reads it, its power-of-two guard) and the consumer
+ * multiplies the guard back: the q/k/v and w1/w3 GEMM epilogues, the qk-norm's
+ * eps (scaled by 2^-2 guard), the attention epilogue, the O and w2 epilogues.
  * `f16_sites` rounds to binary16 exactly where the int8 path stores half; 0
- * gives the pure-f64 diagnostic. */
+ * gives the pure-f64 diagnostic.  amax (nullable, [5]) takes max |stored
+ * value| per site: q/k/v input, panel, attention output, w1/w3 input, hidden. */
 static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_item *items,
-                          const int32_t *pos, double *H, const double *X0, int f16_sites)
+                          const int32_t *pos, double *H, const double *X0, int f16_sites,
+                          double *amax)
 {
     int d = L->d, hd = L->hd, nq = L->nq, nkv = L->nkv, ff = L->ff;
     int qw = nq * hd, kw = nkv * hd;
-    int r16 = f16_sites && L->path == OR_I8F16;
+    int i8 = L->path == OR_I8F16;
+    int r16 = f16_sites && i8;
+    /* guards exist on the int8 path only */
+    int ga = i8 ? L->guard_attn : 0, gq = i8 ? L->guard_qkv : 0, gao = i8 ? L->guard_ao : 0;
+    int gf = i8 ? L->guard_ffn : 0, gh = i8 ? L->guard_hid : 0;
+    double *am = amax; /* [5]: xn, panel, attention out, FFN input, hidden */
     double *A = (double *)malloc(sizeof(double) * rows * d);
+    double *Az = (double *)malloc(sizeof(double) * rows * d);
     double *Q = (double *)malloc(sizeof(double) * rows * qw);
     double *K = (double *)malloc(sizeof(double) * rows * kw);
     double *V = (double *)malloc(sizeof(double) * rows * kw);
@@ -461,58 +520,82 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
     double *U = (double *)malloc(sizeof(double) * rows * ff);
 
     /* attention half */
-    if (L->block == OR_SANDWICH)
-        or_rms_norm(rows, d, H, L->norm1_w, L->eps, A);
-    else
-        or_layer_norm(rows, d, H, L->norm1_w, L->norm1_b, L->eps, A);
-    maybe_f16(r16, A, rows * d);
-    project(L, rows, d, qw, A, L->wq, L->qq, L->sq, L->bq, Q);
-    project(L, rows, d, kw, A, L->wk, L->qk, L->sk, L->bk, K);
-    project(L, rows, d, kw, A, L->wv, L->qv, L->sv, L->bv, V);
-    maybe_f16(r16, Q, rows * qw);
-    maybe_f16(r16, K, rows * kw);
-    maybe_f16(r16, V, rows * kw);
     if (L->block == OR_SANDWICH) {
-        or_qk_norm_rope(rows, nq, hd, Q, L->q_norm_w, L->eps, L->rope_sections, pos, L->rope_base);
-        or_qk_norm_rope(rows, nkv, hd, K, L->k_norm_w, L->eps, L->rope_sections, pos, L->rope_base);
+        or_rms_norm(rows, d, H, L->norm1_w, L->eps, A);
+        modulate(rows, d, A, L->mod_s_attn, A);
+    } else {
+        or_layer_norm(rows, d, H, L->norm1_w, L->norm1_b, L->eps, A);
+    }
+    /* q, k, v each from its own half input A * col * 2^-ga; the GEMM epilogue
+     * multiplies 2^(ga - gq) (undo the input guard, apply the panel's) */
+    const float *cols[3] = {L->col_q, L->col_k, L->col_v};
+    double *outs[3] = {Q, K, V};
+    const int widths[3] = {qw, kw, kw};
+    const float *wf[3] = {L->wq, L->wk, L->wv}, *rs[3] = {L->sq, L->sk, L->sv};
+    const int8_t *wqq[3] = {L->qq, L->qk, L->qv};
+    const float *bs[3] = {L->bq, L->bk, L->bv};
+    for (int z = 0; z < 3; z++) {
+        half_site(rows, d, A, cols[z], ga, r16, Az, am ? &am[0] : NULL);
+        project(L, rows, d, widths[z], Az, wf[z], wqq[z], rs[z], bs[z], outs[z]);
+        scale_all(outs[z], rows * widths[z], ldexp(1.0, ga - gq));
+        half_site(rows, widths[z], outs[z], NULL, 0, r16, outs[z], am ? &am[1] : NULL);
+    }
+    if (L->block == OR_SANDWICH) {
+        /* the panel holds x 2^-gq: eps scaled by 2^-2gq gives rms(x) exactly */
+        double eps_q = L->eps * ldexp(1.0, -2 * gq);
+        or_qk_norm_rope(rows, nq, hd, Q, L->q_norm_w, eps_q, L->rope_sections, pos, L->rope_base);
+        or_qk_norm_rope(rows, nkv, hd, K, L->k_norm_w, eps_q, L->rope_sections, pos, L->rope_base);
         maybe_f16(r16, Q, rows * qw);
         maybe_f16(r16, K, rows * kw);
         if (L->v_norm) {
             /* every v head of every row is one hd-wide row of V */
-            or_rms_norm(rows * nkv, hd, V, NULL, L->eps, V);
+            or_rms_norm(rows * nkv, hd, V, NULL, eps_q, V);
             maybe_f16(r16, V, rows * kw);
         }
     }
     or_attention(nitems, items, nq, nkv, hd, Q, qw, K, kw, V, kw, Att, qw, L->attn_scale, L->window);
-    maybe_f16(r16, Att, rows * qw);
+    /* attention epilogue: v carried 2^-gq; the O input stores att col_o 2^-gao */
+    scale_all(Att, rows * qw, ldexp(1.0, gq));
+    half_site(rows, qw, Att, L->col_o, gao, r16, Att, am ? &am[2] : NULL);
     project(L, rows, qw, d, Att, L->wo, L->qo, L->so, L->bo, T);
+    scale_all(T, rows * d, ldexp(1.0, gao));
     if (L->block == OR_SANDWICH) {
         or_rms_norm(rows, d, T, L->post_attn_w, L->eps, T);
         for (int64_t i = 0; i < rows * d; i++)
-            H[i] += T[i];
+            H[i] += T[i] * (L->mod_g_attn ? (double)L->mod_g_attn[i % d] : 1.0);
         or_rms_norm(rows, d, H, L->norm2_w, L->eps, A);
+        modulate(rows, d, A, L->mod_s_ff, A);
     } else {
         for (int64_t i = 0; i < rows * d; i++)
             H[i] += T[i];
         or_layer_norm(rows, d, H, L->norm2_w, L->norm2_b, L->eps, A);
     }
-    maybe_f16(r16, A, rows * d);
 
-    /* MLP half */
-    project(L, rows, d, ff, A, L->w_up, L->q_up, L->s_up, L->b_up, U);
+    /* MLP half: gate and up each from A * col * 2^-gf, times 2^gf after the GEMM */
+    half_site(rows, d, A, L->col_up, gf, r16, Az, am ? &am[3] : NULL);
+    project(L, rows, d, ff, Az, L->w_up, L->q_up, L->s_up, L->b_up, U);
+    scale_all(U, rows * ff, ldexp(1.0, gf));
     if (L->mlp == OR_GELU) {
         for (int64_t i = 0; i < rows * ff; i++)
             U[i] = or_gelu_tanh(U[i]);
     } else {
-        project(L, rows, d, ff, A, L->w_gate, L->q_gate, L->s_gate, NULL, G);
+        half_site(rows, d, A, L->col_gate, gf, r16, Az, am ? &am[3] : NULL);
+        project(L, rows, d, ff, Az, L->w_gate, L->q_gate, L->s_gate, NULL, G);
+        scale_all(G, rows * ff, ldexp(1.0, gf));
         for (int64_t i = 0; i < rows * ff; i++)
             U[i] = (L->mlp == OR_GELU_GATED ? or_gelu_tanh(G[i]) : or_silu(G[i])) * U[i];
     }
-    maybe_f16(r16, U, rows * ff);
+    /* the w2 input: hidden col_down 2^-gh */
+    half_site(rows, ff, U, L->col_down, gh, r16, U, am ? &am[4] : NULL);
     project(L, rows, ff, d, U, L->w_down, L->q_down, L->s_down, L->b_down, T);
+    scale_all(T, rows * d, ldexp(1.0, gh));
     const double scalar = L->scalar == 0.0 ? 1.0 : L->scalar;
-    if (L->block == OR_SANDWICH)
+    if (L->block == OR_SANDWICH) {
         or_rms_norm(rows, d, T, L->post_ff_w, L->eps, T);
+        if (L->mod_g_ff)
+            for (int64_t i = 0; i < rows * d; i++)
+                T[i] *= (double)L->mod_g_ff[i % d];
+    }
     for (int64_t i = 0; i < rows * d; i++)
         H[i] += T[i];
     if (L->n_ple > 0) {
@@ -541,7 +624,7 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
         for (int64_t i = 0; i < rows * d; i++)
             H[i] *= scalar;
 
-    free(A); free(Q); free(K); free(V); free(Att); free(T); free(G); free(U);
+    free(A); free(Az); free(Q); free(K); free(V); free(Att); free(T); free(G); free(U);
 }
 
 /* The whole forward: x [rows][d] -> out.
@@ -552,7 +635,7 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
  * weighted mean).  Layers run in order, each starting from the H the previous
  * one left (the fused next-layer pre-norm of the pages computes the same A). */
 OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, const or_item *items,
-                               const double *x, double *out, int f16_sites)
+                               const double *x, double *out, int f16_sites, double *amax)
 {
     int d = M->d;
     int sec = M->nlayers > 0 ? M->layers[0].rope_sections : 0;
@@ -562,7 +645,8 @@ OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, cons
     double *H = (double *)malloc(sizeof(double) * rows * d);
     memcpy(H, x, sizeof(double) * rows * d);
     for (int l = 0; l < M->nlayers; l++)
-        layer_forward(&M->layers[l], rows, nitems, items, pos, H, x, f16_sites);
+        layer_forward(&M->layers[l], rows, nitems, items, pos, H, x, f16_sites,
+                      amax ? amax + 5 * l : NULL);
     if (M->final_kind == OR_FINAL_NONE) {
         memcpy(out, H, sizeof(double) * rows * d);
     } else if (M->final_kind == OR_FINAL_LN) {

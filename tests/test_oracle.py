@@ -447,6 +447,134 @@ def test_text_encoder_options_match_torch_composition(oracle):
         assert np.abs(oracle.forward(w2) - out).max() > 1e-3 * np.abs(out).max(), key
 
 
+DIT_MOD_SMALL = dict(layers=1, grid=3, ncap=4, overrides=dict(d=256, nq=2, nkv=2, ff=384))
+
+
+def _dit_mod(**kw):
+    args = dict(DIT_MOD_SMALL)
+    args.update(kw)
+    w = wl.make("zimage_dit_mod_1056", **args)
+    w.cfg["final"] = wl.FINAL_NONE
+    return w
+
+
+def _torch_dit_mod_layer(c, t, x, pos_cos_sin, items):
+    """The modulated int8 block in exact arithmetic (torch f64), with the column
+    fields folded into the weights, W_eff = diag(rs) q diag(col), and no guards
+    (they cancel exactly): an independent form of what the half-site chain
+    computes when nothing is rounded; also returns each site's max |value|
+    (as stored, after the column field and the guard)."""
+    F = torch.nn.functional
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    eps, hd, nq = c["eps"], c["hd"], c["nq"]
+    ga, gq, gao, gf, gh = c["guards"]
+    H = T(x)
+    d = H.shape[1]
+    W = lambda n: (T(t["s" + n[1:]])[:, None] * T(t[n].astype(np.float64))
+                   * T(t["col_" + n[1:].lstrip("_")])[None, :])
+    amax = np.zeros(5)
+    def site(i, v, colname, g):
+        amax[i] = max(amax[i], float((v * T(t[colname]) * 2.0 ** -g).abs().max()) if colname
+                      else float((v * 2.0 ** -g).abs().max()))
+    A = F.rms_norm(H, (d,), T(t["norm1_w"]), eps) * (1 + T(t["mod_s_attn"]))
+    for n in ("col_q", "col_k", "col_v"):
+        site(0, A, n, ga)
+    q, k, v = A @ W("wq").T, A @ W("wk").T, A @ W("wv").T
+    for z in (q, k, v):
+        site(1, z, None, gq)
+    cos, sin = pos_cos_sin
+
+    def qk(z, wn):
+        z = F.rms_norm(z.view(z.shape[0], nq, hd), (hd,), T(wn), eps)
+        S = hd // 2
+        parts = []
+        for s_ in range(2):
+            zz = z[..., s_ * S:(s_ + 1) * S]
+            cs, sn = cos[s_][:, None, :], sin[s_][:, None, :]
+            a, b = zz[..., :S // 2], zz[..., S // 2:]
+            parts += [a * cs - b * sn, b * cs + a * sn]
+        return torch.cat(parts, -1).reshape(z.shape[0], nq * hd)
+
+    q, k = qk(q, t["q_norm_w"]), qk(k, t["k_norm_w"])
+    att = torch.zeros_like(q)
+    for rr in items:
+        idx = torch.cat([torch.arange(r0, r0 + n) for r0, n in rr])
+        L = len(idx)
+        qh, kh, vh = (z[idx].view(L, nq, hd).transpose(0, 1) for z in (q, k, v))
+        att[idx] = F.scaled_dot_product_attention(qh, kh, vh, scale=c["attn_scale"]).transpose(0, 1).reshape(L, nq * hd)
+    site(2, att, "col_o", gao)
+    H = H + T(t["mod_g_attn"]) * F.rms_norm(att @ W("wo").T, (d,), T(t["post_attn_w"]), eps)
+    A = F.rms_norm(H, (d,), T(t["norm2_w"]), eps) * (1 + T(t["mod_s_ff"]))
+    for n in ("col_gate", "col_up"):
+        site(3, A, n, gf)
+    m = F.silu(A @ W("w_gate").T) * (A @ W("w_up").T)
+    site(4, m, "col_down", gh)
+    H = H + T(t["mod_g_ff"]) * F.rms_norm(m @ W("w_down").T, (d,), T(t["post_ff_w"]), eps)
+    return H.numpy(), amax
+
+
+def test_dit_modulated_layer_matches_torch_composition(oracle):
+    """adaLN modulation, q8_2f column fields and guards: the oracle's half-site
+    chain without rounding equals the folded-weight form in exact arithmetic,
+    and so do its per-site maxima."""
+    w = _dit_mod()
+    c = w.cfg
+    pos = oracle.positions(w.rows, w.items, w.grids, 2)
+    ref, ref_amax = _torch_dit_mod_layer(c, w.layers[0], w.x, _angles(pos, 2, c["hd"], c["rope_base"]),
+                                         w.items)
+    amax = np.zeros((1, 5))
+    out = oracle.forward(w, f16_sites=False, amax=amax)
+    assert np.abs(out - ref).max() / np.abs(ref).max() < 1e-12
+    assert np.allclose(amax[0], ref_amax, rtol=1e-12)
+    # with the f16 sites: within the int8 path's tolerance of the exact result
+    out16 = oracle.forward(w)
+    assert np.abs(out16 - ref).max() / np.abs(ref).max() < 3e-3
+
+
+def test_guards_cancel_exactly_without_rounding(oracle):
+    """A guard multiplies by 2^-s at a half site and 2^s at its consumer, and
+    the qk-norm's eps is scaled by 2^-2s: in f64 these are exact, so without
+    the f16 rounding every guard set gives the same bits."""
+    outs = []
+    for g in ([0, 0, 0, 0, 0], [0, 1, 0, 0, 6], [6, 8, 6, 6, 11]):
+        w = _dit_mod(layers=2, overrides=dict(DIT_MOD_SMALL["overrides"], guards=g))
+        outs.append(oracle.forward(w, f16_sites=False))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_guard_keeps_the_hidden_in_half_range(oracle):
+    """Up/gate row scales raised until the SwiGLU hidden passes 65504: the
+    stored half overflows to infinity without a guard; with the hidden guard
+    (2^-6) it stays finite and within the int8 tolerance of the exact result."""
+    res = {}
+    for gh in (0, 6):
+        w = _dit_mod(overrides=dict(DIT_MOD_SMALL["overrides"], guards=[0, 1, 0, 0, gh]))
+        for n in ("s_gate", "s_up"):
+            w.layers[0][n] = w.layers[0][n] * np.float32(150.0)
+        amax = np.zeros((1, 5))
+        res[gh] = (oracle.forward(w, amax=amax), amax[0, 4], oracle.forward(w, f16_sites=False))
+    out0, am0, exact = res[0]
+    out6, am6, _ = res[6]
+    assert not np.isfinite(out0).all() and am0 == np.inf
+    assert np.isfinite(out6).all() and 65504 / 64 < am6 <= 65504
+    assert np.abs(out6 - exact).max() / np.abs(exact).max() < 3e-3
+
+
+def test_unit_modulation_is_unmodulated(oracle):
+    """s = 0, g = 1 (the context refiner's form) gives the unmodulated bits."""
+    w = _dit_mod(layers=2)
+    for t in w.layers:
+        for n in ("mod_s_attn", "mod_s_ff"):
+            t[n] = np.zeros_like(t[n])
+        for n in ("mod_g_attn", "mod_g_ff"):
+            t[n] = np.ones_like(t[n])
+    a = oracle.forward(w)
+    for t in w.layers:
+        for n in ("mod_s_attn", "mod_s_ff", "mod_g_attn", "mod_g_ff"):
+            del t[n]
+    assert np.array_equal(a, oracle.forward(w))
+
+
 def test_packed_equals_separate_forward(oracle):
     w = wl.make("gemma_text_f32", layers=2, lengths=[7, 12, 3], overrides=dict(window=4))
     out = oracle.forward(w)

@@ -1,6 +1,6 @@
 """Synthetic workloads of the packed encoder forward: shapes, items and seeded tensors.
 
-Seven workloads, each the shape of one of the encoders on the reference pages,
+Eight workloads, each the shape of one of the encoders on the reference pages,
 with random weights (no trained checkpoint is available):
 
   vit_layer_f32        one pre-LN ViT layer: 64 tokens, d 128, 2x64 heads, MLP 512
@@ -17,6 +17,8 @@ with random weights (no trained checkpoint is available):
   gemma_text_ple_f32   the text encoder's full layer spec on the gemma_text_f32 batch:
                        8 q / 2 kv heads, v-norm, 5 windowed : 1 global layers with
                        RoPE bases 1e4 / 1e6, layer scalars, per-layer input (256 wide)
+  zimage_dit_mod_1056  zimage_dit_1056 with adaLN modulation, q8_2f column fields and
+                       the Turbo power-of-two guards of the five half sites
   gemma_vision_f32     the text model's vision tower: 16 sandwich layers, d 768, 12x64
                        heads, qk-norm + 2-D RoPE, gated GELU 3072, five images of
                        32x32, 24x24, 16x16, 16x16 and 8x8 patches packed back to back
@@ -84,6 +86,17 @@ CONFIGS = {
         hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
         attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
         grid=32, ncap=32, cfg_pair=False),
+    # the 1056-row DiT stack with the rest of the int8 block's row-op contract:
+    # adaLN modulation per layer, q8_2f column fields folded into the half
+    # producers, and the power-of-two guards of the five half sites (the
+    # pages' Turbo set: q/k/v input 0, panel 1, attention out 0, FFN input 0,
+    # hidden 6)
+    "zimage_dit_mod_1056": dict(
+        num=8, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
+        hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
+        grid=32, ncap=32, cfg_pair=False, modulated=True, col_fields=True,
+        guards=[0, 1, 0, 0, 6]),
     "zimage_dit_cfg_8448": dict(
         num=5, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
         hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
@@ -183,6 +196,18 @@ def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
     else:
         t["window"] = cfg["window"]
         t["rope_base"] = cfg["rope_base"]
+    if cfg.get("modulated"):
+        # [s_msa | g_msa | s_mlp | g_mlp]: scales near 0, gates near 1
+        for name, mean in (("mod_s_attn", 0.0), ("mod_g_attn", 1.0), ("mod_s_ff", 0.0),
+                           ("mod_g_ff", 1.0)):
+            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.1, mean)
+    if cfg.get("col_fields"):
+        # q8_2f column fields: positive, lognormal around 1, one per input column
+        q = cfg["nq"] * hd
+        for name, width in (("col_q", d), ("col_k", d), ("col_v", d), ("col_o", q),
+                            ("col_gate", d), ("col_up", d), ("col_down", cfg["ff"])):
+            z = synth.normal_np(synth.tensor_key(seed, f"L{li}.{name}"), 0, width)
+            t[name] = np.exp(0.25 * z).astype(np.float32)
     if cfg.get("layer_scalar"):
         t["scalar"] = float(1.0 + 0.05 * synth.normal_np(synth.tensor_key(seed, f"L{li}.scalar"), 0, 1)[0])
     if cfg.get("n_ple"):
