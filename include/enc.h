@@ -85,12 +85,15 @@ ENC_API const char *enc_last_error(const enc_ctx *ctx);
  *                                   f32 accumulation — [ZI] module doc)
  *   r  += bias_s[j]                (when bias[s] != NULL)
  *   r   = gelu_tanh(r)             (ENC_EPI_GELU_TANH)
+ *   r   = r * y_col[j] * y_scale   (y_col nullable; y_scale 0 is read as 1)
  *   Y[it.y_off + i*it.ldy + j] = r, or += r with ENC_Y_ACCUMULATE (f32 Y only)
  * where s = it.slot.  With ENC_EPI_GATE_GELU_TANH or ENC_EPI_GATE_SILU the item
  * is a gated MLP projection ([EG] `Prog::gelu` "O = gelu_tanh(G)·U" on the z = 2
  * gate/up launch; [ZI] SwiGLU `PSw`): gate_ij and up_ij are the r above for
- * slots s and s + 1 (no bias), and Y[i][j] = act(gate_ij) * up_ij, so the
- * gate/up pair never reaches memory.  The result equals the unfused gate/up
+ * slots s and s + 1 (no bias), and Y[i][j] = act(gate_ij) * up_ij * y_col[j] *
+ * y_scale, so the gate/up pair never reaches memory.  (y_col and y_scale are
+ * the q8_2f column field of the weight that reads Y and a power-of-two guard
+ * of a half Y: [ZI] module doc "The chain", `Guards`.)  The result equals the unfused gate/up
  * GEMM followed by enc_gated_act bit for bit.  W_s is [m][k] row-major (the nn.Linear layout, [VE]
  * `VitGpuOps::linear`), dense with row stride k.
  * Geometry: k % 4 == 0 (F32) or k % 16 == 0 (I8F16); ldx, x_off multiples of 4
@@ -114,6 +117,8 @@ typedef struct {
     const float *bias[4];     /* (dev) nullable, float [m] */
     float alpha;              /* [EG] EgMm.alpha / [ZI] PMm.mul */
     uint32_t flags;           /* ENC_Y_F16 | ENC_Y_ACCUMULATE | ENC_EPI_GELU_TANH */
+    const float *y_col;       /* (dev) nullable, float [m]: multiplies column j of the result */
+    float y_scale;            /* multiplies every result; 0 is read as 1 */
 } enc_gemm_desc;
 
 ENC_API enc_status gemm_items(enc_ctx *ctx, const enc_gemm_desc *desc, const enc_gemm_item *items,
@@ -157,6 +162,10 @@ typedef struct {
     uint32_t rows;          /* panel rows (bound for the items) */
     void *ws;               /* (dev) scratch for key splits, 256-byte aligned, or NULL */
     size_t ws_bytes;        /* at least enc_attention_workspace_bytes() when ws != NULL */
+    /* output epilogue: out[i][c] = o_i[c] * out_scale * out_col[c] ([ZI]: the
+     * flash epilogue folds the O projection's column field and the guards) */
+    const float *out_col;   /* (dev) nullable, float [nq*hd] */
+    float out_scale;        /* 0 is read as 1 */
 } enc_attn_desc;
 
 /* Key splits (ENC_F32, windowless items): an item too short to occupy the GPU
@@ -199,9 +208,14 @@ ENC_API enc_status enc_rms_norm(enc_ctx *ctx, const enc_norm_desc *desc, enc_str
 ENC_API enc_status enc_layer_norm(enc_ctx *ctx, const enc_norm_desc *desc, enc_stream stream);
 
 /* Post-norm residual fused with the next pre-norm ([EG] `Prog::add_norm`
- * "H = (H + rms(T)·w)·post; then A = rms(H)·w2"; [ZI] `Enc::rowop`):
- *   h = (h + rms(t) * w_post) * post;   then, when w_next != NULL, a = rms(h) * w_next.
- * h, t f32 [rows][d] (dense); a f32 or f16 (ENC_Y_F16) [rows][d]. */
+ * "H = (H + rms(T)·w)·post; then A = rms(H)·w2"; [ZI] `Enc::rowop`, with its
+ * adaLN gate and scale, the q8_2f column fields of the next GEMM's weights and
+ * the half site's guard):
+ *   when t != NULL:      h = (h + gate * rms(t) * w_post) * post
+ *   when w_next != NULL: for z < nout,
+ *                        a_z = rms(h) * w_next * (1 + scale) * col[z] * oscale
+ * gate, scale, col[z] nullable (ones / zeros); nout 0 is read as 1; the copy z
+ * sits at a + z*rows*d.  h, t f32 [rows][d] (dense); a f32 or f16 (ENC_Y_F16). */
 typedef struct {
     uint32_t rows, d;
     float *h;             /* (dev) residual, updated in place */
@@ -212,6 +226,9 @@ typedef struct {
     void *a;              /* (dev) next block input; unused when w_next == NULL */
     uint32_t flags;       /* ENC_Y_F16 */
     float post;           /* the layer scalar; 0 is read as 1 */
+    const float *gate, *scale, *col[3]; /* (dev) nullable, float [d] each */
+    uint32_t nout;        /* copies of a (1..3) */
+    float oscale;         /* 0 is read as 1 */
 } enc_add_norm_desc;
 ENC_API enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *desc, enc_stream stream);
 
@@ -238,7 +255,9 @@ typedef struct {
 } enc_qk_desc;
 ENC_API enc_status enc_qk_norm_rope(enc_ctx *ctx, const enc_qk_desc *desc, enc_stream stream);
 
-/* Gated activation out = act(g) * u, elementwise over [rows][ff]:
+/* Gated activation out = act(g) * u * out_col * out_scale, elementwise over
+ * [rows][ff] (out_col nullable, out_scale 0 read as 1; [ZI] `PSw` folds w2's
+ * column field and the hidden's guard here):
  * ENC_ACT_GELU_TANH_GATED ([EG] `Prog::gelu` "O = gelu_tanh(G)·U") or
  * ENC_ACT_SWIGLU ([ZI] `PSw`, silu(g)·u).  Output f32 or f16 (ENC_Y_F16). */
 typedef enum { ENC_ACT_GELU_TANH_GATED = 1, ENC_ACT_SWIGLU = 2 } enc_act_kind;
@@ -248,6 +267,8 @@ typedef struct {
     const float *u; uint32_t ldu;   /* (dev) */
     void *out; uint32_t ldo;        /* (dev) */
     uint32_t flags;                 /* ENC_Y_F16 */
+    const float *out_col;           /* (dev) nullable, float [ff] */
+    float out_scale;
 } enc_act_desc;
 ENC_API enc_status enc_gated_act(enc_ctx *ctx, const enc_act_desc *desc, enc_stream stream);
 
@@ -309,13 +330,34 @@ typedef struct {
     float ple_scale;
     const float *ple_in, *ple_gate, *ple_proj; /* [n_ple][d], [n_ple][d], [d][n_ple] */
     const float *ple_in_norm_w, *ple_post_w;   /* [n_ple], [d] */
+    /* The int8 DiT block's row-op contract ([ZI] `Enc::block`, `Enc::rowop`,
+     * module doc "The chain"; sandwich block, NULL / 0 = off):
+     *  mod_*    adaLN modulation, f32 [d] each: the pre-norm outputs are
+     *           multiplied by (1 + mod_s_*), the residual updates by mod_g_*
+     *           (the block's [s_msa | g_msa | s_mlp | g_mlp]);
+     *  col_*    the q8_2f column field of each int8 weight, f32 [in]: the
+     *           weight is rs[j] q[j][k] col[k], and col is folded into the half
+     *           input by its producer (the row op writes q, k, v and w1/w3 their
+     *           own copy of A; the attention epilogue multiplies col_o; the
+     *           SwiGLU multiplies col_down; with col_gate/col_up the gate/up
+     *           GEMM runs unfused, z = 2, as on the page);
+     *  guard_*  [ZI] `Guards`, 0..14: each half site stores x 2^-guard and its
+     *           consumer multiplies 2^guard back (q/k/v input, panel, attention
+     *           output, w1/w3 input, SwiGLU hidden); the qk-norm's eps is scaled
+     *           by 2^-2 guard_qkv.  Int8 path only. */
+    const float *mod_s_attn, *mod_g_attn, *mod_s_ff, *mod_g_ff;
+    const float *col_q, *col_k, *col_v, *col_o, *col_gate, *col_up, *col_down;
+    uint32_t guard_attn, guard_qkv, guard_ao, guard_ffn, guard_hid;
 } enc_layer;
 
 /* The packed batch: `rows` rows, `nitems` disjoint items covering them, the
  * RoPE tables (dev, f32 [rows][hd/2] each; a layer rotates with table
  * rope_table; NULL where no layer uses it) and, for layers with a per-layer
  * input, the rows X0 that branch projects (dev, f32 [rows][d]; encoder_forward
- * takes its x when NULL, encoder_layer_forward needs it). */
+ * takes its x when NULL, encoder_layer_forward needs it).  amax (dev, nullable,
+ * f32 [nlayers][5], int8 path): each layer's max |stored half value| at its
+ * q/k/v input, panel, attention output, w1/w3 input and SwiGLU hidden, after
+ * the column fields and guards ([ZI] `amax`, the guard calibration). */
 #define ENC_MAX_ROPE_TABLES 4
 typedef struct {
     uint32_t rows;
@@ -323,6 +365,7 @@ typedef struct {
     uint32_t nitems;
     const float *rope_cos[ENC_MAX_ROPE_TABLES], *rope_sin[ENC_MAX_ROPE_TABLES];
     const float *ple_x;
+    float *amax;
 } enc_batch;
 
 /* All layers share d, path and block kind.  final: NONE -> out = H [rows][d];
@@ -338,7 +381,8 @@ typedef struct {
 } enc_model;
 
 /* Workspace bytes encoder_forward / encoder_layer_forward need for this batch
- * (its rows, and its items for the attention key splits).  0 on null input. */
+ * (its rows, its items for the attention key splits, and a little more when
+ * batch.amax is set).  0 on null input. */
 ENC_API size_t enc_workspace_bytes(const enc_model *model, const enc_batch *batch);
 
 /* One layer in place on h (dev, f32 [rows][d]), computing its own pre-norm. */

@@ -208,6 +208,17 @@ def test_dit_1056_full_width_layer_vs_oracle():
     assert err <= TOL_I8F16
 
 
+def test_dit_modulated_full_width_layer_vs_oracle():
+    """The modulated q8_2f DiT block with the Turbo guards at full width and rows
+    (1056 x 3840), one layer; every output row against the oracle."""
+    w = wl.make("zimage_dit_mod_1056", layers=1)
+    got = host(run(w))
+    err = row_rel_err(got, O.forward(w))
+    say(f"modulated DiT 1056 full-width layer: error {err:.2e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL_I8F16
+
+
 def test_dit_cfg_pair_full_stack_equals_singles():
     """C5 whole (8448 rows, 30 layers): each item of the CFG pair gets the bits of
     its own single forward (4224 rows); outputs finite."""

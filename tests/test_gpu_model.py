@@ -53,6 +53,8 @@ CASES = [
     # the vision tower: images of 20x20, 12x12, 9x9 and 3x3 patches (the first
     # two take the key split)
     ("gemma_vision_f32", dict(layers=2, lengths=[20, 12, 9, 3])),
+    # adaLN modulation, q8_2f column fields, the Turbo guards
+    ("zimage_dit_mod_1056", dict(layers=2, grid=8, ncap=8, overrides=DIT_SMALL)),
 ]
 
 
@@ -76,6 +78,7 @@ def test_forward_vs_oracle(name, kw):
     ("lfm2_vit_f32", dict(layers=2, overrides=dict(), lengths=[200])),
     ("zimage_dit_cfg_8448", dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)),
     ("gemma_text_ple_f32", dict(layers=3, lengths=[300, 77, 700], overrides=dict(global_every=2))),
+    ("zimage_dit_mod_1056", dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)),
 ])
 def test_fused_chain_equals_layer_by_layer(name, kw):
     """encoder_forward (each layer's last row op writes the next pre-norm) gives
@@ -121,16 +124,40 @@ def test_packed_images_equal_separate():
         r += g * g
 
 
-def test_cfg_pair_equals_two_singles():
+@pytest.mark.parametrize("name", ["zimage_dit_cfg_8448", "zimage_dit_mod_1056"])
+def test_cfg_pair_equals_two_singles(name):
     """The CFG batch-2 program gives each item the bits of its single forward."""
     kw = dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)
-    w = wl.make("zimage_dit_cfg_8448", cfg_pair=True, **kw)
+    w = wl.make(name, cfg_pair=True, **kw)
     pair = run(w)
     for i, rr in enumerate(w.items):
         idx = np.concatenate([np.arange(r0, r0 + n) for r0, n in rr])
-        single = wl.make("zimage_dit_cfg_8448", cfg_pair=False, **kw)
+        single = wl.make(name, cfg_pair=False, **kw)
         alone = run(single, x=w.x[idx])
         assert torch.equal(alone, pair[torch.from_numpy(idx).to(DEV)]), f"item {i}"
+
+
+def test_amax_per_site_vs_oracle():
+    """The guard calibration: each layer's max |stored half| at the five sites
+    (q/k/v input, panel, attention output, w1/w3 input, hidden), after the
+    column fields and guards, against the oracle's."""
+    w = wl.make("zimage_dit_mod_1056", layers=2, grid=8, ncap=8, overrides=DIT_SMALL)
+    dm = M.DeviceModel(w, DEV)
+    db = M.DeviceBatch(w, DEV)
+    am = torch.zeros((2, 5), dtype=torch.float32, device=DEV)
+    db.batch.amax = am.data_ptr()
+    X = torch.from_numpy(w.x).to(DEV)
+    out = torch.empty((w.rows, w.cfg["d"]), dtype=torch.float32, device=DEV)
+    ws = dm.workspace(db, DEV)
+    M.encoder_forward(dm, db, X, out, ws)
+    torch.cuda.synchronize()
+    ref = np.zeros((2, 5))
+    O.forward(w, amax=ref)
+    got = host(am)
+    say(f"amax gpu {got.tolist()}\n     oracle {ref.tolist()}")
+    assert np.all(np.abs(got - ref) <= TOL_I8F16 * ref)
+    # the same forward without recording gives the same output bits
+    assert torch.equal(out, run(w))
 
 
 def test_deterministic():

@@ -476,6 +476,93 @@ def test_rms_norm_prescale_and_add_norm_scalar():
     assert row_rel_err(host(H), ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("f16", [False, True])
+@pytest.mark.parametrize("with_t", [True, False])
+def test_row_op_modulation_column_fields_guard(f16, with_t):
+    """The int8 block's row op: h = h + gate * rms(t) w_post, then three copies
+    a_z = rms(h) w (1 + scale) col_z 2^-6 (the q/k/v inputs of a modulated
+    q8_2f block with its guard); with t = None only the pre-norm runs."""
+    rng = np.random.default_rng(21 + f16)
+    n, d = 130, 3840
+    h = rng.normal(0, 5, (n, d)).astype(np.float32)
+    t = rng.normal(0, 1, (n, d)).astype(np.float32)
+    vec = lambda m, sd: (m + sd * rng.normal(0, 1, d)).astype(np.float32)
+    w_post, w_next, gate, scale = vec(1, 0.02), vec(1, 0.02), vec(1, 0.1), vec(0, 0.1)
+    cols = [np.exp(0.25 * rng.normal(0, 1, d)).astype(np.float32) for _ in range(3)]
+    H = to_dev(h)
+    A = torch.empty((3, n, d), dtype=torch.float16 if f16 else torch.float32, device=DEV)
+    B.add_norm(H, to_dev(t) if with_t else None, to_dev(w_post) if with_t else None, 1e-6,
+               w_next=to_dev(w_next), a=A, f16=f16, gate=to_dev(gate) if with_t else None,
+               scale=to_dev(scale), cols=[to_dev(c) for c in cols], nout=3, oscale=2.0 ** -6)
+    hr = h.astype(np.float64)
+    if with_t:
+        hr = hr + O.rms_norm(t, w_post, 1e-6) * gate.astype(np.float64)
+    assert row_rel_err(host(H), hr) <= TOL_F32
+    base = O.rms_norm(hr, w_next, 1e-6) * (1.0 + scale.astype(np.float64))
+    for z in range(3):
+        ref = base * cols[z].astype(np.float64) * 2.0 ** -6
+        if f16:
+            ref = np.vectorize(O.round_f16)(ref)
+        assert row_rel_err(host(A[z]), ref) <= (TOL_I8F16 if f16 else TOL_F32), z
+
+
+@pytest.mark.parametrize("path,n,ff,d", [(B.ENC_I8F16, 520, 12800, 128), (B.ENC_I8F16, 77, 160, 80),
+                                         (B.ENC_F32, 300, 512, 256)])
+def test_gated_epilogue_column_field_and_guard(path, n, ff, d):
+    """The gated GEMM's y_col / y_scale (w2's column field, the hidden's guard)
+    equal the unfused gate/up GEMM + enc_gated_act with out_col / out_scale, bit
+    for bit, on the 256 x 256 direct-to-LDS, the register-staged and the f32
+    gated kernels."""
+    rng = np.random.default_rng(n + ff)
+    i8 = path == B.ENC_I8F16
+    if i8:
+        x = rng.normal(0, 1, (n, d)).astype(np.float16)
+        ws = [rng.integers(-127, 128, (ff, d)).astype(np.int8) for _ in range(2)]
+        rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, ff))).astype(np.float32)) for _ in range(2)]
+    else:
+        x = rng.normal(0, 1, (n, d)).astype(np.float32)
+        ws = [rng.normal(0, 0.05, (ff, d)).astype(np.float32) for _ in range(2)]
+        rs = None
+    col = to_dev(np.exp(0.25 * rng.normal(0, 1, ff)).astype(np.float32))
+    X, W = to_dev(x), [to_dev(w) for w in ws]
+    odt = torch.float16 if i8 else torch.float32
+    fused = torch.empty((n, ff), dtype=odt, device=DEV)
+    B.gemm_items(X, fused, W, [(n, ff, d, d, ff, 0, 0, 0)], path=path, row_scale=rs, alpha=2.0,
+                 flags=B.ENC_EPI_GATE_SILU | (B.ENC_Y_F16 if i8 else 0), y_col=col, y_scale=2.0 ** -6)
+    gu = torch.empty((n, 2 * ff), dtype=torch.float32, device=DEV)
+    B.gemm_items(X, gu, W, [(n, ff, d, d, 2 * ff, 0, 0, 0), (n, ff, d, d, 2 * ff, 1, 0, ff)],
+                 path=path, row_scale=rs, alpha=2.0)
+    unfused = torch.empty((n, ff), dtype=odt, device=DEV)
+    B.gated_act(gu[:, :ff], gu[:, ff:], unfused, B.ENC_ACT_SWIGLU, f16=i8, out_col=col,
+                out_scale=2.0 ** -6)
+    assert torch.equal(fused, unfused)
+
+
+@pytest.mark.parametrize("path,items,nq,hd", [(B.ENC_I8F16, [[(0, 300), (400, 40)], [(300, 100)]], 4, 128),
+                                              (B.ENC_I8F16, [[(0, 200)]], 4, 64),
+                                              (B.ENC_F32, [[(0, 1024)]], 12, 64),
+                                              (B.ENC_F32, [[(0, 100)], [(100, 50)]], 2, 128)])
+def test_attention_output_column_field_and_scale(path, items, nq, hd):
+    """out = o * out_scale * out_col (the O projection's column field and the
+    guards), in the attention epilogue and in the key-split merge."""
+    f16 = path == B.ENC_I8F16
+    rows = max(r0 + n for rr in items for r0, n in rr)
+    rng = np.random.default_rng(rows)
+    p = _panel(rng, rows, nq, nq, hd, f16=f16, qscale=0.5)
+    dt = torch.float16 if f16 else torch.float32
+    col = np.exp(0.25 * rng.normal(0, 1, nq * hd)).astype(np.float32)
+    out = torch.zeros((rows, nq * hd), dtype=dt, device=DEV)
+    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.1, 0, path=path, out_col=to_dev(col),
+                      out_scale=2.0)
+    q, k, v = _split(p, nq, nq, hd)
+    ref = O.attention(items, q, k, v, nq, nq, hd, 0.1, 0) * col.astype(np.float64) * 2.0
+    if f16:
+        ref = np.vectorize(O.round_f16)(ref)
+    got = host(out)
+    idx = np.concatenate([np.arange(r0, r0 + n) for rr in items for r0, n in rr])
+    assert row_rel_err(got[idx], ref[idx]) <= (TOL_I8F16 if f16 else TOL_F32)
+
+
 @pytest.mark.parametrize("hd,f16", [(64, False), (128, True)])
 def test_qk_norm_rope_with_v_norm(hd, f16):
     """With v_norm the v heads are RMS-normed without gain and not rotated; q and

@@ -50,7 +50,8 @@ class GemmItem(C.Structure):
 class GemmDesc(C.Structure):
     _fields_ = [("path", C.c_uint32), ("x", C.c_void_p), ("y", C.c_void_p),
                 ("w", C.c_void_p * 4), ("row_scale", C.c_void_p * 4), ("bias", C.c_void_p * 4),
-                ("alpha", C.c_float), ("flags", C.c_uint32)]
+                ("alpha", C.c_float), ("flags", C.c_uint32), ("y_col", C.c_void_p),
+                ("y_scale", C.c_float)]
 
 
 class Range(C.Structure):
@@ -67,7 +68,7 @@ class AttnDesc(C.Structure):
                 ("out", C.c_void_p), ("ldo", C.c_uint32), ("nq", C.c_uint32),
                 ("nkv", C.c_uint32), ("hd", C.c_uint32), ("scale", C.c_float),
                 ("window", C.c_uint32), ("rows", C.c_uint32), ("ws", C.c_void_p),
-                ("ws_bytes", C.c_size_t)]
+                ("ws_bytes", C.c_size_t), ("out_col", C.c_void_p), ("out_scale", C.c_float)]
 
 
 class NormDesc(C.Structure):
@@ -79,7 +80,9 @@ class NormDesc(C.Structure):
 class AddNormDesc(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("d", C.c_uint32), ("h", C.c_void_p), ("t", C.c_void_p),
                 ("w_post", C.c_void_p), ("w_next", C.c_void_p), ("eps", C.c_float),
-                ("a", C.c_void_p), ("flags", C.c_uint32), ("post", C.c_float)]
+                ("a", C.c_void_p), ("flags", C.c_uint32), ("post", C.c_float),
+                ("gate", C.c_void_p), ("scale", C.c_void_p), ("col", C.c_void_p * 3),
+                ("nout", C.c_uint32), ("oscale", C.c_float)]
 
 
 class QkDesc(C.Structure):
@@ -94,7 +97,8 @@ class QkDesc(C.Structure):
 class ActDesc(C.Structure):
     _fields_ = [("kind", C.c_uint32), ("rows", C.c_uint32), ("ff", C.c_uint32),
                 ("g", C.c_void_p), ("ldg", C.c_uint32), ("u", C.c_void_p), ("ldu", C.c_uint32),
-                ("out", C.c_void_p), ("ldo", C.c_uint32), ("flags", C.c_uint32)]
+                ("out", C.c_void_p), ("ldo", C.c_uint32), ("flags", C.c_uint32),
+                ("out_col", C.c_void_p), ("out_scale", C.c_float)]
 
 
 _LAYER_U32 = ["block", "path", "mlp", "d", "nq", "nkv", "hd", "ff", "window", "rope_sections"]
@@ -106,6 +110,9 @@ _LAYER_PTRS = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
 
 
 _LAYER_PLE_PTRS = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
+_LAYER_MOD_PTRS = ["mod_s_attn", "mod_g_attn", "mod_s_ff", "mod_g_ff"]
+_LAYER_COL_PTRS = ["col_q", "col_k", "col_v", "col_o", "col_gate", "col_up", "col_down"]
+_LAYER_GUARDS = ["guard_attn", "guard_qkv", "guard_ao", "guard_ffn", "guard_hid"]
 
 
 class Layer(C.Structure):
@@ -114,7 +121,8 @@ class Layer(C.Structure):
                 + [(n, C.c_void_p) for n in _LAYER_PTRS]
                 + [("v_norm", C.c_uint32), ("rope_table", C.c_uint32), ("scalar", C.c_float),
                    ("n_ple", C.c_uint32), ("ple_scale", C.c_float)]
-                + [(n, C.c_void_p) for n in _LAYER_PLE_PTRS])
+                + [(n, C.c_void_p) for n in _LAYER_PLE_PTRS + _LAYER_MOD_PTRS + _LAYER_COL_PTRS]
+                + [(n, C.c_uint32) for n in _LAYER_GUARDS])
 
 
 class ProfStat(C.Structure):
@@ -128,7 +136,7 @@ MAX_ROPE_TABLES = 4
 class Batch(C.Structure):
     _fields_ = [("rows", C.c_uint32), ("items", C.POINTER(Item)), ("nitems", C.c_uint32),
                 ("rope_cos", C.c_void_p * MAX_ROPE_TABLES), ("rope_sin", C.c_void_p * MAX_ROPE_TABLES),
-                ("ple_x", C.c_void_p)]
+                ("ple_x", C.c_void_p), ("amax", C.c_void_p)]
 
 
 class Model(C.Structure):
@@ -252,7 +260,7 @@ def context(device: int = 0) -> Context:
 # ------------------------------------------------------------------ ops
 
 def gemm_items(x, y, w, items, path=ENC_F32, row_scale=None, bias=None, alpha=1.0, flags=0,
-               ctx=None, stream=None):
+               y_col=None, y_scale=1.0, ctx=None, stream=None):
     """items: list of dicts/tuples (n, m, k, ldx, ldy, slot, x_off, y_off); w: list of tensors."""
     ctx = ctx or context()
     d = GemmDesc()
@@ -265,6 +273,8 @@ def gemm_items(x, y, w, items, path=ENC_F32, row_scale=None, bias=None, alpha=1.
         d.bias[s] = _ptr(bias[s]) if bias and s < len(bias) else None
     d.alpha = alpha
     d.flags = flags
+    d.y_col = _ptr(y_col)
+    d.y_scale = y_scale
     arr = (GemmItem * len(items))(*[GemmItem(*it) for it in items])
     ctx.check(lib().gemm_items(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
 
@@ -293,12 +303,13 @@ def attention_workspace_bytes(desc, items):
 
 def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_col=0,
                     k_col=None, v_col=None, ldo=None, path=ENC_F32, rows=None, ws="auto",
-                    ctx=None, stream=None):
+                    out_col=None, out_scale=1.0, ctx=None, stream=None):
     """ws: "auto" (a torch buffer of the size the key splits need), None (no
     split) or a uint8 device tensor."""
     ctx = ctx or context()
     d = attention_desc(qkv, out, nq, nkv, hd, scale, window, ld, q_col, k_col, v_col, ldo, path,
                        rows)
+    d.out_col, d.out_scale = _ptr(out_col), out_scale
     if isinstance(ws, str):
         import torch
         n = attention_workspace_bytes(d, items)
@@ -332,10 +343,17 @@ def layer_norm(x, w, b, eps, y, f16=False, ctx=None, stream=None):
     _norm(lib().enc_layer_norm, x, w, b, eps, y, f16, ctx, stream)
 
 
-def add_norm(h, t, w_post, eps, w_next=None, a=None, f16=False, post=1.0, ctx=None, stream=None):
+def add_norm(h, t, w_post, eps, w_next=None, a=None, f16=False, post=1.0, gate=None, scale=None,
+             cols=None, nout=1, oscale=1.0, ctx=None, stream=None):
+    """h = (h + gate rms(t) w_post) post (t may be None: no update); then with
+    w_next, `nout` copies a_z = rms(h) w_next (1 + scale) cols[z] oscale."""
     ctx = ctx or context()
     d = AddNormDesc()
     d.post = post
+    d.gate, d.scale = _ptr(gate), _ptr(scale)
+    for z, c in enumerate(cols or []):
+        d.col[z] = _ptr(c)
+    d.nout, d.oscale = nout, oscale
     d.rows, d.d = h.shape[0], h.shape[1]
     d.h, d.t, d.w_post, d.w_next, d.a = _ptr(h), _ptr(t), _ptr(w_post), _ptr(w_next), _ptr(a)
     d.eps = eps
@@ -362,9 +380,10 @@ def qk_norm_rope(panel, nq, nkv, hd, q_norm_w, k_norm_w, eps, cos, sin, sections
     ctx.check(lib().enc_qk_norm_rope(ctx.h, C.byref(d), _stream(stream)))
 
 
-def gated_act(g, u, out, kind, f16=False, ctx=None, stream=None):
+def gated_act(g, u, out, kind, f16=False, out_col=None, out_scale=1.0, ctx=None, stream=None):
     ctx = ctx or context()
     d = ActDesc()
+    d.out_col, d.out_scale = _ptr(out_col), out_scale
     d.kind, d.rows, d.ff = kind, g.shape[0], g.shape[1]
     d.g, d.ldg, d.u, d.ldu = _ptr(g), g.stride(0), _ptr(u), u.stride(0)
     d.out, d.ldo = _ptr(out), out.stride(0)

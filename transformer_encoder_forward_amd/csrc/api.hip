@@ -159,6 +159,8 @@ enc_status check_gemm(Err &e, const enc_gemm_desc *d, const enc_gemm_item *items
         if ((uint64_t)it.n * it.ldx > (1ull << 40) || (uint64_t)it.n * it.ldy > (1ull << 40))
             return e.set(ENC_ESHAPE, "gemm_items: item %u too large", i);
     }
+    if (!std::isfinite(d->y_scale) || !std::isfinite(d->alpha))
+        return e.set(ENC_EINVAL, "gemm_items: alpha or y_scale not finite");
     // Y regions of different items must not overlap (2-D rectangles when the
     // strides agree, else address intervals).
     for (uint32_t i = 0; i < n; i++)
@@ -191,6 +193,8 @@ void plan_gemm(const enc_gemm_desc *d, const enc_gemm_item *items, uint32_t n, G
     }
     g.alpha = d->alpha;
     g.flags = d->flags;
+    g.ycol = d->y_col;
+    g.yscale = d->y_scale == 0.0f ? 1.0f : d->y_scale;
     g.nitems = n;
     uint32_t tiles = 0;
     for (uint32_t i = 0; i < n; i++) {
@@ -340,8 +344,10 @@ enc_status check_attn(Err &e, const enc_attn_desc *d, const enc_item *items, uin
         return e.set(ENC_ESHAPE, "attention_items: ldo %u < nq*hd %u", d->ldo, d->nq * d->hd);
     if (!aligned(d->qkv, 16) || !aligned(d->out, 16))
         return e.set(ENC_EUNSUPPORTED, "attention_items: panel/output must be 16-byte aligned");
-    if (!(d->scale == d->scale) || std::isinf(d->scale))
-        return e.set(ENC_EINVAL, "attention_items: scale is not finite");
+    if (!(d->scale == d->scale) || std::isinf(d->scale) || !std::isfinite(d->out_scale))
+        return e.set(ENC_EINVAL, "attention_items: scale or out_scale is not finite");
+    if (d->out_col && !aligned(d->out_col, 16))
+        return e.set(ENC_EUNSUPPORTED, "attention_items: out_col must be 16-byte aligned");
     if (check_items(e, "attention_items", items, n, d->rows) != ENC_OK) return e.st;
     if (d->ws) {
         if (!aligned(d->ws, 256))
@@ -375,6 +381,8 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         a.window = d->window;
         a.part_o = part_o;
         a.part_ml = part_ml;
+        a.ocol = d->out_col;
+        a.oscale = d->out_scale == 0.0f ? 1.0f : d->out_scale;
         CombineArgs cb;
         memset(&cb, 0, sizeof cb);
         cb.part_o = part_o;
@@ -383,6 +391,8 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         cb.ldo = d->ldo;
         cb.nq = d->nq;
         cb.hd = d->hd;
+        cb.ocol = a.ocol;
+        cb.oscale = a.oscale;
         uint32_t k = 0, part = 0;
         double pairs = 0;
         for (size_t c = c0; c < std::min(order.size(), c0 + (size_t)kMaxAttnItems); c++, k++) {
@@ -442,12 +452,18 @@ enc_status check_norm(Err &e, const char *who, const enc_norm_desc *d) {
 
 enc_status check_add_norm(Err &e, const enc_add_norm_desc *d) {
     if (!d) return e.set(ENC_EINVAL, "enc_add_norm: null descriptor");
-    if (!d->h || !d->t || !d->w_post) return e.set(ENC_EINVAL, "enc_add_norm: null h, t or w_post");
+    if (!d->h) return e.set(ENC_EINVAL, "enc_add_norm: null h");
+    if (d->t && !d->w_post) return e.set(ENC_EINVAL, "enc_add_norm: null w_post");
+    if (!d->t && !d->w_next) return e.set(ENC_EINVAL, "enc_add_norm: neither t nor w_next");
     if (d->w_next && !d->a) return e.set(ENC_EINVAL, "enc_add_norm: w_next without an output");
+    if (d->nout > 3) return e.set(ENC_EINVAL, "enc_add_norm: nout %u (1..3)", d->nout);
+    if (!std::isfinite(d->oscale)) return e.set(ENC_EINVAL, "enc_add_norm: oscale is not finite");
+    for (const float *v : {d->gate, d->scale, d->col[0], d->col[1], d->col[2]})
+        if (v && !aligned(v, 16)) return e.set(ENC_EUNSUPPORTED, "enc_add_norm: vectors must be 16-byte aligned");
     if (d->flags & ~1u) return e.set(ENC_EINVAL, "enc_add_norm: unknown flags");
     if (d->d == 0 || d->d % 4 || d->d > 4096)
         return e.set(ENC_EUNSUPPORTED, "enc_add_norm: width %u (multiple of 4, <= 4096)", d->d);
-    if (!aligned(d->h, 16) || !aligned(d->t, 16) || !aligned(d->w_post, 16) ||
+    if (!aligned(d->h, 16) || (d->t && (!aligned(d->t, 16) || !aligned(d->w_post, 16))) ||
         (d->w_next && (!aligned(d->w_next, 16) || !aligned(d->a, 16))))
         return e.set(ENC_EUNSUPPORTED, "enc_add_norm: pointers must be 16-byte aligned");
     if (!std::isfinite(d->post)) return e.set(ENC_EINVAL, "enc_add_norm: post is not finite");
@@ -486,6 +502,8 @@ enc_status check_act(Err &e, const enc_act_desc *d) {
         return e.set(ENC_EUNSUPPORTED, "enc_gated_act: widths/strides multiples of 4, 16-byte pointers");
     if (d->ldg < d->ff || d->ldu < d->ff || d->ldo < d->ff)
         return e.set(ENC_ESHAPE, "enc_gated_act: stride below width");
+    if ((d->out_col && !aligned(d->out_col, 16)) || !std::isfinite(d->out_scale))
+        return e.set(ENC_EINVAL, "enc_gated_act: out_col 16-byte aligned, out_scale finite");
     return ENC_OK;
 }
 
@@ -502,7 +520,8 @@ hipError_t rows_ln(const NormArgs &n, bool f16, hipStream_t s) {
     return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_layer_norm(n, f16, s); });
 }
 hipError_t rows_add_norm(const AddNormArgs &a, bool f16, hipStream_t s) {
-    const double b = (double)a.rows * a.d * (12 + (a.w_next ? (f16 ? 2 : 4) : 0)) + 8.0 * a.d;
+    const double b = (double)a.rows * a.d * ((a.t ? 12 : 4) + (a.w_next ? (f16 ? 2 : 4) * a.nout : 0)) +
+                     8.0 * a.d;
     return prof_launch(ENC_CLASS_ROWS, s, 0, b, [&] { return launch_add_norm(a, f16, s); });
 }
 hipError_t rows_qk(const QkArgs &q, bool f16, hipStream_t s) {
@@ -543,9 +562,18 @@ hipError_t pool_items(const enc_item *items, uint32_t nitems, uint32_t rows, uin
 }
 
 struct WsPlan {
-    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, pin = 0, z = 0, total = 0;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, pin = 0, z = 0, gu = 0, amax = 0,
+           total = 0;
     size_t part_bytes = 0;
 };
+
+float p2(int e) { return ldexpf(1.0f, e); }
+
+// Copies of the attention input A the q/k/v GEMM reads (one per column field)
+// and of the FFN input the gate/up GEMM reads.
+uint32_t nout_attn(const enc_layer &L) { return (L.col_q || L.col_k || L.col_v) ? 3 : 1; }
+uint32_t nout_ff(const enc_layer &L) { return (L.col_gate || L.col_up) ? 2 : 1; }
+bool unfused_gate(const enc_layer &L) { return L.mlp != ENC_MLP_GELU_TANH && nout_ff(L) > 1; }
 
 // The attention descriptor of one layer over the batch's panel.
 enc_attn_desc layer_attn_desc(const enc_layer &L, uint32_t rows) {
@@ -569,11 +597,12 @@ enc_attn_desc layer_attn_desc(const enc_layer &L, uint32_t rows) {
 WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
     WsPlan p;
     const uint32_t rows = B->rows;
-    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, ple = 0;
+    size_t a = 0, panel = 0, att = 0, t = 0, part = 0, m = 0, h = 0, ple = 0, gu = 0;
     for (uint32_t l = 0; l < M->nlayers; l++) {
         const enc_layer &L = M->layers[l];
         const size_t esz = L.path == ENC_I8F16 ? 2 : 4;
-        a = std::max(a, (size_t)rows * L.d * esz);
+        a = std::max(a, (size_t)rows * L.d * esz * std::max(nout_attn(L), nout_ff(L)));
+        if (unfused_gate(L)) gu = std::max(gu, (size_t)rows * 2 * L.ff * 4);
         panel = std::max(panel, (size_t)rows * (L.nq + 2 * L.nkv) * L.hd * esz);
         att = std::max(att, (size_t)rows * L.nq * L.hd * esz);
         t = std::max(t, (size_t)rows * L.d * 4);
@@ -594,6 +623,8 @@ WsPlan plan_ws(const enc_model *M, const enc_batch *B) {
     p.h = off; off += up256(h);  // residual stream (out holds it when final is NONE)
     p.pin = off; off += up256(ple);  // per-layer input: normed projection of X0
     p.z = off; off += up256(ple);    // and its gate
+    p.gu = off; off += up256(gu);    // gate|up of an unfused gated MLP
+    p.amax = off; off += B->amax ? up256(kAmaxBlocks * 4) : 0;  // per-block maxima of the amax pass
     p.total = off;
     return p;
 }
@@ -627,6 +658,17 @@ enc_status check_layer(Err &e, uint32_t l, const enc_layer &L, const enc_layer &
         if (L.rope_table >= ENC_MAX_ROPE_TABLES)
             return e.set(ENC_EINVAL, "layer %u: rope_table %u", l, L.rope_table);
         if (!std::isfinite(L.scalar)) return e.set(ENC_EINVAL, "layer %u: scalar not finite", l);
+        const uint32_t gmax = std::max({L.guard_attn, L.guard_qkv, L.guard_ao, L.guard_ffn, L.guard_hid});
+        const bool cols = L.col_q || L.col_k || L.col_v || L.col_o || L.col_gate || L.col_up || L.col_down;
+        if (L.path != ENC_I8F16 && (gmax || cols))
+            return e.set(ENC_EUNSUPPORTED, "layer %u: column fields and guards are int8-path options", l);
+        if (gmax > 14) return e.set(ENC_EINVAL, "layer %u: guard above 14", l);
+        if (L.v_norm && L.guard_qkv)
+            return e.set(ENC_EUNSUPPORTED, "layer %u: v-norm takes no panel guard", l);
+        for (const float *v : {L.mod_s_attn, L.mod_g_attn, L.mod_s_ff, L.mod_g_ff, L.col_q, L.col_k, L.col_v,
+                               L.col_o, L.col_gate, L.col_up, L.col_down})
+            if (v && !aligned(v, 16))
+                return e.set(ENC_EUNSUPPORTED, "layer %u: modulation and column fields 16-byte aligned", l);
         if (L.n_ple) {
             if (L.path != ENC_F32)
                 return e.set(ENC_EUNSUPPORTED, "layer %u: the per-layer input runs the f32 path", l);
@@ -636,8 +678,10 @@ enc_status check_layer(Err &e, uint32_t l, const enc_layer &L, const enc_layer &
             if (!std::isfinite(L.ple_scale)) return e.set(ENC_EINVAL, "layer %u: ple_scale not finite", l);
         }
     } else {
-        if (L.v_norm || L.n_ple || (L.scalar != 0.0f && L.scalar != 1.0f) || L.rope_table)
-            return e.set(ENC_EUNSUPPORTED, "layer %u: v-norm, per-layer input and scalar are sandwich options", l);
+        if (L.v_norm || L.n_ple || (L.scalar != 0.0f && L.scalar != 1.0f) || L.rope_table || L.mod_s_attn ||
+            L.mod_g_attn || L.mod_s_ff || L.mod_g_ff)
+            return e.set(ENC_EUNSUPPORTED,
+                         "layer %u: v-norm, per-layer input, scalar and modulation are sandwich options", l);
         if (L.path == ENC_I8F16) return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block runs the f32 path", l);
         if (L.mlp != ENC_MLP_GELU_TANH)
             return e.set(ENC_EUNSUPPORTED, "layer %u: pre-LN block takes the GELU MLP", l);
@@ -669,6 +713,8 @@ enc_status check_model(Err &e, const enc_model *M, const enc_batch *B) {
         const enc_layer &L = M->layers[l];
         if (L.rope_sections && (!B->rope_cos[L.rope_table] || !B->rope_sin[L.rope_table]))
             return e.set(ENC_EINVAL, "layer %u: RoPE table %u missing", l, L.rope_table);
+        if (B->amax && L.path != ENC_I8F16)
+            return e.set(ENC_EUNSUPPORTED, "amax records the int8 path's half sites");
     }
     return ENC_OK;
 }
@@ -679,13 +725,14 @@ struct Bufs {
     void *part;
     size_t part_bytes;
     void *m;
-    float *h, *pin, *z;
+    float *h, *pin, *z, *gu, *amax;
 };
 
 Bufs carve(void *ws, const WsPlan &p) {
     char *b = (char *)ws;
     return Bufs{b + p.a, b + p.panel, b + p.att, (float *)(b + p.t), p.part_bytes ? b + p.part : nullptr,
-                p.part_bytes, b + p.m, (float *)(b + p.h), (float *)(b + p.pin), (float *)(b + p.z)};
+                p.part_bytes, b + p.m, (float *)(b + p.h), (float *)(b + p.pin), (float *)(b + p.z),
+                (float *)(b + p.gu), (float *)(b + p.amax)};
 }
 
 #define TRY(expr)                                                                               \
@@ -694,10 +741,72 @@ Bufs carve(void *ws, const WsPlan &p) {
         if (_h != hipSuccess) return _h;                                                        \
     } while (0)
 
-hipError_t pre_norm(const enc_layer &L, uint32_t rows, const float *h, void *a, hipStream_t s) {
-    NormArgs n{rows, L.d, L.d, L.d, h, L.norm1_w, L.norm1_b, L.eps, a};
+// What a sandwich row op writes after the residual update: the next GEMM's
+// half (or f32) inputs, A_z = rms(h) w (1 + scale) col_z 2^-guard.
+struct NextIn {
+    const float *w = nullptr, *scale = nullptr;
+    const float *col[3] = {nullptr, nullptr, nullptr};
+    uint32_t nout = 1;
+    float oscale = 1.0f;
+};
+
+// the q/k/v input of layer N
+NextIn attn_in(const enc_layer &N) {
+    NextIn r;
+    r.w = N.norm1_w;
+    r.scale = N.mod_s_attn;
+    r.nout = nout_attn(N);
+    if (r.nout > 1) {
+        r.col[0] = N.col_q;
+        r.col[1] = N.col_k;
+        r.col[2] = N.col_v;
+    }
+    r.oscale = p2(-(int)N.guard_attn);
+    return r;
+}
+
+// the gate/up (or up) input of layer L
+NextIn ff_in(const enc_layer &L) {
+    NextIn r;
+    r.w = L.norm2_w;
+    r.scale = L.mod_s_ff;
+    r.nout = nout_ff(L);
+    if (r.nout > 1) {
+        r.col[0] = L.col_gate;
+        r.col[1] = L.col_up;
+    }
+    r.oscale = p2(-(int)L.guard_ffn);
+    return r;
+}
+
+// The sandwich row op: with t, h = (h + gate rms(t) w_post) post; then the
+// next inputs `nx` (none when nx.w == NULL).
+hipError_t row_op(const enc_layer &L, uint32_t rows, float *h, const float *t, const float *w_post,
+                  const float *gate, float post, const NextIn &nx, void *a, bool f16, hipStream_t s) {
+    AddNormArgs an{rows, L.d, h, t, w_post, nx.w, L.eps, a, post};
+    an.gate = gate;
+    an.scale = nx.scale;
+    for (int z = 0; z < 3; z++) an.col[z] = nx.col[z];
+    an.nout = nx.nout;
+    an.oscale = nx.oscale;
+    an.a_stride = (uint64_t)rows * L.d;
+    return rows_add_norm(an, f16, s);
+}
+
+hipError_t pre_norm(const enc_layer &L, uint32_t rows, float *h, void *a, hipStream_t s) {
     const bool f16 = L.path == ENC_I8F16;
-    return L.block == ENC_SANDWICH_RMS ? rows_rms(n, f16, s) : rows_ln(n, f16, s);
+    if (L.block == ENC_SANDWICH_RMS)  // rms(h) of the same helpers as rms_norm: the same bits
+        return row_op(L, rows, h, nullptr, nullptr, nullptr, 1.0f, attn_in(L), a, f16, s);
+    NormArgs n{rows, L.d, L.d, L.d, h, L.norm1_w, L.norm1_b, L.eps, a};
+    return rows_ln(n, f16, s);
+}
+
+// max |x| of n halves into *out (the guard calibration of the int8 path)
+hipError_t amax_site(const void *x, uint64_t n, float *part, float *out, hipStream_t s) {
+    if (!out || !n) return hipSuccess;
+    AmaxArgs a{reinterpret_cast<const _Float16 *>(x), n, part,
+               (uint32_t)std::min<uint64_t>(kAmaxBlocks, std::max<uint64_t>(1, (n / 8 + 255) / 256)), out};
+    return prof_launch(ENC_CLASS_ROWS, s, 0, 2.0 * n, [&] { return launch_amax_f16(a, s); });
 }
 
 // The final RMS of a sandwich f32 stack is the last row op's next-norm output
@@ -732,18 +841,24 @@ hipError_t run_ple(const enc_layer &L, uint32_t rows, const float *x0, const flo
     return proj(b.z, np, L.ple_proj, d, b.t);
 }
 
-// One layer on h.  On entry, for the sandwich block, A holds rms(h; norm1)
-// (pre-LN computes its own LN).  On exit the last row op has written
-// A = rms(h; w_next) when w_next != NULL (sandwich only).
+// One layer on h.  On entry, for the sandwich block, A holds the layer's q/k/v
+// input(s) (pre-LN computes its own LN).  On exit the last row op has written
+// the next inputs `nx` (sandwich only; none when nx.w == NULL).  amax: this
+// layer's five slots, or NULL.
 hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, float *h, const Bufs &b,
-                     const float *w_next, hipStream_t s) {
+                     const NextIn &nx, float *amax, hipStream_t s) {
     const uint32_t rows = B->rows, d = L.d, hd = L.hd;
     const uint32_t qw = L.nq * hd, kw = L.nkv * hd, ld = qw + 2 * kw;
     const bool i8 = L.path == ENC_I8F16;
     const bool sandwich = L.block == ENC_SANDWICH_RMS;
+    const int ga = L.guard_attn, gq = L.guard_qkv, gao = L.guard_ao, gf = L.guard_ffn, gh = L.guard_hid;
+    const uint64_t rd = (uint64_t)rows * d;
     if (!sandwich) TRY(pre_norm(L, rows, h, b.a, s));
+    if (amax) TRY(amax_site(b.a, rd * nout_attn(L), b.amax, amax + 0, s));
 
-    // q|k|v projections: one launch, three items
+    // q|k|v projections: one launch, three items (each reading its own copy of
+    // A when the weights carry column fields); 2^(ga - gq): undo the input
+    // guard, apply the panel's
     {
         enc_gemm_desc g{};
         g.path = L.path;
@@ -752,26 +867,34 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
         g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
         g.row_scale[0] = L.sq; g.row_scale[1] = L.sk; g.row_scale[2] = L.sv;
         g.bias[0] = L.bq; g.bias[1] = L.bk; g.bias[2] = L.bv;
-        g.alpha = 1.0f;
+        g.alpha = p2(ga - gq);
         g.flags = i8 ? ENC_Y_F16 : 0;
+        const uint64_t xs = nout_attn(L) > 1 ? rd : 0;
         enc_gemm_item it[3] = {{rows, qw, d, d, ld, 0, 0, 0},
-                               {rows, kw, d, d, ld, 1, 0, qw},
-                               {rows, kw, d, d, ld, 2, 0, qw + kw}};
+                               {rows, kw, d, d, ld, 1, xs, qw},
+                               {rows, kw, d, d, ld, 2, 2 * xs, qw + kw}};
         TRY(run_gemm(&g, it, 3, s));
     }
+    if (amax) TRY(amax_site(b.panel, (uint64_t)rows * ld, b.amax, amax + 1, s));
     if (sandwich) {
+        // the panel holds x 2^-gq: eps 2^-2gq gives the norm of x exactly
         QkArgs q{b.panel, rows, ld, 0, qw, L.nq, L.nkv, hd, L.rope_sections, L.q_norm_w, L.k_norm_w,
-                 L.eps, B->rope_cos[L.rope_table], B->rope_sin[L.rope_table], qw + kw, L.v_norm};
+                 L.eps * p2(-2 * gq), B->rope_cos[L.rope_table], B->rope_sin[L.rope_table], qw + kw,
+                 L.v_norm};
         TRY(rows_qk(q, i8, s));
     }
     {
+        // v carried 2^-gq; the O projection reads att col_o 2^-gao
         enc_attn_desc a = layer_attn_desc(L, rows);
         a.qkv = b.panel;
         a.out = b.att;
         a.ws = b.part;
         a.ws_bytes = b.part_bytes;
+        a.out_col = L.col_o;
+        a.out_scale = p2(gq - gao);
         TRY(run_attention(&a, B->items, B->nitems, s));
     }
+    if (amax) TRY(amax_site(b.att, (uint64_t)rows * qw, b.amax, amax + 2, s));
     // output projection: sandwich -> T; pre-LN -> h += att Wo^T + bo
     {
         enc_gemm_desc g{};
@@ -781,19 +904,20 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
         g.w[0] = L.wo;
         g.row_scale[0] = L.so;
         g.bias[0] = L.bo;
-        g.alpha = 1.0f;
+        g.alpha = p2(gao);
         g.flags = sandwich ? 0 : ENC_Y_ACCUMULATE;
         enc_gemm_item it{rows, d, qw, qw, d, 0, 0, 0};
         TRY(run_gemm(&g, &it, 1, s));
     }
     if (sandwich) {
-        AddNormArgs an{rows, d, h, b.t, L.post_attn_w, L.norm2_w, L.eps, b.a};
-        TRY(rows_add_norm(an, i8, s));
+        TRY(row_op(L, rows, h, b.t, L.post_attn_w, L.mod_g_attn, 1.0f, ff_in(L), b.a, i8, s));
     } else {
         NormArgs n{rows, d, d, d, h, L.norm2_w, L.norm2_b, L.eps, b.a};
         TRY(rows_ln(n, false, s));
     }
-    // MLP
+    if (amax) TRY(amax_site(b.a, rd * nout_ff(L), b.amax, amax + 3, s));
+    // MLP; gate/up times 2^gf (the input guard); the hidden stores
+    // act(gate) up col_down 2^-gh for the down projection
     if (L.mlp == ENC_MLP_GELU_TANH) {
         enc_gemm_desc g{};
         g.path = L.path;
@@ -806,7 +930,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
         g.flags = ENC_EPI_GELU_TANH;
         enc_gemm_item it{rows, L.ff, d, d, L.ff, 0, 0, 0};
         TRY(run_gemm(&g, &it, 1, s));
-    } else {
+    } else if (!unfused_gate(L)) {
         // gate and up in one launch, act(gate) * up formed in the epilogue
         enc_gemm_desc g{};
         g.path = L.path;
@@ -814,12 +938,30 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
         g.y = b.m;
         g.w[0] = L.w_gate; g.w[1] = L.w_up;
         g.row_scale[0] = L.s_gate; g.row_scale[1] = L.s_up;
-        g.alpha = 1.0f;
+        g.alpha = p2(gf);
         g.flags = (L.mlp == ENC_MLP_GELU_TANH_GATED ? ENC_EPI_GATE_GELU_TANH : ENC_EPI_GATE_SILU) |
                   (i8 ? ENC_Y_F16 : 0u);
+        g.y_col = L.col_down;
+        g.y_scale = p2(-gh);
         enc_gemm_item it{rows, L.ff, d, d, L.ff, 0, 0, 0};
         TRY(run_gemm(&g, &it, 1, s));
+    } else {
+        // gate and up read their own copies of A (column fields): z = 2 into
+        // gate|up, then the gated activation
+        enc_gemm_desc g{};
+        g.path = L.path;
+        g.x = b.a;
+        g.y = b.gu;
+        g.w[0] = L.w_gate; g.w[1] = L.w_up;
+        g.row_scale[0] = L.s_gate; g.row_scale[1] = L.s_up;
+        g.alpha = p2(gf);
+        enc_gemm_item it[2] = {{rows, L.ff, d, d, 2 * L.ff, 0, 0, 0}, {rows, L.ff, d, d, 2 * L.ff, 1, rd, L.ff}};
+        TRY(run_gemm(&g, it, 2, s));
+        ActArgs act{L.mlp == ENC_MLP_GELU_TANH_GATED ? (uint32_t)ENC_ACT_GELU_TANH_GATED : (uint32_t)ENC_ACT_SWIGLU,
+                    rows, L.ff, 2 * L.ff, 2 * L.ff, L.ff, b.gu, b.gu + L.ff, b.m, L.col_down, p2(-gh)};
+        TRY(rows_act(act, i8, s));
     }
+    if (amax) TRY(amax_site(b.m, (uint64_t)rows * L.ff, b.amax, amax + 4, s));
     {
         enc_gemm_desc g{};
         g.path = L.path;
@@ -828,7 +970,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
         g.w[0] = L.w_down;
         g.row_scale[0] = L.s_down;
         g.bias[0] = L.b_down;
-        g.alpha = 1.0f;
+        g.alpha = p2(gh);
         g.flags = sandwich ? 0 : ENC_Y_ACCUMULATE;
         enc_gemm_item it{rows, d, L.ff, L.ff, d, 0, 0, 0};
         TRY(run_gemm(&g, &it, 1, s));
@@ -836,14 +978,11 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
     if (sandwich) {
         const float scalar = L.scalar == 0.0f ? 1.0f : L.scalar;
         if (!L.n_ple) {
-            AddNormArgs an{rows, d, h, b.t, L.post_ff_w, w_next, L.eps, b.a, scalar};
-            TRY(rows_add_norm(an, i8, s));
+            TRY(row_op(L, rows, h, b.t, L.post_ff_w, L.mod_g_ff, scalar, nx, b.a, i8, s));
         } else {
-            AddNormArgs an{rows, d, h, b.t, L.post_ff_w, nullptr, L.eps, nullptr, 1.0f};
-            TRY(rows_add_norm(an, false, s));
+            TRY(row_op(L, rows, h, b.t, L.post_ff_w, L.mod_g_ff, 1.0f, NextIn{}, nullptr, false, s));
             TRY(run_ple(L, rows, x0, h, b, s));
-            AddNormArgs pn{rows, d, h, b.t, L.ple_post_w, w_next, L.eps, b.a, scalar};
-            TRY(rows_add_norm(pn, false, s));
+            TRY(row_op(L, rows, h, b.t, L.ple_post_w, nullptr, scalar, nx, b.a, false, s));
         }
     }
     return hipSuccess;
@@ -989,6 +1128,12 @@ enc_status enc_add_norm(enc_ctx *ctx, const enc_add_norm_desc *d, enc_stream str
     if (check_add_norm(e, d) == ENC_OK) {
         AddNormArgs a{d->rows, d->d, d->h, d->t, d->w_post, d->w_next, d->eps, d->a,
                       d->post == 0.0f ? 1.0f : d->post};
+        a.gate = d->gate;
+        a.scale = d->scale;
+        for (int z = 0; z < 3; z++) a.col[z] = d->col[z];
+        a.nout = d->nout ? d->nout : 1;
+        a.oscale = d->oscale == 0.0f ? 1.0f : d->oscale;
+        a.a_stride = (uint64_t)d->rows * d->d;
         launch_status(e, rows_add_norm(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_add_norm");
     }
     return finish(ctx, e);
@@ -1011,7 +1156,8 @@ enc_status enc_gated_act(enc_ctx *ctx, const enc_act_desc *d, enc_stream stream)
     if (!ctx) return ENC_EINVAL;
     CtxScope cs(ctx);
     if (check_act(e, d) == ENC_OK) {
-        ActArgs a{d->kind, d->rows, d->ff, d->ldg, d->ldu, d->ldo, d->g, d->u, d->out};
+        ActArgs a{d->kind, d->rows, d->ff, d->ldg, d->ldu, d->ldo, d->g, d->u, d->out, d->out_col,
+                  d->out_scale == 0.0f ? 1.0f : d->out_scale};
         launch_status(e, rows_act(a, d->flags & ENC_Y_F16, (hipStream_t)stream), "enc_gated_act");
     }
     return finish(ctx, e);
@@ -1086,7 +1232,7 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
     hipStream_t s = (hipStream_t)stream;
     hipError_t hr = hipSuccess;
     if (layer->block == ENC_SANDWICH_RMS) hr = pre_norm(*layer, batch->rows, h, b.a, s);
-    if (hr == hipSuccess) hr = run_layer(*layer, batch, batch->ple_x, h, b, nullptr, s);
+    if (hr == hipSuccess) hr = run_layer(*layer, batch, batch->ple_x, h, b, NextIn{}, batch->amax, s);
     launch_status(e, hr, "encoder_layer_forward");
     return finish(ctx, e);
 }
@@ -1126,13 +1272,14 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
     if (h != x) hr = hipMemcpyAsync(h, x, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s);
     if (hr == hipSuccess && L0.block == ENC_SANDWICH_RMS) hr = pre_norm(L0, rows, h, b.a, s);
     for (uint32_t l = 0; l < model->nlayers && hr == hipSuccess; l++) {
-        const float *w_next = nullptr;
-        if (l + 1 < model->nlayers)
-            w_next = model->layers[l + 1].norm1_w;
-        else if (fused_final(model))
-            w_next = model->final_w;  // the final RMS (f32) written by the last row op
-        hr = run_layer(model->layers[l], batch, x0, h, b, L0.block == ENC_SANDWICH_RMS ? w_next : nullptr,
-                       s);
+        NextIn nx;
+        if (L0.block == ENC_SANDWICH_RMS) {
+            if (l + 1 < model->nlayers)
+                nx = attn_in(model->layers[l + 1]);
+            else if (fused_final(model))
+                nx.w = model->final_w;  // the final RMS (f32) written by the last row op
+        }
+        hr = run_layer(model->layers[l], batch, x0, h, b, nx, batch->amax ? batch->amax + 5 * l : nullptr, s);
     }
     if (hr == hipSuccess && model->final_kind == ENC_FINAL_LN) {
         NormArgs n{rows, d, d, d, h, model->final_w, model->final_b, model->final_eps, out};

@@ -225,9 +225,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
     for (int d = 0; d < HD / 32; d++)
 #pragma unroll
         for (int q = 0; q < 4; q++) {
+            const int ch = 32 * d + 8 * q + 4 * hf;
             f32x4 v = {o[d][4 * q] * inv, o[d][4 * q + 1] * inv, o[d][4 * q + 2] * inv,
                        o[d][4 * q + 3] * inv};
-            st4(out + 32 * d + 8 * q + 4 * hf, v);
+            st4(out + ch, out_scale(a, head * HD + ch, v));
         }
 }
 
@@ -267,6 +268,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombineArgs a) {
         const float inv = 1.0f / lsum;
 #pragma unroll
         for (int e = 0; e < 4; e++) acc[e] *= inv;
+        if (a.ocol) {
+            const f32x4 m = ld4(a.ocol + head * a.hd + 4 * ch);
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[e] *= m[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[e] *= a.oscale;
         const size_t off = (size_t)row_of(it, (int)t) * a.ldo + head * a.hd + 4 * ch;
         if (F16)
             st4h(reinterpret_cast<_Float16 *>(a.out) + off, acc);

@@ -32,6 +32,21 @@
 #include "kern.h"
 
 namespace enc {
+
+// The attention epilogue's output scale: out[c] = o[c] * oscale * ocol[c] for
+// the four channels c0.. (ocol nullable).  With oscale 1 and no ocol the value
+// is unchanged, bit for bit.
+__device__ __forceinline__ f32x4 out_scale(const AttnArgs &a, int c0, f32x4 v) {
+    if (a.ocol) {
+        const f32x4 m = ld4(a.ocol + c0);
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] *= m[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) v[e] *= a.oscale;
+    return v;
+}
+
 namespace attn {
 
 constexpr int KB = 32;  // keys per block
@@ -278,14 +293,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int ch = 32 * d + 8 * q + 4 * hf;
-                if constexpr (F16) {
-                    f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
-                               (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
-                    *reinterpret_cast<f16x4 *>(out + ch) = v;
-                } else {
-                    st4(out + ch, f32x4{o[d][4 * q] * inv, o[d][4 * q + 1] * inv, o[d][4 * q + 2] * inv,
-                                        o[d][4 * q + 3] * inv});
-                }
+                const f32x4 v = out_scale(a, head * HD + ch,
+                                          f32x4{o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
+                                                o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv});
+                if constexpr (F16)
+                    st4h(out + ch, v);
+                else
+                    st4(out + ch, v);
             }
     }
 }
@@ -475,9 +489,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int ch = 32 * d + 8 * q + 4 * hf;
-                f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
-                           (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
-                *reinterpret_cast<f16x4 *>(out + ch) = v;
+                st4h(out + ch, out_scale(a, head * HD + ch,
+                                         f32x4{o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
+                                               o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv}));
             }
     }
 }
@@ -693,9 +707,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const int ch = 32 * d + 8 * q + 4 * hf;
-                f16x4 v = {(_Float16)(o[d][4 * q] * inv), (_Float16)(o[d][4 * q + 1] * inv),
-                           (_Float16)(o[d][4 * q + 2] * inv), (_Float16)(o[d][4 * q + 3] * inv)};
-                *reinterpret_cast<f16x4 *>(out + ch) = v;
+                st4h(out + ch, out_scale(a, head * HD + ch,
+                                         f32x4{o[d][4 * q] * inv, o[d][4 * q + 1] * inv,
+                                               o[d][4 * q + 2] * inv, o[d][4 * q + 3] * inv}));
             }
     }
 }

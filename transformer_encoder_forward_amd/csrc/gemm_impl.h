@@ -135,6 +135,7 @@ __device__ __forceinline__ void store_block(const GemmArgs &a, const TileCtx &t,
     float mul = a.alpha;
     if (I8) mul *= t.rs[c];
     const float b = t.bias ? t.bias[c] : 0.0f;
+    const float oc = a.ycol ? a.ycol[c] : 1.0f;
     const bool f16 = a.flags & 1u, accum = a.flags & 2u, gelu = a.flags & 4u;
     const size_t base = t.it.y_off + c;
 #pragma unroll
@@ -143,6 +144,7 @@ __device__ __forceinline__ void store_block(const GemmArgs &a, const TileCtx &t,
         if (row >= (int)t.it.n) continue;
         float v = acc[r] * mul + b;
         if (gelu) v = gelu_tanh(v);
+        v = v * oc * a.yscale;  // exact when both are 1
         const size_t off = base + (size_t)row * t.it.ldy;
         if (f16) {
             reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
@@ -666,6 +668,7 @@ __global__ __launch_bounds__(64 * WGM * (BN / 64), MINB) void gemm_gated_kernel(
         mu *= ru[c];
     }
     const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
+    const float oc = a.ycol ? a.ycol[c] : 1.0f;
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(64 * WGM * (BN / 64), MINB) void gemm_gated_kernel(
             const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
             if (row >= n) continue;
             const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
-            const float v = (gelu ? gelu_tanh(g) : silu(g)) * u;
+            const float v = (gelu ? gelu_tanh(g) : silu(g)) * u * oc * a.yscale;
             const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
             if (f16)
                 reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
@@ -902,6 +905,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
         const int c = t.col0 + wc * 32 + li;
         if (c < m) {
             const float mg = a.alpha * rg[c], mu = a.alpha * ru[c];
+            const float oc = a.ycol ? a.ycol[c] : 1.0f;
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -909,7 +913,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
                     const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                     if (row >= n) continue;
                     const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
-                    const float v = (gelu ? gelu_tanh(g) : silu(g)) * u;
+                    const float v = (gelu ? gelu_tanh(g) : silu(g)) * u * oc * a.yscale;
                     const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
                     if (f16)
                         reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;

@@ -26,6 +26,8 @@ struct GemmArgs {
     uint32_t flags;
     uint32_t nitems;
     uint32_t total_tiles;
+    const float *ycol;     // per output column multiplier of the stored value (nullable)
+    float yscale;          // and a scale of every stored value (a power-of-two guard)
     GemmItemK items[kMaxGemmItems];
 };
 
@@ -48,6 +50,8 @@ struct AttnArgs {
     uint32_t nitems, ntiles;
     float *part_o;   // [records][hd] unnormalised outputs of split items
     float *part_ml;  // [records][2] running max (base 2) and sum
+    const float *ocol;   // output channel multiplier [nq*hd] (nullable)
+    float oscale;        // output scale
     AttnItemK items[kMaxAttnItems];
 };
 
@@ -56,6 +60,8 @@ struct CombineArgs {
     const float *part_o, *part_ml;
     void *out;
     uint32_t ldo, nq, hd, nitems;
+    const float *ocol;
+    float oscale;
     uint32_t row0[kMaxAttnItems + 1];  // prefix of item lengths over the split items
     AttnItemK items[kMaxAttnItems];
 };
@@ -70,6 +76,9 @@ struct NormArgs {
     float pre = 1.0f;  // RMSNorm of pre * x (1 = plain)
 };
 
+// Row op of the sandwich block: with t, h = (h + gate * rms(t) w_post) * post;
+// then with w_next, for z < nout: a_z = rms(h) w_next (1 + scale) col_z oscale
+// (a_z at a + z * a_stride elements).  gate, scale, col_z nullable.
 struct AddNormArgs {
     uint32_t rows, d;
     float *h;
@@ -78,7 +87,12 @@ struct AddNormArgs {
     const float *w_next;
     float eps;
     void *a;
-    float post = 1.0f;  // h = (h + rms(t) w_post) * post
+    float post = 1.0f;
+    const float *gate = nullptr, *scale = nullptr;
+    const float *col[3] = {nullptr, nullptr, nullptr};
+    uint32_t nout = 1;
+    float oscale = 1.0f;
+    uint64_t a_stride = 0;
 };
 
 struct QkArgs {
@@ -94,6 +108,18 @@ struct ActArgs {
     uint32_t kind, rows, ff, ldg, ldu, ldo;
     const float *g, *u;
     void *out;
+    const float *ocol = nullptr;  // per column multiplier of the stored value
+    float oscale = 1.0f;
+};
+
+// Max |x| over n halves: per-block maxima into part[blocks], then one block
+// reduces them into *out.
+struct AmaxArgs {
+    const _Float16 *x;
+    uint64_t n;
+    float *part;
+    uint32_t blocks;
+    float *out;
 };
 
 struct PoolArgs {
@@ -115,6 +141,8 @@ hipError_t launch_add_norm(const AddNormArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_qk_norm_rope(const QkArgs &a, bool f16, hipStream_t s);
 hipError_t launch_gated_act(const ActArgs &a, bool f16_out, hipStream_t s);
 hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s);
+hipError_t launch_amax_f16(const AmaxArgs &a, hipStream_t s);
+constexpr uint32_t kAmaxBlocks = 512;
 hipError_t launch_mfma_peak(bool f16, uint32_t blocks, uint32_t iters, float *out, hipStream_t s);
 
 // Tile sizes the launchers and the planner agree on.

@@ -138,26 +138,62 @@ __global__ __launch_bounds__(256) void layer_norm_kernel(NormArgs a) {
         store_row(y, reinterpret_cast<float *>(a.y) + (size_t)row * a.ldy, false, a.d, lane);
 }
 
+// y[c] *= v[c] (+ add) for the row slots of this lane
+template <int NV>
+__device__ __forceinline__ void mul_cols(Row<NV> &y, const float *v, float add, int d, int lane) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+        const int c = (i * 64 + lane) * 4;
+        const f32x4 m = c < d ? ld4(v + c) : f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; e++) y.v[i][e] *= m[e] + add;
+    }
+}
+
 template <int NV, bool F16>
 __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (row >= (int)a.rows) return;
     const size_t off = (size_t)row * a.d;
-    Row<NV> t, h;
-    load_row(t, a.t + off, a.d, lane);
+    Row<NV> h;
     load_row(h, a.h + off, a.d, lane);
-    const float inv_t = rms_inv(t, a.d, a.eps);
-    const Row<NV> tn = rms_apply(t, inv_t, a.w_post, a.d, lane);
+    if (a.t) {
+        Row<NV> t;
+        load_row(t, a.t + off, a.d, lane);
+        const float inv_t = rms_inv(t, a.d, a.eps);
+        Row<NV> tn = rms_apply(t, inv_t, a.w_post, a.d, lane);
+        if (a.gate) mul_cols(tn, a.gate, 0.0f, a.d, lane);
 #pragma unroll
-    for (int i = 0; i < NV; i++) h.v[i] = (h.v[i] + tn.v[i]) * a.post;  // exact when post == 1
-    store_row(h, a.h + off, false, a.d, lane);
+        for (int i = 0; i < NV; i++) h.v[i] = (h.v[i] + tn.v[i]) * a.post;  // exact when post == 1
+        store_row(h, a.h + off, false, a.d, lane);
+    }
     if (a.w_next) {
         const float inv_h = rms_inv(h, a.d, a.eps);
-        const Row<NV> y = rms_apply(h, inv_h, a.w_next, a.d, lane);
-        if (F16)
-            store_row(y, reinterpret_cast<_Float16 *>(a.a) + off, true, a.d, lane);
-        else
-            store_row(y, reinterpret_cast<float *>(a.a) + off, false, a.d, lane);
+        Row<NV> y = rms_apply(h, inv_h, a.w_next, a.d, lane);
+        if (a.scale) mul_cols(y, a.scale, 1.0f, a.d, lane);  // adaLN: times (1 + s)
+        // copy z = y col_z oscale, formed slot by slot as it is stored (no
+        // second register row)
+        for (uint32_t z = 0; z < a.nout; z++) {
+            const float *col = a.col[z];
+            const size_t zo = off + z * a.a_stride;
+#pragma unroll
+            for (int i = 0; i < NV; i++) {
+                const int c = (i * 64 + lane) * 4;
+                if (c >= (int)a.d) continue;
+                f32x4 v = y.v[i];
+                if (col) {
+                    const f32x4 m = ld4(col + c);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v[e] *= m[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) v[e] *= a.oscale;  // a power of two: exact
+                if (F16)
+                    st4h(reinterpret_cast<_Float16 *>(a.a) + zo + c, v);
+                else
+                    st4(reinterpret_cast<float *>(a.a) + zo + c, v);
+            }
+        }
     }
 }
 
@@ -265,6 +301,13 @@ __global__ __launch_bounds__(256) void gated_act_kernel(ActArgs a) {
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = (a.kind == 1 ? gelu_tanh(g[e]) : silu(g[e])) * u[e];
+        if (a.ocol) {
+            const f32x4 m = ld4(a.ocol + c);
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] *= m[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] *= a.oscale;
         if (F16)
             st4h(reinterpret_cast<_Float16 *>(a.out) + r * a.ldo + c, o);
         else
@@ -298,6 +341,35 @@ __global__ __launch_bounds__(256) void mean_pool_kernel(PoolArgs a) {
                 (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / (float)L;
         __syncthreads();
     }
+}
+
+// Max |x| of a half buffer: pass 1 (blocks of 256) writes one maximum per
+// block, pass 2 (one block) reduces them.  Max is order-free: deterministic.
+__global__ __launch_bounds__(256) void amax_part_kernel(AmaxArgs a) {
+    __shared__ float red[4];
+    float m = 0.0f;
+    const uint64_t n8 = a.n / 8;
+    for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (uint64_t)gridDim.x * 256) {
+        const f16x8 v = reinterpret_cast<const f16x8 *>(a.x)[i];
+#pragma unroll
+        for (int e = 0; e < 8; e++) m = fmaxf(m, fabsf((float)v[e]));
+    }
+    for (uint64_t i = n8 * 8 + (uint64_t)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (uint64_t)gridDim.x * 256)
+        m = fmaxf(m, fabsf((float)a.x[i]));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) a.part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void amax_final_kernel(AmaxArgs a) {
+    __shared__ float red[4];
+    float m = 0.0f;
+    for (uint32_t i = threadIdx.x; i < a.blocks; i += 256) m = fmaxf(m, a.part[i]);
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) *a.out = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 }  // namespace
@@ -376,6 +448,13 @@ hipError_t launch_gated_act(const ActArgs &a, bool f16, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 256 * 64);
     if (f16) hipLaunchKernelGGL(gated_act_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(gated_act_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_f16(const AmaxArgs &a, hipStream_t s) {
+    if (!a.n || !a.blocks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(amax_part_kernel, dim3(a.blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

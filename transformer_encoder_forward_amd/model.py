@@ -19,6 +19,8 @@ _F32_NAMES = ["bq", "bk", "bv", "bo", "b_up", "b_down", "norm1_w", "norm1_b", "n
               "sq", "sk", "sv", "so", "s_gate", "s_up", "s_down"]
 _W_NAMES = ["wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"]
 _PLE_NAMES = ["ple_in", "ple_gate", "ple_proj", "ple_in_norm_w", "ple_post_w"]
+_MOD_COL_NAMES = ["mod_s_attn", "mod_g_attn", "mod_s_ff", "mod_g_ff",
+                  "col_q", "col_k", "col_v", "col_o", "col_gate", "col_up", "col_down"]
 
 
 def rope_bases(w: wl.Workload) -> list:
@@ -65,7 +67,11 @@ class DeviceModel:
                     dev = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
                 self.keep.append(dev)
                 setattr(L, n, dev.data_ptr())
-            for n in _F32_NAMES + _PLE_NAMES:
+            guards = t.get("guards", cfg.get("guards"))
+            if guards:
+                for n, g in zip(B._LAYER_GUARDS, guards):
+                    setattr(L, n, int(g))
+            for n in _F32_NAMES + _PLE_NAMES + _MOD_COL_NAMES:
                 if t.get(n) is not None:
                     dev = torch.from_numpy(np.ascontiguousarray(t[n], np.float32)).to(device)
                     self.keep.append(dev)
