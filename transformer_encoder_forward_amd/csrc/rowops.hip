@@ -198,12 +198,48 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
 }
 
 // One wave per row over all of its nq q heads and nkv k heads (and, with
-// v_norm, its nkv v heads: weightless RMS, no rotation).  A head is held
-// by LH = hd / VE lanes, each owning VE consecutive channels (one 16-byte
-// vector: 4 f32 or 8 f16), so a wave covers 64 / LH heads per pass with fully
+// v_norm, its nkv v heads: weightless RMS, no rotation).  A head is held by
+// LH = hd / VE lanes, each owning VE consecutive channels (one 16-byte vector:
+// 4 f32 or 8 f16), so a wave covers 64 / LH heads per pass with fully
 // coalesced loads.  The per-head RMS is a butterfly inside the LH-lane group;
 // the rotate_half partner of channel c (c +- S/2) sits (S/2)/VE lanes away, in
-// the same vector slot.
+// the same vector slot.  A lane's channels are the same in every head, so its
+// norm gains and cos/sin are loaded once; the next pass's vector is loaded
+// before the current one is processed.
+template <int HD, bool F16>
+__device__ __forceinline__ void qk_load(const QkArgs &a, uint32_t row, uint32_t col, int c0, bool valid,
+                                        float (&x)[F16 ? 8 : 4]) {
+    constexpr int VE = F16 ? 8 : 4;
+    if (!valid) {
+#pragma unroll
+        for (int e = 0; e < VE; e++) x[e] = 0.0f;
+    } else if (F16) {
+        const f16x8 v = *reinterpret_cast<const f16x8 *>(
+            reinterpret_cast<const _Float16 *>(a.panel) + (size_t)row * a.ld + col + c0);
+#pragma unroll
+        for (int e = 0; e < VE; e++) x[e] = (float)v[e % 8];
+    } else {
+        const f32x4 v = ld4(reinterpret_cast<const float *>(a.panel) + (size_t)row * a.ld + col + c0);
+#pragma unroll
+        for (int e = 0; e < VE; e++) x[e] = v[e % 4];
+    }
+}
+
+template <int HD, bool F16>
+__device__ __forceinline__ void qk_store(const QkArgs &a, uint32_t row, uint32_t col, int c0,
+                                         const float (&x)[F16 ? 8 : 4]) {
+    constexpr int VE = F16 ? 8 : 4;
+    if (F16) {
+        f16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = (_Float16)x[e % VE];
+        *reinterpret_cast<f16x8 *>(reinterpret_cast<_Float16 *>(a.panel) + (size_t)row * a.ld + col + c0) = v;
+    } else {
+        st4(reinterpret_cast<float *>(a.panel) + (size_t)row * a.ld + col + c0,
+            f32x4{x[0], x[1 % VE], x[2 % VE], x[3 % VE]});
+    }
+}
+
 template <int HD, bool F16>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     constexpr int VE = F16 ? 8 : 4;
@@ -213,13 +249,12 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     const int lane = threadIdx.x & 63;
     if (row >= a.rows) return;
     const int hsub = lane / LH, c0 = (lane % LH) * VE;
-    const uint32_t heads = a.nq + a.nkv + (a.v_norm ? a.nkv : 0);
     const int S = a.sections ? HD / (int)a.sections : HD, half = S / 2;
     const int s_idx = c0 / S, i0 = c0 % S;
     const bool first = i0 < half;
     const int ti = s_idx * half + (first ? i0 : i0 - half);
     const int pmask = half / VE;  // partner lane distance (power of two)
-    float cs[VE], sn[VE];
+    float cs[VE], sn[VE], wq[VE], wk[VE];
     if (a.sections) {
         const float *cp = a.cos + (size_t)row * (HD / 2) + ti;
         const float *sp = a.sin + (size_t)row * (HD / 2) + ti;
@@ -229,42 +264,37 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
             sn[e] = sp[e];
         }
     }
+#pragma unroll
+    for (int e = 0; e < VE; e++) {
+        wq[e] = a.qw[c0 + e];
+        wk[e] = a.kw[c0 + e];
+    }
+    // heads in order: q, k, then (v_norm) v; group g of HP heads is one pass
+    const uint32_t nqk = a.nq + a.nkv, heads = nqk + (a.v_norm ? a.nkv : 0);
+    auto col_of = [&](uint32_t hh) -> uint32_t {
+        return hh < a.nq ? a.q_col + hh * HD
+                         : hh < nqk ? a.k_col + (hh - a.nq) * HD : a.v_col + (hh - nqk) * HD;
+    };
+    float xn[VE];
+    qk_load<HD, F16>(a, row, col_of(hsub), c0, (uint32_t)hsub < heads, xn);
     for (uint32_t h0 = 0; h0 < heads; h0 += HP) {
         const uint32_t hh = h0 + hsub;
-        const bool valid = hh < heads;
-        const bool isq = hh < a.nq, isv = hh >= a.nq + a.nkv;
-        const uint32_t col = isq ? a.q_col + hh * HD
-                                 : isv ? a.v_col + (hh - a.nq - a.nkv) * HD : a.k_col + (hh - a.nq) * HD;
-        const float *w = isq ? a.qw : a.kw;
+        const bool valid = hh < heads, isv = hh >= nqk;
         float x[VE];
-        if (valid) {
-            if (F16) {
-                const f16x8 v = *reinterpret_cast<const f16x8 *>(
-                    reinterpret_cast<const _Float16 *>(a.panel) + (size_t)row * a.ld + col + c0);
 #pragma unroll
-                for (int e = 0; e < VE; e++) x[e] = (float)v[e % 8];
-            } else {
-                const f32x4 v = ld4(reinterpret_cast<const float *>(a.panel) + (size_t)row * a.ld + col + c0);
-#pragma unroll
-                for (int e = 0; e < VE; e++) x[e] = v[e % 4];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < VE; e++) x[e] = 0.0f;
-        }
+        for (int e = 0; e < VE; e++) x[e] = xn[e];
+        if (h0 + HP < heads) qk_load<HD, F16>(a, row, col_of(hh + HP), c0, hh + HP < heads, xn);
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < VE; e++) ss = fmaf(x[e], x[e], ss);
 #pragma unroll
         for (int o = LH / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
         const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
-        if (valid) {
+        const bool isq = hh < a.nq;
 #pragma unroll
-            for (int e = 0; e < VE; e++) x[e] = isv ? x[e] * inv : x[e] * inv * w[c0 + e];
-        }
-        // the v heads come last: a pass of them is wave-uniform in isv except
-        // for its k/v boundary, where the rotated value of a v lane is dropped
+        for (int e = 0; e < VE; e++) x[e] = isv ? x[e] * inv : x[e] * inv * (isq ? wq[e] : wk[e]);
         if (a.sections) {
+            // every lane takes part in the exchange; v heads keep their value
             float y[VE];
 #pragma unroll
             for (int e = 0; e < VE; e++) {
@@ -275,17 +305,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
 #pragma unroll
                 for (int e = 0; e < VE; e++) x[e] = y[e];
         }
-        if (valid) {
-            if (F16) {
-                f16x8 v;
-#pragma unroll
-                for (int e = 0; e < 8; e++) v[e] = (_Float16)x[e % VE];
-                *reinterpret_cast<f16x8 *>(reinterpret_cast<_Float16 *>(a.panel) + (size_t)row * a.ld + col + c0) = v;
-            } else {
-                st4(reinterpret_cast<float *>(a.panel) + (size_t)row * a.ld + col + c0,
-                    f32x4{x[0], x[1 % VE], x[2 % VE], x[3 % VE]});
-            }
-        }
+        if (valid) qk_store<HD, F16>(a, row, col_of(hh), c0, x);
     }
 }
 
