@@ -76,21 +76,36 @@ def main():
     t0 = time.time()
     w = wl.make(args.workload, layers=args.layers, lazy_int8=True)
     cfg = w.cfg
-    dm = M.DeviceModel(w, dev)
-    db = M.DeviceBatch(w, dev)
     x = torch.from_numpy(w.x).to(dev)
     out = torch.empty((M.out_rows(w), cfg["d"]), dtype=torch.float32, device=dev)
-    ws = dm.workspace(db, dev)
+    ctx = B.context(0)
+    stream = torch.cuda.current_stream()
+    if w.stages:
+        # a staged DiT program: the context refiner runs once (per prompt) on the
+        # caption rows; a step is the noise refiner + the main stack
+        pre = M.DeviceProgram(w, dev, skip=("noise refiner", "main"))
+        prog = M.DeviceProgram(w, dev, skip=("context refiner",))
+        ws = torch.empty(max(pre.workspace_bytes(), prog.workspace_bytes()), dtype=torch.uint8,
+                         device=dev)
+        if pre.parts:
+            x0 = x.clone()
+            M.stages_forward(pre, x0, x, ws, ctx=ctx, stream=stream)
+        timed = [st for lab, st, _ in w.stages if lab != "context refiner"]
+    else:
+        dm = M.DeviceModel(w, dev)
+        db = M.DeviceBatch(w, dev)
+        ws = dm.workspace(db, dev)
+        timed = [w]
     torch.cuda.synchronize()
     setup_s = time.time() - t0
     print(f"[bench] {args.workload}: rows={w.rows} items={len(w.items)} layers={cfg['layers']} "
           f"setup {setup_s:.1f}s", file=sys.stderr, flush=True)
 
-    ctx = B.context(0)
-    stream = torch.cuda.current_stream()
-
     def step():
-        M.encoder_forward(dm, db, x, out, ws, ctx=ctx, stream=stream)
+        if w.stages:
+            M.stages_forward(prog, x, out, ws, ctx=ctx, stream=stream)
+        else:
+            M.encoder_forward(dm, db, x, out, ws, ctx=ctx, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -107,8 +122,8 @@ def main():
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     assert torch.isfinite(out).all().item(), "non-finite output"
 
-    gflop = wl.gemm_flops(w)
-    aflop = wl.attn_flops(w)
+    gflop = sum(wl.gemm_flops(st) for st in timed)
+    aflop = sum(wl.attn_flops(st) for st in timed)
     tflops = (gflop + aflop) / (ms * 1e-3) / 1e12
     dtype = "f32" if cfg["path"] == wl.PATH_F32 else "i8f16"
     peak = PEAK[dtype]
@@ -173,13 +188,18 @@ def main():
         "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
         "measured_mfma_peak": round(measured_peak, 1),
         "pct_of_measured_peak": round(100.0 * tflops / measured_peak, 2),
-        "tokens_per_s_per_layer": round(w.rows / (ms * 1e-3 / cfg["layers"]), 1),
+        "tokens_per_s_per_layer": round(sum(st.rows * st.cfg["layers"] for st in timed) / (ms * 1e-3), 1),
         "config": {"workload": args.workload, "rows": w.rows, "items": len(w.items),
                    "layers": cfg["layers"], "d": cfg["d"], "heads": f"{cfg['nq']}x{cfg['hd']}",
                    "kv_heads": cfg["nkv"], "ff": cfg["ff"], "window": cfg["window"],
                    **({"global_every": cfg["global_every"]} if cfg.get("global_every") else {}),
                    **({"v_norm": True} if cfg.get("v_norm") else {}),
                    **({"n_ple": cfg["n_ple"]} if cfg.get("n_ple") else {}),
+                   **({"modulated": True} if cfg.get("modulated") else {}),
+                   **({"guards": cfg["guards"]} if cfg.get("guards") else {}),
+                   **({"step_stages": [f"{lab}: {st.cfg['layers']} layers x {st.rows} rows"
+                                       for lab, st, _ in w.stages if lab != "context refiner"]}
+                      if w.stages else {}),
                    "gemm_gflop": round(gflop / 1e9, 2), "attn_gflop": round(aflop / 1e9, 2),
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "GEMM class: gemm_kernel + gemm_gated_kernel ("

@@ -398,6 +398,25 @@ ENC_API enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const e
                            const float *x, float *out, void *ws, size_t ws_bytes,
                            enc_stream stream);
 
+/* A staged program ([ZI] `step`: the noise refiner blocks over the image rows
+ * of every item, the caption rows copied in, then the main stack over all
+ * rows; `refine_caption`: the unmodulated context refiner over the caption
+ * rows).  Stage i runs its model's layers in place on rows [row0, row0 +
+ * batch.rows) of the residual h, its batch's items and tables relative to row0;
+ * with the rows of a packed batch in place ([img0 | img1 | cap0 | cap1]) no
+ * row moves.  Every stage's final is ENC_FINAL_NONE; all share one width.
+ * h (dev, f32 [rows][d]) starts as a copy of x (or is x). */
+typedef struct {
+    const enc_model *model; /* (host) */
+    enc_batch batch;
+    uint32_t row0;
+} enc_stage;
+
+ENC_API size_t enc_stages_workspace_bytes(const enc_stage *stages, uint32_t nstages);
+ENC_API enc_status encoder_stages_forward(enc_ctx *ctx, const enc_stage *stages, uint32_t nstages,
+                                          uint32_t rows, const float *x, float *h, void *ws,
+                                          size_t ws_bytes, enc_stream stream);
+
 /* --------------------------------------------------------- per-class timing */
 
 /* Launch classes ([EG] `Rec` and [ZI] `Rec`: one GPU time per op class under a

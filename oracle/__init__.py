@@ -111,6 +111,9 @@ def _setup(L):
     L.or_attention_rows.argtypes = L.or_attention.argtypes + [_I8]
     L.or_encoder_forward.argtypes = [C.POINTER(Model), C.c_int64, C.c_int, C.POINTER(Item), _D,
                                      _D, C.c_int, _D]
+    L.or_encoder_forward_pos.argtypes = [C.POINTER(Model), C.c_int64, C.c_int, C.POINTER(Item),
+                                         _I32, _D, _D, C.c_int, _D]
+    L.or_encoder_forward_pos.restype = None
     for f in ("or_rms_norm", "or_layer_norm", "or_linear", "or_linear_q8", "or_positions",
               "or_qk_norm_rope", "or_attention", "or_attention_rows", "or_encoder_forward"):
         getattr(L, f).restype = None
@@ -277,10 +280,11 @@ def _layer_struct(cfg, t, keep):
     return L
 
 
-def forward(w, layers=None, f16_sites: bool = True, x=None, amax=None):
+def forward(w, layers=None, f16_sites: bool = True, x=None, amax=None, pos=None):
     """The oracle forward of a workload-like object (first `layers` layers).
     amax: an optional float64 array [layers][5] that receives the per-site
-    max |stored value| of the int8 path's half sites."""
+    max |stored value| of the int8 path's half sites.  pos: the rows' RoPE
+    positions [rows][sections] (default: from the items, as or_positions)."""
     cfg = w.cfg
     nl = len(w.layers) if layers is None else layers
     keep = []
@@ -305,8 +309,25 @@ def forward(w, layers=None, f16_sites: bool = True, x=None, amax=None):
     if amax is not None:
         assert amax.dtype == np.float64 and amax.shape == (nl, 5) and amax.flags.c_contiguous
         amax[:] = 0.0
-    lib().or_encoder_forward(C.byref(M), w.rows, len(w.items), it, xp, out.ctypes.data_as(_D),
-                             1 if f16_sites else 0,
-                             amax.ctypes.data_as(_D) if amax is not None else None)
+    am = amax.ctypes.data_as(_D) if amax is not None else None
+    if pos is None:
+        lib().or_encoder_forward(C.byref(M), w.rows, len(w.items), it, xp, out.ctypes.data_as(_D),
+                                 1 if f16_sites else 0, am)
+    else:
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        assert pos.shape[0] == w.rows
+        lib().or_encoder_forward_pos(C.byref(M), w.rows, len(w.items), it, pos.ctypes.data_as(_I32),
+                                     xp, out.ctypes.data_as(_D), 1 if f16_sites else 0, am)
     del keep, fw, fb
     return out
+
+
+def forward_stages(stages, x, f16_sites: bool = True):
+    """A staged program: each stage (a workload-like object over rows
+    [row0, row0 + rows), its items relative to row0, its positions, final NONE)
+    runs its layers in place on those rows of the residual, in order."""
+    H = np.array(x, dtype=np.float64, copy=True)
+    for st, row0, pos in stages:
+        assert st.cfg["final"] == 0
+        H[row0:row0 + st.rows] = forward(st, f16_sites=f16_sites, x=H[row0:row0 + st.rows], pos=pos)
+    return H

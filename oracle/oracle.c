@@ -634,13 +634,16 @@ static void layer_forward(const or_layer *L, int64_t rows, int nitems, const or_
  * mean pool" step of `TextGpu::forward`: the per-row inverse RMS first, then the
  * weighted mean).  Layers run in order, each starting from the H the previous
  * one left (the fused next-layer pre-norm of the pages computes the same A). */
-OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, const or_item *items,
-                               const double *x, double *out, int f16_sites, double *amax)
+OR_API void or_encoder_forward_pos(const or_model *M, int64_t rows, int nitems, const or_item *items,
+                                   const int32_t *pos_in, const double *x, double *out, int f16_sites,
+                                   double *amax)
 {
     int d = M->d;
     int sec = M->nlayers > 0 ? M->layers[0].rope_sections : 0;
     int32_t *pos = (int32_t *)calloc((size_t)rows * (sec > 0 ? sec : 1), sizeof(int32_t));
-    if (sec > 0)
+    if (sec > 0 && pos_in)
+        memcpy(pos, pos_in, sizeof(int32_t) * rows * sec);
+    else if (sec > 0)
         or_positions(nitems, items, sec, pos);
     double *H = (double *)malloc(sizeof(double) * rows * d);
     memcpy(H, x, sizeof(double) * rows * d);
@@ -667,4 +670,13 @@ OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, cons
     }
     free(H);
     free(pos);
+}
+
+/* The forward with the positions of or_positions (the usual case); pos_in of
+ * or_encoder_forward_pos gives a stage of a larger program the positions its
+ * rows have in that program. */
+OR_API void or_encoder_forward(const or_model *M, int64_t rows, int nitems, const or_item *items,
+                               const double *x, double *out, int f16_sites, double *amax)
+{
+    or_encoder_forward_pos(M, rows, nitems, items, NULL, x, out, f16_sites, amax);
 }

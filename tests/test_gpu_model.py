@@ -160,6 +160,35 @@ def test_amax_per_site_vs_oracle():
     assert torch.equal(out, run(w))
 
 
+def _program(w, x=None):
+    prog = M.DeviceProgram(w, DEV)
+    X = torch.from_numpy(np.ascontiguousarray(w.x if x is None else x)).to(DEV)
+    h = torch.empty_like(X)
+    ws = prog.workspace(DEV)
+    M.stages_forward(prog, X, h, ws)
+    torch.cuda.synchronize()
+    return h
+
+
+def test_refiner_program_vs_oracle():
+    """The DiT step program with its refiners (context refiner on the caption
+    rows, noise refiner on the image rows, then the stack), CFG pair, in place."""
+    w = wl.make("zimage_dit_step_1056", layers=2, grid=8, ncap=8, cfg_pair=True, overrides=DIT_SMALL)
+    got = host(_program(w))
+    joint = O.positions(w.rows, w.items, w.grids, 2)
+    ref = O.forward_stages([(st, r0, joint[r0:r0 + st.rows]) for _, st, r0 in w.stages], w.x)
+    err = row_rel_err(got, ref)
+    say(f"  refiner program error {err:.2e}")
+    assert err <= TOL_I8F16
+    # each CFG item's rows equal the program of that item alone, bit for bit
+    for i, rr in enumerate(w.items):
+        idx = np.concatenate([np.arange(r0, r0 + n) for r0, n in rr])
+        single = wl.make("zimage_dit_step_1056", layers=2, grid=8, ncap=8, cfg_pair=False,
+                         overrides=DIT_SMALL)
+        alone = _program(single, x=w.x[idx])
+        assert np.array_equal(host(alone), got[idx]), f"item {i}"
+
+
 def test_deterministic():
     w = wl.make("gemma_text_f32", layers=2, lengths=[333, 64])
     assert torch.equal(run(w), run(w))

@@ -575,6 +575,25 @@ def test_unit_modulation_is_unmodulated(oracle):
     assert np.array_equal(a, oracle.forward(w))
 
 
+def test_refiner_program_stages(oracle):
+    """The staged DiT program: the noise refiner's rows carry their own grid
+    positions (the joint table's image slice), the two refiners touch disjoint
+    rows so their order does not change a bit, a program of the main stage
+    alone is the plain forward, and the refiners do act."""
+    w = wl.make("zimage_dit_step_1056", layers=1, grid=3, ncap=4, cfg_pair=True,
+                overrides=dict(d=256, nq=2, nkv=2, ff=384))
+    joint = oracle.positions(w.rows, w.items, w.grids, 2)
+    stages = [(st, r0, joint[r0:r0 + st.rows]) for _, st, r0 in w.stages]
+    assert [lab for lab, _, _ in w.stages] == ["context refiner", "noise refiner", "main"]
+    nr = w.stages[1][1]
+    assert np.array_equal(joint[:nr.rows], oracle.positions(nr.rows, nr.items, nr.grids, 2))
+    out = oracle.forward_stages(stages, w.x)
+    assert np.array_equal(oracle.forward_stages([stages[1], stages[0], stages[2]], w.x), out)
+    main_only = oracle.forward_stages([stages[2]], w.x)
+    assert np.array_equal(main_only, oracle.forward(w))
+    assert np.abs(main_only - out).max() > 1e-2 * np.abs(out).max()
+
+
 def test_packed_equals_separate_forward(oracle):
     w = wl.make("gemma_text_f32", layers=2, lengths=[7, 12, 3], overrides=dict(window=4))
     out = oracle.forward(w)

@@ -29,7 +29,7 @@ EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attenti
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
            "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
            "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak",
-           "enc_attention_workspace_bytes"]
+           "enc_attention_workspace_bytes", "encoder_stages_forward", "enc_stages_workspace_bytes"]
 CLASS_NAMES = ["gemm", "attn", "rows"]
 
 
@@ -145,6 +145,10 @@ class Model(C.Structure):
                 ("final_eps", C.c_float)]
 
 
+class Stage(C.Structure):
+    _fields_ = [("model", C.POINTER(Model)), ("batch", Batch), ("row0", C.c_uint32)]
+
+
 # ------------------------------------------------------------------ loading
 
 _lib = None
@@ -181,6 +185,10 @@ def lib():
     L.enc_attention_workspace_bytes.restype = C.c_size_t
     L.encoder_layer_forward.argtypes = [P, C.POINTER(Layer), C.POINTER(Batch), P, P, C.c_size_t, P]
     L.encoder_forward.argtypes = [P, C.POINTER(Model), C.POINTER(Batch), P, P, P, C.c_size_t, P]
+    L.encoder_stages_forward.argtypes = [P, C.POINTER(Stage), C.c_uint32, C.c_uint32, P, P, P,
+                                         C.c_size_t, P]
+    L.enc_stages_workspace_bytes.argtypes = [C.POINTER(Stage), C.c_uint32]
+    L.enc_stages_workspace_bytes.restype = C.c_size_t
     L.enc_check_gemm.argtypes = [C.POINTER(GemmDesc), C.POINTER(GemmItem), C.c_uint32,
                                  C.c_char_p, C.c_size_t]
     L.enc_check_attention.argtypes = [C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32,
@@ -193,7 +201,7 @@ def lib():
     L.enc_mfma_peak.argtypes = [P, C.c_uint32, C.c_uint32, C.c_uint32, P, C.POINTER(C.c_double), P]
     for f in ("gemm_items", "attention_items", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
               "enc_qk_norm_rope", "enc_gated_act", "enc_mean_pool", "encoder_layer_forward",
-              "encoder_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
+              "encoder_forward", "encoder_stages_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
               "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read",
               "enc_mfma_peak"):
         getattr(L, f).restype = S

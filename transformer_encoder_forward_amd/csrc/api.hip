@@ -988,6 +988,53 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
     return hipSuccess;
 }
 
+// The layers of a model in place on h (every layer's last row op writes the
+// next layer's inputs, or the fused final RMS).
+hipError_t run_stack(const enc_model *model, const enc_batch *batch, const float *x0, float *h, const Bufs &b,
+                     hipStream_t s) {
+    const enc_layer &L0 = model->layers[0];
+    if (L0.block == ENC_SANDWICH_RMS) TRY(pre_norm(L0, batch->rows, h, b.a, s));
+    for (uint32_t l = 0; l < model->nlayers; l++) {
+        NextIn nx;
+        if (L0.block == ENC_SANDWICH_RMS) {
+            if (l + 1 < model->nlayers)
+                nx = attn_in(model->layers[l + 1]);
+            else if (fused_final(model))
+                nx.w = model->final_w;  // the final RMS (f32) written by the last row op
+        }
+        TRY(run_layer(model->layers[l], batch, x0, h, b, nx, batch->amax ? batch->amax + 5 * l : nullptr, s));
+    }
+    return hipSuccess;
+}
+
+// A staged program: every stage valid, in range, final NONE, one width.
+enc_status check_stages(Err &e, const enc_stage *st, uint32_t n, uint32_t rows, WsPlan *most) {
+    if (!st || !n) return e.set(ENC_EINVAL, "encoder_stages_forward: no stages");
+    uint32_t d = 0;
+    size_t total = 0;
+    for (uint32_t i = 0; i < n; i++) {
+        const enc_model *M = st[i].model;
+        if (check_model(e, M, &st[i].batch) != ENC_OK) {
+            const std::string m = e.msg;
+            return e.set(e.st, "stage %u: %s", i, m.c_str());
+        }
+        if (!M->nlayers) return e.set(ENC_EINVAL, "stage %u: no layers", i);
+        if (M->final_kind != ENC_FINAL_NONE)
+            return e.set(ENC_EUNSUPPORTED, "stage %u: a stage's final must be NONE", i);
+        if ((uint64_t)st[i].row0 + st[i].batch.rows > rows)
+            return e.set(ENC_EINVAL, "stage %u: rows [%u, %u) past the program's %u", i, st[i].row0,
+                         st[i].row0 + st[i].batch.rows, rows);
+        if (i && M->layers[0].d != d) return e.set(ENC_ESHAPE, "stage %u: width differs", i);
+        d = M->layers[0].d;
+        const WsPlan p = plan_ws(M, &st[i].batch);
+        if (p.total > total) {
+            total = p.total;
+            *most = p;
+        }
+    }
+    return ENC_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -1270,17 +1317,7 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
     }
     hipError_t hr = hipSuccess;
     if (h != x) hr = hipMemcpyAsync(h, x, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s);
-    if (hr == hipSuccess && L0.block == ENC_SANDWICH_RMS) hr = pre_norm(L0, rows, h, b.a, s);
-    for (uint32_t l = 0; l < model->nlayers && hr == hipSuccess; l++) {
-        NextIn nx;
-        if (L0.block == ENC_SANDWICH_RMS) {
-            if (l + 1 < model->nlayers)
-                nx = attn_in(model->layers[l + 1]);
-            else if (fused_final(model))
-                nx.w = model->final_w;  // the final RMS (f32) written by the last row op
-        }
-        hr = run_layer(model->layers[l], batch, x0, h, b, nx, batch->amax ? batch->amax + 5 * l : nullptr, s);
-    }
+    if (hr == hipSuccess) hr = run_stack(model, batch, x0, h, b, s);
     if (hr == hipSuccess && model->final_kind == ENC_FINAL_LN) {
         NormArgs n{rows, d, d, d, h, model->final_w, model->final_b, model->final_eps, out};
         hr = rows_ln(n, false, s);
@@ -1295,6 +1332,55 @@ enc_status encoder_forward(enc_ctx *ctx, const enc_model *model, const enc_batch
         if (hr == hipSuccess) hr = pool_items(batch->items, batch->nitems, rows, d, a, out, s);
     }
     launch_status(e, hr, "encoder_forward");
+    return finish(ctx, e);
+}
+
+size_t enc_stages_workspace_bytes(const enc_stage *stages, uint32_t nstages) {
+    size_t most = 0;
+    if (!stages) return 0;
+    for (uint32_t i = 0; i < nstages; i++) {
+        const enc_model *M = stages[i].model;
+        if (!M || (M->nlayers && !M->layers) || (stages[i].batch.nitems && !stages[i].batch.items)) return 0;
+        most = std::max(most, plan_ws(M, &stages[i].batch).total);
+    }
+    return most;
+}
+
+enc_status encoder_stages_forward(enc_ctx *ctx, const enc_stage *stages, uint32_t nstages, uint32_t rows,
+                                  const float *x, float *h, void *ws, size_t ws_bytes, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
+    if (!x || !h || !ws) {
+        e.set(ENC_EINVAL, "encoder_stages_forward: null x, h or workspace");
+        return finish(ctx, e);
+    }
+    WsPlan p;
+    if (check_stages(e, stages, nstages, rows, &p) != ENC_OK) return finish(ctx, e);
+    if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(x, 16) || !aligned(h, 16)) {
+        e.set(ENC_EINVAL, "encoder_stages_forward: workspace needs %zu bytes, 256-byte aligned", p.total);
+        return finish(ctx, e);
+    }
+    const uint32_t d = stages[0].model->layers[0].d;
+    for (uint32_t i = 0; i < nstages; i++) {
+        bool ple = false;
+        for (uint32_t l = 0; l < stages[i].model->nlayers; l++) ple |= stages[i].model->layers[l].n_ple != 0;
+        if (ple && (!stages[i].batch.ple_x || stages[i].batch.ple_x == h + (size_t)stages[i].row0 * d)) {
+            e.set(ENC_EINVAL, "stage %u: a per-layer input needs its batch ple_x", i);
+            return finish(ctx, e);
+        }
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t hr = hipSuccess;
+    if (h != x) hr = hipMemcpyAsync(h, x, (size_t)rows * d * 4, hipMemcpyDeviceToDevice, s);
+    for (uint32_t i = 0; i < nstages && hr == hipSuccess; i++) {
+        // each stage's buffers carved for its own batch (all fit the largest plan)
+        const WsPlan sp = plan_ws(stages[i].model, &stages[i].batch);
+        const Bufs b = carve(ws, sp);
+        float *hs = h + (size_t)stages[i].row0 * d;
+        hr = run_stack(stages[i].model, &stages[i].batch, stages[i].batch.ple_x, hs, b, s);
+    }
+    launch_status(e, hr, "encoder_stages_forward");
     return finish(ctx, e);
 }
 

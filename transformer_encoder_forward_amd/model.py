@@ -61,7 +61,7 @@ class DeviceModel:
                 if n not in shapes:
                     continue
                 if cfg["path"] == wl.PATH_I8F16 and n not in t:
-                    dev = wl.int8_weight_torch(w.seed, li, n, shapes[n], device)
+                    dev = wl.int8_weight_torch(w.seed, li, n, shapes[n], device, w.prefix)
                 else:
                     arr = t[n]
                     dev = torch.from_numpy(np.ascontiguousarray(arr)).to(device)
@@ -96,7 +96,11 @@ class DeviceModel:
 
 
 class DeviceBatch:
-    def __init__(self, w: wl.Workload, device="cuda"):
+    """The batch struct of a workload; `pos` gives the rows' RoPE positions
+    (default: from its items, enc_positions) -- a stage of a larger program
+    passes the positions its rows have in that program."""
+
+    def __init__(self, w: wl.Workload, device="cuda", pos=None):
         cfg = w.cfg
         self.rows = w.rows
         self.items_py = w.items
@@ -109,7 +113,7 @@ class DeviceBatch:
         sec = cfg["rope_sections"]
         self.tables = []
         if sec:
-            self.pos = B.positions(w.rows, w.items, w.grids, sec)
+            self.pos = B.positions(w.rows, w.items, w.grids, sec) if pos is None else pos
             for i, base in enumerate(rope_bases(w)):
                 cos, sin = B.rope_table(self.pos, cfg["hd"], sec, base)
                 cos, sin = torch.from_numpy(cos).to(device), torch.from_numpy(sin).to(device)
@@ -136,3 +140,38 @@ def encoder_layer_forward(model: DeviceModel, layer: int, batch: DeviceBatch, h,
 
 def out_rows(w: wl.Workload):
     return len(w.items) if w.cfg["final"] == wl.FINAL_RMS_MEANPOOL else w.rows
+
+
+class DeviceProgram:
+    """A staged program (w.stages: context refiner, noise refiner, main stack)
+    as an enc_stage array; `skip` leaves out stages by label (the context
+    refiner runs once per prompt, not per step)."""
+
+    def __init__(self, w: wl.Workload, device="cuda", skip=()):
+        sec = w.cfg["rope_sections"]
+        joint = B.positions(w.rows, w.items, w.grids, sec) if sec else None
+        self.rows, self.d = w.rows, w.cfg["d"]
+        self.parts = []
+        for label, st, row0 in w.stages:
+            if label in skip:
+                continue
+            pos = joint[row0:row0 + st.rows] if joint is not None else None
+            self.parts.append((label, DeviceModel(st, device), DeviceBatch(st, device, pos=pos), row0))
+        self.stages = (B.Stage * len(self.parts))()
+        for i, (_, dm, db, row0) in enumerate(self.parts):
+            self.stages[i].model = C.pointer(dm.model)
+            self.stages[i].batch = db.batch
+            self.stages[i].row0 = row0
+
+    def workspace_bytes(self):
+        return B.lib().enc_stages_workspace_bytes(self.stages, len(self.parts))
+
+    def workspace(self, device="cuda"):
+        return torch.empty(self.workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def stages_forward(prog: DeviceProgram, x, h, ws, ctx=None, stream=None):
+    ctx = ctx or B.context()
+    ctx.check(B.lib().encoder_stages_forward(ctx.h, prog.stages, len(prog.parts), prog.rows,
+                                             x.data_ptr(), h.data_ptr(), ws.data_ptr(), ws.numel(),
+                                             B._stream(stream)))

@@ -1,6 +1,6 @@
 """Synthetic workloads of the packed encoder forward: shapes, items and seeded tensors.
 
-Eight workloads, each the shape of one of the encoders on the reference pages,
+Nine workloads, each the shape of one of the encoders on the reference pages,
 with random weights (no trained checkpoint is available):
 
   vit_layer_f32        one pre-LN ViT layer: 64 tokens, d 128, 2x64 heads, MLP 512
@@ -19,6 +19,9 @@ with random weights (no trained checkpoint is available):
                        RoPE bases 1e4 / 1e6, layer scalars, per-layer input (256 wide)
   zimage_dit_mod_1056  zimage_dit_1056 with adaLN modulation, q8_2f column fields and
                        the Turbo power-of-two guards of the five half sites
+  zimage_dit_step_1056 zimage_dit_mod_1056 as the page's staged program: context
+                       refiner (2 unmodulated blocks, caption rows), noise refiner
+                       (2 blocks, image rows), then the 30-block stack
   gemma_vision_f32     the text model's vision tower: 16 sandwich layers, d 768, 12x64
                        heads, qk-norm + 2-D RoPE, gated GELU 3072, five images of
                        32x32, 24x24, 16x16, 16x16 and 8x8 patches packed back to back
@@ -97,6 +100,16 @@ CONFIGS = {
         attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
         grid=32, ncap=32, cfg_pair=False, modulated=True, col_fields=True,
         guards=[0, 1, 0, 0, 6]),
+    # one DiT step of the 1056-row program with its refiner stages: two noise
+    # refiner blocks on the image rows, then the 30-block stack (both modulated);
+    # before them, once per prompt, two unmodulated context refiner blocks on
+    # the caption rows
+    "zimage_dit_step_1056": dict(
+        num=9, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
+        hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
+        grid=32, ncap=32, cfg_pair=False, modulated=True, col_fields=True,
+        guards=[0, 1, 0, 0, 6], noise_refiner=2, context_refiner=2),
     "zimage_dit_cfg_8448": dict(
         num=5, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
         hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
@@ -125,6 +138,10 @@ class Workload:
     final_w: np.ndarray | None = None
     final_b: np.ndarray | None = None
     seed: int = 0
+    prefix: str = "L"   # tensor-name prefix of the layers' draws
+    # a staged program: (label, stage workload over rows [row0, row0 + rows),
+    # row0); the stage's items are relative to row0
+    stages: list = field(default_factory=list)
 
     @property
     def ld(self):
@@ -147,46 +164,47 @@ def _normal(seed, name, shape, std, mean=0.0):
     return (mean + std * z).astype(np.float32).reshape(shape)
 
 
-def int8_weight_rows(seed: int, layer: int, name: str, shape, r0: int, r1: int) -> np.ndarray:
+def int8_weight_rows(seed: int, layer: int, name: str, shape, r0: int, r1: int,
+                     prefix: str = "L") -> np.ndarray:
     """Rows r0..r1-1 of an int8 weight (host draw of just those rows)."""
-    k = synth.tensor_key(seed, f"L{layer}.{name}")
+    k = synth.tensor_key(seed, f"{prefix}{layer}.{name}")
     cols = shape[1]
     return synth.int8_np(k, r0 * cols, (r1 - r0) * cols).reshape(r1 - r0, cols)
 
 
-def int8_weight_torch(seed: int, layer: int, name: str, shape, device):
-    k = synth.tensor_key(seed, f"L{layer}.{name}")
+def int8_weight_torch(seed: int, layer: int, name: str, shape, device, prefix: str = "L"):
+    k = synth.tensor_key(seed, f"{prefix}{layer}.{name}")
     return synth.int8_torch(k, 0, shape[0] * shape[1], device).view(shape[0], shape[1])
 
 
-def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
+def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool, prefix: str = "L") -> dict:
     t = {}
     d, hd = cfg["d"], cfg["hd"]
     for name, shape in weight_shapes(cfg).items():
         if cfg["path"] == PATH_F32:
-            t[name] = _normal(seed, f"L{li}.{name}", shape, 0.02)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", shape, 0.02)
         else:
             if not lazy_int8:
-                t[name] = int8_weight_rows(seed, li, name, shape, 0, shape[0])
+                t[name] = int8_weight_rows(seed, li, name, shape, 0, shape[0], prefix)
             sname = "s" + name[1:]
-            z = synth.normal_np(synth.tensor_key(seed, f"L{li}.{sname}"), 0, shape[0])
+            z = synth.normal_np(synth.tensor_key(seed, f"{prefix}{li}.{sname}"), 0, shape[0])
             t[sname] = (0.002 * np.exp(0.25 * z)).astype(np.float32)
     if cfg["biases"]:
         for name, width in (("bq", cfg["nq"] * hd), ("bk", cfg["nkv"] * hd),
                             ("bv", cfg["nkv"] * hd), ("bo", d), ("b_up", cfg["ff"]),
                             ("b_down", d)):
-            t[name] = _normal(seed, f"L{li}.{name}", (width,), 0.01)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (width,), 0.01)
     if cfg["block"] == BLOCK_PRE_LN:
         for name in ("norm1_w", "norm2_w"):
-            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (d,), 0.02, 1.0)
         for name in ("norm1_b", "norm2_b"):
-            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.01)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (d,), 0.01)
     else:
         for name in ("norm1_w", "post_attn_w", "norm2_w", "post_ff_w"):
-            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.02, 1.0)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (d,), 0.02, 1.0)
         for name in ("q_norm_w", "k_norm_w"):
             g = cfg.get("qk_gain", 1.0)
-            t[name] = _normal(seed, f"L{li}.{name}", (hd,), 0.02 * g, g)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (hd,), 0.02 * g, g)
     # per-layer values: every global_every-th layer attends globally (window 0)
     # with its own RoPE base; the rest keep the config's window and base
     ge = cfg.get("global_every", 0)
@@ -200,23 +218,23 @@ def _layer(cfg: dict, seed: int, li: int, lazy_int8: bool) -> dict:
         # [s_msa | g_msa | s_mlp | g_mlp]: scales near 0, gates near 1
         for name, mean in (("mod_s_attn", 0.0), ("mod_g_attn", 1.0), ("mod_s_ff", 0.0),
                            ("mod_g_ff", 1.0)):
-            t[name] = _normal(seed, f"L{li}.{name}", (d,), 0.1, mean)
+            t[name] = _normal(seed, f"{prefix}{li}.{name}", (d,), 0.1, mean)
     if cfg.get("col_fields"):
         # q8_2f column fields: positive, lognormal around 1, one per input column
         q = cfg["nq"] * hd
         for name, width in (("col_q", d), ("col_k", d), ("col_v", d), ("col_o", q),
                             ("col_gate", d), ("col_up", d), ("col_down", cfg["ff"])):
-            z = synth.normal_np(synth.tensor_key(seed, f"L{li}.{name}"), 0, width)
+            z = synth.normal_np(synth.tensor_key(seed, f"{prefix}{li}.{name}"), 0, width)
             t[name] = np.exp(0.25 * z).astype(np.float32)
     if cfg.get("layer_scalar"):
-        t["scalar"] = float(1.0 + 0.05 * synth.normal_np(synth.tensor_key(seed, f"L{li}.scalar"), 0, 1)[0])
+        t["scalar"] = float(1.0 + 0.05 * synth.normal_np(synth.tensor_key(seed, f"{prefix}{li}.scalar"), 0, 1)[0])
     if cfg.get("n_ple"):
         np_ = cfg["n_ple"]
-        t["ple_in"] = _normal(seed, f"L{li}.ple_in", (np_, d), 0.02)
-        t["ple_gate"] = _normal(seed, f"L{li}.ple_gate", (np_, d), 0.02)
-        t["ple_proj"] = _normal(seed, f"L{li}.ple_proj", (d, np_), 0.02)
+        t["ple_in"] = _normal(seed, f"{prefix}{li}.ple_in", (np_, d), 0.02)
+        t["ple_gate"] = _normal(seed, f"{prefix}{li}.ple_gate", (np_, d), 0.02)
+        t["ple_proj"] = _normal(seed, f"{prefix}{li}.ple_proj", (d, np_), 0.02)
         t["ple_in_norm_w"] = _normal(seed, "ple_in_norm_w", (np_,), 0.02, 1.0)  # model-wide
-        t["ple_post_w"] = _normal(seed, f"L{li}.ple_post_w", (d,), 0.02, 1.0)
+        t["ple_post_w"] = _normal(seed, f"{prefix}{li}.ple_post_w", (d,), 0.02, 1.0)
     return t
 
 
@@ -289,7 +307,41 @@ def make(name: str, layers=None, lengths=None, grid=None, ncap=None, cfg_pair=No
         w.final_w = _normal(seed, "final_w", (d,), 0.02, 1.0)
         if cfg["final"] == FINAL_LN:
             w.final_b = _normal(seed, "final_b", (d,), 0.01)
+    if cfg.get("noise_refiner") or cfg.get("context_refiner"):
+        w.stages = _dit_stages(w, lazy_int8)
     return w
+
+
+def _dit_stages(w: Workload, lazy_int8: bool) -> list:
+    """The DiT step program with its refiners: the context refiner (its own
+    unmodulated blocks) on each item's caption rows, the noise refiner (the
+    first step blocks) on the image rows of every item, then the main stack on
+    all rows.  Rows stay where the packed batch has them, so a refiner stage
+    is a contiguous slice: [img0 | img1 | cap0 | cap1]."""
+    cfg, seed = w.cfg, w.seed
+    img = [rr[0] for rr in w.items]
+    caps = [rr[1] for rr in w.items if len(rr) > 1]
+    stages = []
+    nc = cfg.get("context_refiner", 0)
+    if nc and caps:
+        ccfg = dict(cfg, layers=nc, modulated=False)
+        r0 = caps[0][0]
+        rows = sum(n for _, n in caps)
+        sub = Workload(name=w.name + ".context_refiner", cfg=ccfg, rows=rows,
+                       items=[[(c0 - r0, n)] for c0, n in caps], grids=[0] * len(caps),
+                       x=w.x[r0:r0 + rows], seed=seed, prefix="CR")
+        sub.layers = [_layer(ccfg, seed, li, lazy_int8, "CR") for li in range(nc)]
+        stages.append(("context refiner", sub, r0))
+    nn = cfg.get("noise_refiner", 0)
+    if nn:
+        ncfg = dict(cfg, layers=nn)
+        rows = sum(n for _, n in img)
+        sub = Workload(name=w.name + ".noise_refiner", cfg=ncfg, rows=rows, items=[[r] for r in img],
+                       grids=list(w.grids), x=w.x[:rows], seed=seed, prefix="NR")
+        sub.layers = [_layer(ncfg, seed, li, lazy_int8, "NR") for li in range(nn)]
+        stages.append(("noise refiner", sub, 0))
+    stages.append(("main", w, 0))
+    return stages
 
 
 def gemm_flops(w: Workload) -> float:
