@@ -27,7 +27,9 @@ def _lib():
 # ---------------------------------------------------------------- GEMM f32
 
 @pytest.mark.parametrize("n,m,k", [(1, 1, 4), (37, 70, 36), (130, 257, 128), (257, 128, 512),
-                                   (64, 384, 128), (300, 96, 2048)])
+                                   (64, 384, 128), (300, 96, 2048),
+                                   (8001, 1000, 96),    # 256 x 128 tiles, ragged rows and columns
+                                   (4100, 4000, 64)])   # 128 x 128 tiles
 def test_gemm_f32_integer_exact(n, m, k):
     say(f"gemm f32 integer n={n} m={m} k={k}")
     rng = np.random.default_rng(n * 31 + m * 7 + k)
@@ -109,7 +111,7 @@ def test_gemm_packed_rows_bit_identical():
     (B.ENC_F32, "gelu", 1000, 2048, 512), (B.ENC_F32, "gelu", 37, 200, 128),
     (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64),
     (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192),
-    (B.ENC_I8F16, "silu", 77, 160, 80)])
+    (B.ENC_I8F16, "silu", 77, 160, 80), (B.ENC_F32, "gelu", 8001, 2048, 512)])
 def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
     bit for bit, and == the oracle within tolerance."""

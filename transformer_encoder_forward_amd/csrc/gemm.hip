@@ -1,8 +1,9 @@
 // Launchers of the item-table GEMM (kernel templates in gemm_impl.h).
 //
 // The tile shape is chosen per launch from the problem size.  f32: large
-// problems take 128 x 128 tiles, small ones (too few 128 x 128 tiles to fill
-// the 256 CUs twice over) take 64 x 64 tiles.  int8 x f16: large problems take
+// problems take 256 x 128 tiles (gated: 256 rows x 128 outputs), middling ones
+// 128 x 128, small ones (too few 128 x 128 tiles to fill the 256 CUs twice
+// over) 64 x 64 tiles.  int8 x f16: large problems take
 // the kernel fed by direct global -> LDS loads (256 x 256 tiles, or 128 x 256
 // when there are few of those), and K % 64 != 0 the register-staged 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
@@ -24,14 +25,21 @@ uint32_t tiles_of(const GemmArgs &a, int BM, int BN) {
 }
 
 constexpr uint32_t kBigTiles = 1024;  // >= 4 tiles per CU at 128 x 128
+constexpr uint32_t kWideF32 = 240;    // about one 256 x 128 tile per CU
 
 }  // namespace
 
+// f32, measured on the 16 057-row text encoder (min of interleaved runs): the
+// 256 x 128 tile of 8 waves with 64 x 64 each beats 64 x 64 tiles by 8% on the
+// down projection and ties elsewhere; the gated 256 x (128 + 128) tile of 16
+// waves beats 128 x (64 + 64) by 6%.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
     if (a.flags & (gemm::kGateGelu | gemm::kGateSilu)) {
+        if (tiles_of(a, 256, 128) >= kWideF32) return gemm::launch_gated<256, 256, 32, 4, false, 1>(a, s);
         if (tiles_of(a, 128, 64) >= kBigTiles) return gemm::launch_gated<128, 128, 32, 2, false, 2>(a, s);
         return gemm::launch_gated<64, 128, 32, 2, false, 4>(a, s);
     }
+    if (tiles_of(a, 256, 128) >= kWideF32) return gemm::launch<256, 128, 32, 4, 2, false, 1>(a, s);
     if (tiles_of(a, 128, 128) >= kBigTiles) return gemm::launch<128, 128, 32, 2, 4, false, 1>(a, s);
     return gemm::launch_v2<64, 64, 32, 2, 2, false, 4>(a, s);
 }
