@@ -60,6 +60,12 @@ __device__ __forceinline__ bool block_active(int q0, int q1, int kb, int k_hi, u
     return kb <= q1 - 1 + (int)W && kb + KB - 1 >= q0 - (int)W;
 }
 
+// Column of the 16-byte group g (keys 4g..4g+3) in row `row` of the staged V^T:
+// groups are XOR-swizzled by bits 4-6 of the row so that both the transposing
+// 4-byte stores (16 rows x 4 keys per wave) and the 16-byte reads (consecutive
+// rows, one group) spread over all banks.
+__device__ __forceinline__ int vt_col(int row, int g) { return 4 * (g ^ ((row >> 4) & 7)); }
+
 // Online-softmax update of one lane's 16 scores (query = lane%32).  s holds
 // raw dot products; masked keys become -inf.  Returns p in place.  2^x is the
 // bare v_exp_f32 (results below 2^-126 flush to 0, far below anything a row
@@ -109,6 +115,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
     const int tq = c.q_lo + wave * 32 + li;
     const bool qvalid = tq < c.q_hi;
     const int wq0 = c.q_lo + wave * 32, wq1 = min(wq0 + 32, c.q_hi);
+    // keys this lane's query sees: [vlo, vhi), empty for a padding lane
+    const int vlo = W ? max(c.k_lo, tq - (int)W) : c.k_lo;
+    const int vhi = !qvalid ? vlo : max(vlo, W ? min(c.k_hi, tq + (int)W + 1) : c.k_hi);
 
     // this lane's query, channels (hd/2)*hf .. +hd/2 (its half of the dot product)
     f32x4 qf[NQ4];
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
             const int f = tid + NT * i, key = f / (HD / 4), ch = (f % (HD / 4)) * 4;
             st4(&Ks[buf][key][ch], rk[i]);
 #pragma unroll
-            for (int e = 0; e < 4; e++) Vs[buf][ch + e][key] = rv[i][e];
+            for (int e = 0; e < 4; e++) Vs[buf][ch + e][vt_col(ch + e, key >> 2) + (key & 3)] = rv[i][e];
         }
     };
 
@@ -166,25 +175,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; r++) s[r] = 0.0f;
             const float *kr = &Ks[buf][li][(HD / 2) * hf];
+            f32x4 kf[NQ4];
 #pragma unroll
-            for (int j = 0; j < NQ4; j++) {
-                const f32x4 kf = ld4(kr + 4 * j);
+            for (int j = 0; j < NQ4; j++) kf[j] = ld4(kr + 4 * j);
+#pragma unroll
+            for (int j = 0; j < NQ4; j++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[j][e], s, 0, 0, 0);
-            }
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[j][e], qf[j][e], s, 0, 0, 0);
+            // every pair of the wave x block visible: all 32 queries valid, all
+            // keys inside the range and inside every query's window
+            const bool full = wq1 - wq0 == 32 && kb + KB <= c.k_hi &&
+                              (!W || (wq1 - 1 - kb <= (int)W && kb + KB - 1 - wq0 <= (int)W));
             float sv[16];
+            if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                const bool vis = qvalid && key < c.k_hi && (!W || abs(tq - key) <= (int)W);
-                sv[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
+                for (int r = 0; r < 16; r++) sv[r] = s[r] * a.scale_log2;
+            } else {
+                // key kb + off(r) is visible iff it lies in [vlo, vhi)
+                const uint32_t base = (uint32_t)(kb + 4 * hf - vlo), span = (uint32_t)(vhi - vlo);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const bool vis = base + (uint32_t)(8 * (r >> 2) + (r & 3)) < span;
+                    sv[r] = vis ? s[r] * a.scale_log2 : -INFINITY;
+                }
             }
+            const float m_old = m_run;
             const float alpha = softmax_step(sv, m_run, l_run);
+            // o is rescaled only when some query's max grew (else alpha is 1 or
+            // o is still 0)
+            if (__any(m_run > m_old)) {
 #pragma unroll
-            for (int d = 0; d < HD / 32; d++)
+                for (int d = 0; d < HD / 32; d++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+                    for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+            }
             // O^T[d][q] += V^T[d][key] P^T[key][q]; step r pairs lane halves'
             // keys 8(r/4) + 4 hf + r%4, so the keys of steps 4g..4g+3 are four
             // consecutive floats of a V^T row: one 16-byte read per 4 MFMAs
@@ -192,7 +217,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
             for (int g4 = 0; g4 < 4; g4++)
 #pragma unroll
                 for (int d = 0; d < HD / 32; d++) {
-                    const f32x4 v4 = ld4(&Vs[buf][32 * d + li][8 * g4 + 4 * hf]);
+                    const f32x4 v4 = ld4(&Vs[buf][32 * d + li][vt_col(32 * d + li, 2 * g4 + hf)]);
 #pragma unroll
                     for (int e = 0; e < 4; e++)
                         o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(v4[e], sv[4 * g4 + e], o[d], 0, 0, 0);
