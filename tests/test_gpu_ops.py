@@ -296,6 +296,31 @@ def test_attention_f16(name, items, window, hd, nq, nkv):
     assert err <= TOL_I8F16
 
 
+def test_attention_f16_wide_launch_two_range_sampled():
+    """A launch wide enough for the 256-query f16 blocks (nq 24, GQA 3:1), with
+    two-range items whose first range ends inside a 32-key block, a ragged last
+    block and a one-row item; sampled query rows of every range against the
+    oracle."""
+    items = [[(0, 3001), (6100, 37)], [(3001, 3099), (6137, 50)], [(6187, 1)]]
+    rows, nq, nkv, hd = 6188, 24, 8, 128
+    rng = np.random.default_rng(11)
+    p = _panel(rng, rows, nq, nkv, hd, f16=True, qscale=0.5)
+    out = torch.zeros((rows, nq * hd), dtype=torch.float16, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(to_dev(p), out, items, nq, nkv, hd, scale, 0, path=B.ENC_I8F16)
+    sel = []
+    for rr in items:
+        for r0, n in rr:
+            sel += [r0, r0 + 1, r0 + n // 2, r0 + n - 2, r0 + n - 1]
+    sel = np.unique(np.clip(sel + list(rng.integers(0, rows, 24)), 0, rows - 1))
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, scale, 0, query_rows=sel)[sel]
+    ref = np.vectorize(O.round_f16)(ref)
+    err = row_rel_err(host(out)[sel], ref)
+    say(f"  {len(sel)} sampled queries, err {err:.2e}")
+    assert err <= TOL_I8F16
+
+
 @pytest.mark.parametrize("path", [B.ENC_F32, B.ENC_I8F16])
 @pytest.mark.parametrize("L,W", [(64, 0), (64, 5), (64, 31), (40, 39), (64, 1)])
 def test_attention_mask_probe(path, L, W):

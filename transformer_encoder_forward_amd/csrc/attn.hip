@@ -325,12 +325,6 @@ hipError_t launch_attn_f32(const AttnArgs &a, uint32_t hd, hipStream_t s) {
     return launch_f32<128, 4>(a, s);
 }
 
-// hd 128 takes the direct-to-LDS kernels.  Without a window: the pipelined
-// one, in blocks of 256 queries (8 waves, one block per CU, each K/V block
-// staged once for twice the queries) when the launch still has two such blocks
-// per CU, else 128.  With a window, a block's first key depends on its query
-// tile, so the tile size must not change between launches of the same item:
-// always 128 queries.  Every choice sums each query's keys in the same order.
 hipError_t launch_attn_combine(const CombineArgs &a, bool f16_out, hipStream_t s) {
     const uint64_t total = (uint64_t)a.row0[a.nitems] * a.nq * (a.hd / 4);
     if (!total) return hipSuccess;
@@ -342,13 +336,19 @@ hipError_t launch_attn_combine(const CombineArgs &a, bool f16_out, hipStream_t s
     return hipGetLastError();
 }
 
+// hd 128 takes the direct-to-LDS kernels.  Without a window: the pipelined
+// one, in blocks of 256 queries (8 waves, one block per CU, each K/V block
+// staged once for twice the queries) when the launch still has two such blocks
+// per CU, else 128.  With a window, a block's first key depends on its query
+// tile, so the tile size must not change between launches of the same item:
+// always 128 queries.  Every choice sums each query's keys in the same order.
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s) {
     if (hd == 64) return attn::launch<64, true, 4, 4, true>(a, s);
     if (a.window) return attn::launch_f16d<4, 2>(a, s);
     uint32_t t256 = 0;
     for (uint32_t i = 0; i < a.nitems; i++) t256 += (a.items[i].na + a.items[i].nb + 255) / 256;
-    if (t256 * a.nq >= 512) return attn::launch_f16p<8, 1>(a, s);
-    return attn::launch_f16p<4, 2>(a, s);
+    if (t256 * a.nq >= 512) return attn::launch_f16s<8, 1>(a, s);
+    return attn::launch_f16s<4, 2>(a, s);
 }
 
 }  // namespace enc

@@ -496,29 +496,53 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
     }
 }
 
-// The same attention without a window, software-pipelined within each wave:
-// iteration b computes the scores of key block b+1 (eight dependent MFMAs)
-// next to the softmax of block b (VALU), which do not depend on each other, so
-// the matrix core and the vector ALU of one wave can work at the same time;
-// then P V of block b.  Four LDS stages: block b+3 is loaded while block b+1's
-// K and block b's V are read.  Keys past the item occur only in the last block
-// and are masked there; rows past the item's queries are computed on clamped
-// data and never stored.  The cross-half row max uses v_permlane32_swap; the
-// query loads land before the staging loads start, so no wait for them sits
-// inside the loop.
-__device__ __forceinline__ float max_halves(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// LDS reads at a base address plus an immediate byte offset.
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16_at(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read8_tr16_at(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+    return v;
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// The attention without a window at hd 128, software-pipelined within each
+// wave, with K/V staged as in attn_f16d_kernel (direct global -> LDS loads, a
+// ring of four stages, the same LDS swizzles) and the per-block overhead cut
+// down to the softmax itself:
+//  - the loop is unrolled over the four LDS stages, so every fragment read is a
+//    loop-invariant per-lane address plus an immediate offset (no address
+//    arithmetic per block), and the scores of consecutive blocks alternate
+//    between two register sets instead of being copied;
+//  - a block that lies inside one row range of the item is staged from a
+//    wave-uniform row base plus per-lane byte offsets fixed at the start;
+//  - the row sum adds the f16 probabilities that the P V product consumes, two
+//    at a time (v_dot2_f32_f16 with ones, f32 accumulation), so numerator and
+//    denominator see the same rounded p;
+//  - the row max takes three scores per instruction (v_maximum3, no input
+//    quieting);
+//  - the output is rescaled only when some query's running max grew.
+// Iteration b computes the scores of block b+1 (a dependent MFMA chain,
+// interleaved with the exponentials of block b by scheduling groups), then
+// P V of block b; block b+3 is staged meanwhile.  Keys past the item occur only
+// in the last block and are masked there; rows past the item's queries are
+// computed on clamped data and never stored.
 template <int NW, int MINW>
-__global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     constexpr int HD = 128, QT = 32 * NW, NS = 4;
-    constexpr int TBYTES = KB * HD * 2;
-    constexpr int SBYTES = 2 * TBYTES;
+    constexpr int TBYTES = KB * HD * 2;   // one K or V block: 8 KB
+    constexpr int SBYTES = 2 * TBYTES;    // a stage: K then V
     constexpr int NI = TBYTES / 1024 / NW;
     constexpr int NDMA = 2 * NI;
     static_assert(TBYTES / 1024 % NW == 0, "waves");
+    static_assert(NS * SBYTES <= 65536, "immediate LDS offsets");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SBYTES];
 
     const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
@@ -538,45 +562,74 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
         const _Float16 *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col + head * HD + 64 * hf;
 #pragma unroll
         for (int j = 0; j < HD / 16; j++) qf[j] = *reinterpret_cast<const f16x8 *>(qp + 8 * j);
-        // land q before the staging loads start, so that no wait for them is
-        // placed inside the loop (it would also wait for every block in flight)
         vm_wait<0>();
 #pragma unroll
         for (int j = 0; j < HD / 16; j++) ready(qf[j]);
     }
 
+    // staging: instruction q of this wave covers keys 4 (wave NI + q) .. +3 of a
+    // block; lane l takes key + l/16 and LDS position l % 16 of that key row,
+    // which holds chunk (l%16) ^ (key & 15) of K and (l%16) ^ 4 (key & 3) of V
     const int kl = lane >> 4, pl = lane & 15;
-    auto dma = [&](int b) {
-        const int kb = c.k_lo + b * KB;
-        uint8_t *buf = smem + (b % NS) * SBYTES;
+    uint32_t kso[NI], vso[NI];  // byte offsets from the block's first row
 #pragma unroll
-        for (int q = 0; q < NI; q++) {
-            const int ti = 4 * (wave * NI + q) + kl;
-            const int t = min(kb + ti, c.k_hi - 1);
-            const _Float16 *row = P + (size_t)row_of(c.it, t) * a.ld + kvh * HD;
-            dma16(row + a.k_col + 8 * (pl ^ (ti & 15)), buf + (wave * NI + q) * 1024);
-            dma16(row + a.v_col + 8 * (pl ^ (4 * (ti & 3))), buf + TBYTES + (wave * NI + q) * 1024);
+    for (int q = 0; q < NI; q++) {
+        const uint32_t ti = 4 * (wave * NI + q) + kl;
+        const uint32_t r = ti * a.ld + kvh * HD;
+        kso[q] = 2 * (r + a.k_col + 8 * (pl ^ (ti & 15)));
+        vso[q] = 2 * (r + a.v_col + 8 * (pl ^ (4 * (ti & 3))));
+    }
+    const int na = (int)c.it.na;
+    auto dma = [&](auto st, int b) {
+        uint8_t *buf = smem + decltype(st)::value * SBYTES;
+        const int kb = c.k_lo + b * KB;
+        if (kb + KB <= c.k_hi && (kb + KB <= na || kb >= na)) {
+            const int r0 = kb < na ? (int)c.it.r0a + kb : (int)c.it.r0b + (kb - na);
+            const char *base = reinterpret_cast<const char *>(P + (size_t)r0 * a.ld);
+#pragma unroll
+            for (int q = 0; q < NI; q++) {
+                dma16(base + kso[q], buf + (wave * NI + q) * 1024);
+                dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+            }
+        } else {
+            // the block crosses into the second row range or past the item:
+            // rows per lane, keys past the item clamped to its last row (masked)
+#pragma unroll
+            for (int q = 0; q < NI; q++) {
+                const int ti = 4 * (wave * NI + q) + kl;
+                const int t = min(kb + ti, c.k_hi - 1);
+                const char *base = reinterpret_cast<const char *>(P + ((ptrdiff_t)row_of(c.it, t) - ti) * a.ld);
+                dma16(base + kso[q], buf + (wave * NI + q) * 1024);
+                dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+            }
         }
     };
 
+    // fragment addresses (stage 0): K row li, chunk 8 hf + j; V^T transposed
+    // reads of channel block d (key group and half are immediates)
     const uint32_t lds0 = lds_offset(smem);
-    const uint32_t krow = lds0 + (uint32_t)li * 256u;
-    const int g = lane >> 4, src = lane & 15;
-    const uint32_t vrow = lds0 + TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
-    const int vc0 = 2 * (g & 1) + ((src & 3) >> 1);
-    const int vsw = 4 * (src >> 2);
-
-    u32x4 kf[HD / 16];
-    auto kread = [&](uint32_t sb) {
+    uint32_t kaddr[HD / 16], vaddr[HD / 32];
 #pragma unroll
-        for (int j = 0; j < HD / 16; j++) kf[j] = ds_read16(krow + sb + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16));
+    for (int j = 0; j < HD / 16; j++) kaddr[j] = lds0 + (uint32_t)li * 256u + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16);
+    {
+        const int g = lane >> 4, src = lane & 15;
+        const uint32_t vrow = lds0 + TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
+        const int vc0 = 2 * (g & 1) + ((src & 3) >> 1), vsw = 4 * (src >> 2);
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) vaddr[d] = vrow + (uint32_t)(((4 * d + vc0) ^ vsw) * 16);
+    }
+    u32x4 kf[HD / 16];
+    auto kread = [&](auto st) {
+        constexpr int off = decltype(st)::value * SBYTES;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) kf[j] = ds_read16_at<off>(kaddr[j]);
     };
     u32x2 vf[HD / 32][2][2];
-    auto vread = [&](uint32_t sb, int d, int s2) {
-#pragma unroll
-        for (int e8 = 0; e8 < 2; e8++)
-            vf[d][s2][e8] = ds_read8_tr16(vrow + sb + (uint32_t)((16 * s2 + 8 * e8) * 256) +
-                                          (uint32_t)(((4 * d + vc0) ^ vsw) * 16));
+    auto vread = [&](auto st, int d, auto s2c) {
+        constexpr int s2 = decltype(s2c)::value;
+        constexpr int off = decltype(st)::value * SBYTES + 16 * s2 * 256;
+        vf[d][s2][0] = ds_read8_tr16_at<off>(vaddr[d]);
+        vf[d][s2][1] = ds_read8_tr16_at<off + 8 * 256>(vaddr[d]);
     };
 
     f32x16 o[HD / 32];
@@ -586,11 +639,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
         for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
     float m_run = -INFINITY, l_lane = 0.0f;
     const float cs = a.scale_log2;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
-    if (nblk > 0) dma(0);
-    if (nblk > 1) dma(1);
-    if (nblk > 2) dma(2);
+    if (nblk > 0) dma(IC<0>{}, 0);
+    if (nblk > 1) dma(IC<1>{}, 1);
+    if (nblk > 2) dma(IC<2>{}, 2);
     if (nblk > 2)
         vm_wait<2 * NDMA>();
     else if (nblk > 1)
@@ -598,30 +652,31 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
     else
         vm_wait<0>();
     block_barrier();
-    f32x16 s_cur;
+    f32x16 sA, sB;
 #pragma unroll
-    for (int r = 0; r < 16; r++) s_cur[r] = 0.0f;
+    for (int r = 0; r < 16; r++) sA[r] = 0.0f;
     if (wactive && nblk > 0) {
-        kread(0);
+        kread(IC<0>{});
         lgkm_wait_n<0>();
 #pragma unroll
         for (int j = 0; j < HD / 16; j++) {
             ready(kf[j]);
-            s_cur = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_cur, 0, 0, 0);
+            sA = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], sA, 0, 0, 0);
         }
     }
-    for (int b = 0; b < nblk; b++) {
-        // block b+1 landed (own loads; b+2's may fly), then everyone's; after
-        // the barrier nobody reads block b-1's buffer, which takes block b+3
+
+    // block b (stage st): scores in s_cur; leaves block b+1's scores in s_nx
+    // (on the last block, products of a stale stage that nobody uses)
+    auto step = [&](auto st, int b, f32x16 &s_cur, f32x16 &s_nx) {
+        constexpr int S = decltype(st)::value;
         if (b + 2 < nblk)
             vm_wait<NDMA>();
         else
             vm_wait<0>();
         block_barrier();
-        if (b + 3 < nblk) dma(b + 3);
-        if (!wactive) continue;
+        if (b + 3 < nblk) dma(IC<(S + 3) % NS>{}, b + 3);
+        if (!wactive) return;
         const int kb = c.k_lo + b * KB;
-        const uint32_t sb = (uint32_t)((b % NS) * SBYTES), sn = (uint32_t)(((b + 1) % NS) * SBYTES);
         if (kb + KB > c.k_hi) {
 #pragma unroll
             for (int r = 0; r < 16; r++) {
@@ -629,45 +684,17 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
                 s_cur[r] = key < c.k_hi ? s_cur[r] : -INFINITY;
             }
         }
-        // reads: block b+1's K (8; on the last block a stale buffer, unused) and
-        // the first half of block b's V group 0 (4): 12 in flight at most
-        kread(sn);
-        vread(sb, 0, 0);
-        vread(sb, 1, 0);
-        lgkm_wait_n<4>();
+        // row max (v_maximum3: no input quieting; a NaN score gives a NaN max,
+        // which reaches the output)
+        float mx = __builtin_elementwise_maximum(s_cur[0], s_cur[1]);
 #pragma unroll
-        for (int j = 0; j < HD / 16; j++) ready(kf[j]);
-        vread(sb, 2, 0);
-        vread(sb, 3, 0);
-
-        // scores of block b+1 (a dependent chain of MFMAs) and the softmax of
-        // block b (VALU) are independent: the scheduler overlaps them
-        f32x16 s_nx;
-#pragma unroll
-        for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < HD / 16; j++)
-            s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
-        float mx = fmaxf(fmaxf(fmaxf(s_cur[0], s_cur[1]), fmaxf(s_cur[2], s_cur[3])),
-                         fmaxf(fmaxf(s_cur[4], s_cur[5]), fmaxf(s_cur[6], s_cur[7])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s_cur[8], s_cur[9]), fmaxf(s_cur[10], s_cur[11])),
-                             fmaxf(fmaxf(s_cur[12], s_cur[13]), fmaxf(s_cur[14], s_cur[15]))));
-        const float m_new = fmaxf(m_run, max_halves(mx) * cs);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        // 2^x as the bare v_exp_f32: results below 2^-126 flush to 0, far
-        // below anything a row sum of at least 1 can register
-        float pv[16], rs = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            pv[r] = __builtin_amdgcn_exp2f(fmaf(s_cur[r], cs, -m_use));
-            rs += pv[r];
+        for (int r = 2; r < 16; r++) mx = __builtin_elementwise_maximum(mx, s_cur[r]);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        f16x8 pb[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; s2++)
-#pragma unroll
-            for (int e = 0; e < 8; e++) pb[s2][e] = (_Float16)pv[8 * s2 + e];
-
+        const float m_new = __builtin_elementwise_maximum(m_run, mx * cs);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         // the output and the row sum follow the new max only when it grew
         if (__any(m_new > m_run)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -678,25 +705,75 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16p_kernel(AttnArgs a) {
                 for (int r = 0; r < 16; r++) o[d][r] *= alpha;
         }
         m_run = m_new;
-        l_lane += rs;
+
+        // reads: block b+1's K (8) and the first half of block b's V group 0 (4)
+        kread(IC<(S + 1) % NS>{});
+        vread(st, 0, IC<0>{});
+        vread(st, 1, IC<0>{});
+        lgkm_wait_n<4>();
 #pragma unroll
-        for (int s2 = 0; s2 < 2; s2++) {
-            lgkm_wait_n<0>();
+        for (int j = 0; j < HD / 16; j++) ready(kf[j]);
+        vread(st, 2, IC<0>{});
+        vread(st, 3, IC<0>{});
+        // scores of block b+1 (a dependent MFMA chain) interleaved with the
+        // exponentials of block b (2^x as the bare v_exp_f32: results below
+        // 2^-126 flush to 0)
 #pragma unroll
-            for (int d = 0; d < HD / 32; d++) {
-                ready(vf[d][s2][0]);
-                ready(vf[d][s2][1]);
+        for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++)
+            s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
+        f16x8 pb[2];
+        float rs = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
+                                  (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
+                pb[s2][e] = pr[0];
+                pb[s2][e + 1] = pr[1];
+                rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
             }
-            if (s2 == 0)
 #pragma unroll
-                for (int d = 0; d < HD / 32; d++) vread(sb, d, 1);
-#pragma unroll
-            for (int d = 0; d < HD / 32; d++) {
-                const u32x4 vv = {vf[d][s2][0][0], vf[d][s2][0][1], vf[d][s2][1][0], vf[d][s2][1][1]};
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[s2], o[d], 0, 0, 0);
-            }
+        for (int j = 0; j < HD / 16; j++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
         }
-        s_cur = s_nx;
+        l_lane += rs;
+        lgkm_wait_n<0>();
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) {
+            ready(vf[d][0][0]);
+            ready(vf[d][0][1]);
+        }
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) vread(st, d, IC<1>{});
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) {
+            const u32x4 vv = {vf[d][0][0][0], vf[d][0][0][1], vf[d][0][1][0], vf[d][0][1][1]};
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[0], o[d], 0, 0, 0);
+        }
+        lgkm_wait_n<0>();
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) {
+            ready(vf[d][1][0]);
+            ready(vf[d][1][1]);
+        }
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) {
+            const u32x4 vv = {vf[d][1][0][0], vf[d][1][0][1], vf[d][1][1][0], vf[d][1][1][1]};
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[1], o[d], 0, 0, 0);
+        }
+    };
+    for (int b = 0; b < nblk; b += NS) {
+        step(IC<0>{}, b, sA, sB);
+        if (b + 1 >= nblk) break;
+        step(IC<1>{}, b + 1, sB, sA);
+        if (b + 2 >= nblk) break;
+        step(IC<2>{}, b + 2, sA, sB);
+        if (b + 3 >= nblk) break;
+        step(IC<3>{}, b + 3, sB, sA);
     }
     const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
     if (qvalid) {
@@ -736,10 +813,10 @@ hipError_t launch_f16d(AttnArgs a, hipStream_t s) {
 }
 
 template <int NW, int MINW>
-hipError_t launch_f16p(AttnArgs a, hipStream_t s) {
+hipError_t launch_f16s(AttnArgs a, hipStream_t s) {
     const uint32_t tiles = plan_tiles(a, 32 * NW);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((attn_f16p_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
