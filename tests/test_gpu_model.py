@@ -124,10 +124,12 @@ def test_packed_images_equal_separate():
         r += g * g
 
 
-@pytest.mark.parametrize("name", ["zimage_dit_cfg_8448", "zimage_dit_mod_1056"])
-def test_cfg_pair_equals_two_singles(name):
-    """The CFG batch-2 program gives each item the bits of its single forward."""
-    kw = dict(layers=2, grid=4, ncap=8, overrides=DIT_SMALL)
+@pytest.mark.parametrize("name,grid,ncap", [("zimage_dit_cfg_8448", 4, 8), ("zimage_dit_mod_1056", 4, 8),
+                                            ("zimage_dit_cfg_8448", 32, 32)])
+def test_cfg_pair_equals_two_singles(name, grid, ncap):
+    """The CFG batch-2 program gives each item the bits of its single forward
+    (at 32x32 + 32 rows per item the attention takes key splits)."""
+    kw = dict(layers=2, grid=grid, ncap=ncap, overrides=DIT_SMALL)
     w = wl.make(name, cfg_pair=True, **kw)
     pair = run(w)
     for i, rr in enumerate(w.items):

@@ -358,29 +358,33 @@ def test_attention_packed_equals_separate(path):
 
 
 KEY_SPLIT_CASES = [
-    # (items, nq, nkv, hd): each windowless item too short to fill the GPU alone
-    ([[(0, 1024)]], 12, 12, 64),                     # the 1024-row ViT: 8 chunks of 128 keys
-    ([[(0, 1000)]], 12, 4, 64),                      # 7 chunks, the last one ragged (40 keys)
-    ([[(0, 600), (700, 300)]], 4, 4, 64),            # two ranges, chunks across the seam
-    ([[(0, 800)], [(800, 100)], [(900, 300)]], 4, 2, 128),  # split and unsplit items in one launch
+    # (path, items, nq, nkv, hd): each windowless item too short to fill the GPU alone
+    (B.ENC_F32, [[(0, 1024)]], 12, 12, 64),             # the 1024-row ViT: 8 chunks of 128 keys
+    (B.ENC_F32, [[(0, 1000)]], 12, 4, 64),              # 7 chunks, the last one ragged (40 keys)
+    (B.ENC_F32, [[(0, 600), (700, 300)]], 4, 4, 64),    # two ranges, chunks across the seam
+    (B.ENC_F32, [[(0, 800)], [(800, 100)], [(900, 300)]], 4, 2, 128),  # split and unsplit items
 ]
 
 
-@pytest.mark.parametrize("items,nq,nkv,hd", KEY_SPLIT_CASES)
-def test_attention_f32_key_split(items, nq, nkv, hd):
-    say(f"attention f32 key split items={items} nq={nq} nkv={nkv} hd={hd}")
+@pytest.mark.parametrize("path,items,nq,nkv,hd", KEY_SPLIT_CASES)
+def test_attention_key_split(path, items, nq, nkv, hd):
+    f16 = path == B.ENC_I8F16
+    say(f"attention key split path={path} items={items} nq={nq} nkv={nkv} hd={hd}")
     rows = max(r0 + n for rr in items for r0, n in rr)
     rng = np.random.default_rng(rows + nq + hd)
-    p = _panel(rng, rows, nq, nkv, hd, qscale=0.5)
+    p = _panel(rng, rows, nq, nkv, hd, f16=f16, qscale=0.5)
     scale = 1.0 / np.sqrt(hd)
     d = B.attention_desc(None, None, nq, nkv, hd, scale, 0, ld=p.shape[1], ldo=nq * hd,
-                         rows=rows)
+                         rows=rows, path=path)
     assert B.attention_workspace_bytes(d, items) > 0, "the case must take the split path"
     P = to_dev(p)
-    out = torch.full((rows, nq * hd), 7.0, dtype=torch.float32, device=DEV)
-    B.attention_items(P, out, items, nq, nkv, hd, scale, 0)
+    dt = torch.float16 if f16 else torch.float32
+    out = torch.full((rows, nq * hd), 7.0, dtype=dt, device=DEV)
+    B.attention_items(P, out, items, nq, nkv, hd, scale, 0, path=path)
     q, k, v = _split(p, nq, nkv, hd)
     ref = O.attention(items, q, k, v, nq, nkv, hd, scale, 0)
+    if f16:
+        ref = np.vectorize(O.round_f16)(ref)
     covered = np.zeros(rows, bool)
     for rr in items:
         for r0, n in rr:
@@ -390,27 +394,32 @@ def test_attention_f32_key_split(items, nq, nkv, hd):
     err = row_rel_err(got[covered], ref[covered])
     # the unsplit kernel (no workspace) computes the same softmax in one pass
     out1 = torch.full_like(out, 7.0)
-    B.attention_items(P, out1, items, nq, nkv, hd, scale, 0, ws=None)
+    B.attention_items(P, out1, items, nq, nkv, hd, scale, 0, ws=None, path=path)
     err1 = row_rel_err(got[covered], host(out1)[covered].astype(np.float64))
+    tol = TOL_I8F16 if f16 else TOL_F32
     say(f"  err vs oracle {err:.2e}, vs unsplit {err1:.2e}")
-    assert err <= TOL_F32 and err1 <= TOL_F32
+    assert err <= tol and err1 <= tol
     out2 = torch.full_like(out, 7.0)
-    B.attention_items(P, out2, items, nq, nkv, hd, scale, 0)
+    B.attention_items(P, out2, items, nq, nkv, hd, scale, 0, path=path)
     assert torch.equal(out, out2), "key-split attention is not deterministic"
 
 
-def test_attention_key_split_packed_equals_separate():
-    nq, hd = 4, 64
+@pytest.mark.parametrize("path,hd", [(B.ENC_F32, 64), (B.ENC_I8F16, 128)])
+def test_attention_packed_equals_separate_long_items(path, hd):
+    """Items long enough for the f32 key split (the f16 path runs them unsplit)."""
+    f16 = path == B.ENC_I8F16
+    nq = 4
     items = [[(0, 1024)], [(1024, 700)], [(1724, 90)]]
     rows = 1814
     rng = np.random.default_rng(11)
-    p = _panel(rng, rows, nq, nq, hd)
-    out = torch.zeros((rows, nq * hd), dtype=torch.float32, device=DEV)
-    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.125, 0)
+    p = _panel(rng, rows, nq, nq, hd, f16=f16)
+    dt = torch.float16 if f16 else torch.float32
+    out = torch.zeros((rows, nq * hd), dtype=dt, device=DEV)
+    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.125, 0, path=path)
     for rr in items:
         (r0, n), = rr
-        o1 = torch.zeros((n, nq * hd), dtype=torch.float32, device=DEV)
-        B.attention_items(to_dev(p[r0:r0 + n]), o1, [[(0, n)]], nq, nq, hd, 0.125, 0)
+        o1 = torch.zeros((n, nq * hd), dtype=dt, device=DEV)
+        B.attention_items(to_dev(p[r0:r0 + n]), o1, [[(0, n)]], nq, nq, hd, 0.125, 0, path=path)
         assert torch.equal(o1, out[r0:r0 + n])
 
 
