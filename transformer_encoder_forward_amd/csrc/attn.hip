@@ -66,16 +66,19 @@ __device__ __forceinline__ bool block_active(int q0, int q1, int kb, int k_hi, u
 // rows, one group) spread over all banks.
 __device__ __forceinline__ int vt_col(int row, int g) { return 4 * (g ^ ((row >> 4) & 7)); }
 
-// Online-softmax update of one lane's 16 scores (query = lane%32).  s holds
-// raw dot products; masked keys become -inf.  Returns p in place.  2^x is the
-// bare v_exp_f32 (results below 2^-126 flush to 0, far below anything a row
-// sum of at least 1 registers).
+// Online-softmax update of one lane's 16 scores (query = lane%32).  sv holds
+// scaled dot products; masked keys are -inf.  Returns p in place.  The running
+// max moves, to this block's max, only when that passes it by more than 8 (log2
+// units): p stays at most 256, the factor alpha is exactly 1 otherwise, and the
+// quotient o / l does not depend on where m sits.  2^x is the bare v_exp_f32
+// (results below 2^-126 flush to 0, far below anything a row sum of at least 1
+// registers).
 __device__ __forceinline__ float softmax_step(float (&sv)[16], float &m_run, float &l_run) {
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; r++) mx = fmaxf(mx, sv[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = mx > m_run + 8.0f ? mx : m_run;
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float rs = 0.0f;
@@ -202,9 +205,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_f32_kernel(AttnArgs a) {
             }
             const float m_old = m_run;
             const float alpha = softmax_step(sv, m_run, l_run);
-            // o is rescaled only when some query's max grew (else alpha is 1 or
-            // o is still 0)
-            if (__any(m_run > m_old)) {
+            // o is rescaled only when some query's max moved (else alpha is 1)
+            if (__any(m_run != m_old)) {
 #pragma unroll
                 for (int d = 0; d < HD / 32; d++)
 #pragma unroll

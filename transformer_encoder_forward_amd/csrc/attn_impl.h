@@ -528,7 +528,10 @@ using IC = std::integral_constant<int, V>;
 //    denominator see the same rounded p;
 //  - the row max takes three scores per instruction (v_maximum3, no input
 //    quieting);
-//  - the output is rescaled only when some query's running max grew.
+//  - the running max moves only when a block's max passes it by more than 8
+//    (in log2 units), and then to that block's max: p = 2^(s c - m) stays at
+//    most 256 (exact in f16's range), the output is rescaled only on such a
+//    move, and the quotient o / l does not depend on where m sits.
 // Iteration b computes the scores of block b+1 (a dependent MFMA chain,
 // interleaved with the exponentials of block b by scheduling groups), then
 // P V of block b; block b+3 is staged meanwhile.  Keys past the item occur only
@@ -693,18 +696,21 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        const float m_new = __builtin_elementwise_maximum(m_run, mx * cs);
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        // the output and the row sum follow the new max only when it grew
-        if (__any(m_new > m_run)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        // the running max moves (to this block's max) only when it is passed by
+        // more than 8; the output and the row sum follow it then
+        const float mb = mx * cs;
+        const bool up = mb > m_run + 8.0f;
+        if (__any(up)) {
+            const float m_new = up ? mb : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_lane *= alpha;
 #pragma unroll
             for (int d = 0; d < HD / 32; d++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
         // reads: block b+1's K (8) and the first half of block b's V group 0 (4)
         kread(IC<(S + 1) % NS>{});
