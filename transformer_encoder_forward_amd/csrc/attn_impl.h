@@ -496,22 +496,6 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
     }
 }
 
-// LDS reads at a base address plus an immediate byte offset.
-template <int OFF>
-__device__ __forceinline__ u32x4 ds_read16_at(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
-    return v;
-}
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_read8_tr16_at(uint32_t addr) {
-    u32x2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
-    return v;
-}
-
-template <int V>
-using IC = std::integral_constant<int, V>;
 
 // The attention without a window at hd 128, software-pipelined within each
 // wave, with K/V staged as in attn_f16d_kernel (direct global -> LDS loads, a

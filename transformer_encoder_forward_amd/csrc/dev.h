@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace enc {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -78,6 +80,24 @@ __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     return v;
 }
 
+// LDS reads at a base address plus an immediate byte offset (0..65535).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset");
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+    return v;
+}
+
+// N reads at OFF, OFF + STRIDE, ... into d[0..N).
+template <int OFF, int STRIDE, int N>
+__device__ __forceinline__ void ds_read16_run(u32x4 *d, uint32_t addr) {
+    if constexpr (N > 0) {
+        d[0] = ds_read16_at<OFF>(addr);
+        ds_read16_run<OFF + STRIDE, STRIDE, N - 1>(d + 1, addr);
+    }
+}
+
 // Transposing 64-bit read of 16-bit data: within each group of 16 lanes, lane i
 // receives element i % 4 of the four 64-bit rows addressed by lanes i/4 + 4e,
 // e = 0..3 (the layout measured on gfx950).
@@ -86,6 +106,18 @@ __device__ __forceinline__ u32x2 ds_read8_tr16(uint32_t addr) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
     return v;
 }
+
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read8_tr16_at(uint32_t addr) {
+    static_assert(OFF >= 0 && OFF < 65536, "DS offset");
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+    return v;
+}
+
+// A compile-time integer as a value (stage indices of unrolled loops).
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // Wait until at most N LDS reads (of this wave) are in flight.  The registers
 // the reads filled are then passed through empty asm statements (see `ready`):

@@ -809,25 +809,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
 
     // fragment addresses: X row wr*(BM/WGM) + 32 i + li, chunk 4 hf + kk; W
     // row wc*(BN/WGN) + 32 j + li, chunk 2 hf + p (p = kk / 2, one read per two
-    // k-steps)
+    // k-steps).  A read group is one per-lane base plus the stage offset (one
+    // add) and immediates for i / j.
     const uint32_t lds0 = lds_offset(smem);
     const uint32_t arow = lds0 + (uint32_t)(wr * (BM / WGM) + li) * 128u;
     const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * (BN / WGN) + li) * 64u;
     const int sa = (li >> 1) & 7, sb = (li >> 2) & 3;
-    uint32_t asw[4], bsw[2];
+    uint32_t abase[4], bbase[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; kk++) asw[kk] = (uint32_t)(((4 * hf + kk) ^ sa) * 16);
+    for (int kk = 0; kk < 4; kk++) abase[kk] = arow + (uint32_t)(((4 * hf + kk) ^ sa) * 16);
 #pragma unroll
-    for (int p = 0; p < 2; p++) bsw[p] = (uint32_t)(((2 * hf + p) ^ sb) * 16);
+    for (int p = 0; p < 2; p++) bbase[p] = brow + (uint32_t)(((2 * hf + p) ^ sb) * 16);
 
     u32x4 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
     auto read_a = [&](u32x4 (&d)[FM], int b, int kk) {
-#pragma unroll
-        for (int i = 0; i < FM; i++) d[i] = ds_read16(arow + b * S_BYTES + 4096 * i + asw[kk]);
+        ds_read16_run<0, 4096, FM>(d, abase[kk] + (uint32_t)(b * S_BYTES));
     };
     auto read_b = [&](u32x4 (&d)[FN], int b, int p) {
-#pragma unroll
-        for (int j = 0; j < FN; j++) d[j] = ds_read16(brow + b * S_BYTES + 2048 * j + bsw[p]);
+        ds_read16_run<0, 2048, FN>(d, bbase[p] + (uint32_t)(b * S_BYTES));
     };
 
     f32x16 acc[FM][FN];
