@@ -3,7 +3,8 @@
 // The tile shape is chosen per launch from the problem size.  f32: large
 // problems take 256 x 128 tiles (gated: 256 rows x 128 outputs), middling ones
 // 128 x 128, small ones (too few 128 x 128 tiles to fill the 256 CUs twice
-// over) 64 x 64 tiles.  int8 x f16: large problems take
+// over) 64 x 64 tiles; plain GEMMs with K % 32 == 0 are fed by direct
+// global -> LDS loads.  int8 x f16: large problems take
 // the kernel fed by direct global -> LDS loads (256 x 256 tiles, or 128 x 256
 // when there are few of those), and K % 64 != 0 the register-staged 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
@@ -29,41 +30,48 @@ constexpr uint32_t kWideF32 = 240;    // about one 256 x 128 tile per CU
 
 }  // namespace
 
-// f32, measured on the 16 057-row text encoder (min of interleaved runs): the
-// 256 x 128 tile of 8 waves with 64 x 64 each beats 64 x 64 tiles by 8% on the
-// down projection and ties elsewhere; the gated 256 x (128 + 128) tile of 16
-// waves beats 128 x (64 + 64) by 6%.
+static bool kmul(const GemmArgs &a, uint32_t q) {
+    for (uint32_t i = 0; i < a.nitems; i++)
+        if (a.items[i].k % q) return false;
+    return true;
+}
+
+// f32, measured on the 16 057-row text encoder and the 1024-row ViT (min of
+// interleaved runs, same-run comparisons):
+//  - plain GEMMs with K % 32 == 0 take the direct-to-LDS kernel: 256 x 128
+//    tiles of 16 waves (64 x 32 each) beat the register-staged 256 x 128 tile
+//    by 8-13% on the text encoder's q/k/v, O and down projections; 64 x 64
+//    tiles (4 waves, up to four blocks per CU) beat the register-staged 64 x 64
+//    by 4-12% on the ViT's;
+//  - the gated 256 x (128 + 128) register-staged tile of 16 waves beats
+//    128 x (64 + 64) by 6% and the direct-to-LDS gated tiles by 1-2%.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
     if (a.flags & (gemm::kGateGelu | gemm::kGateSilu)) {
         if (tiles_of(a, 256, 128) >= kWideF32) return gemm::launch_gated<256, 256, 32, 4, false, 1>(a, s);
         if (tiles_of(a, 128, 64) >= kBigTiles) return gemm::launch_gated<128, 128, 32, 2, false, 2>(a, s);
         return gemm::launch_gated<64, 128, 32, 2, false, 4>(a, s);
     }
-    if (tiles_of(a, 256, 128) >= kWideF32) return gemm::launch<256, 128, 32, 4, 2, false, 1>(a, s);
+    const bool direct = kmul(a, 32);
+    if (tiles_of(a, 256, 128) >= kWideF32)
+        return direct ? gemm::launch_f32d<256, 128, 4, 4, 1, false>(a, s) : gemm::launch<256, 128, 32, 4, 2, false, 1>(a, s);
     if (tiles_of(a, 128, 128) >= kBigTiles) return gemm::launch<128, 128, 32, 2, 4, false, 1>(a, s);
-    return gemm::launch_v2<64, 64, 32, 2, 2, false, 4>(a, s);
+    return direct ? gemm::launch_f32d<64, 64, 2, 2, 4, false>(a, s) : gemm::launch_v2<64, 64, 32, 2, 2, false, 4>(a, s);
 }
 
 namespace {
 
-// The direct-to-LDS kernel needs K % 64 == 0.  256 x 256 tiles (8 waves of
+// The direct-to-LDS int8 kernel needs K % 64 == 0.  256 x 256 tiles (8 waves of
 // 128 x 64, one block per CU) when the launch has at least 128 of them; fewer
 // (the output projections of a 1056-row DiT batch: 75 tiles) take 128 x 256
 // tiles (8 waves of 64 x 64), which measured 10-40% faster there.  Otherwise
 // the register-staged 128 x 128 kernel.  All sum in the same K order.
-bool k64(const GemmArgs &a) {
-    for (uint32_t i = 0; i < a.nitems; i++)
-        if (a.items[i].k % 64) return false;
-    return true;
-}
-
 constexpr uint32_t kWideTiles = 128;
 
 }  // namespace
 
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
-    if (k64(a)) {
+    if (kmul(a, 64)) {
         if (tiles_of(a, 256, gated ? 128 : 256) >= kWideTiles)
             return gated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
                          : gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);

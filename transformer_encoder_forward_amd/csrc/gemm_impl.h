@@ -931,5 +931,204 @@ hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// f32 GEMM fed by direct global -> LDS loads, the counterpart of
+// gemm_q8d_kernel for the FP32 path.  Three LDS stages of 32 K each: the loads
+// of stage s+3 are issued once every wave has finished reading stage s, and no
+// register holds staged data.  X and W rows are 32 floats (128 bytes = 8
+// chunks of 4 floats); row r keeps chunk c at position c ^ ((r >> 1) & 7), so
+// the 16 consecutive lanes of a fragment read hit 16 distinct bank groups.
+// Fragments are read with ds_read_b128 in inline assembly (one per-lane base
+// per chunk, the stage and the 32-row block as immediates or one add) and
+// awaited explicitly, as in the int8 kernel.
+//
+// Same K order as gemm_kernel<.., 32, .., false, ..>: stage 32, lane half h
+// owns k in [16h, 16h + 16), k-step kk pairs k = kk (half 0) with 16 + kk
+// (half 1); so every f32 instantiation gives the same bits.  Requires K % 32
+// == 0.  Rows past n and columns past m load clamped (finite) rows and are
+// never stored.  Gated: each wave column holds 32 gate and 32 up rows of the
+// same 32 output columns (BN / WGN == 64); the epilogue forms act(g) * u.
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArgs a) {
+    constexpr int NW = WGM * WGN, BK = 32, NS = 3;
+    constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
+    constexpr int A_BYTES = BM * BK * 4, S_BYTES = A_BYTES + BN * BK * 4;
+    constexpr int AL = A_BYTES / 1024 / NW, BL = BN * BK * 4 / 1024 / NW;  // loads per wave per stage
+    constexpr int NDMA = AL + BL;
+    static_assert(AL >= 1 && BL >= 1 && AL * 1024 * NW == A_BYTES && BL * 1024 * NW == BN * BK * 4, "loads");
+    static_assert(FM >= 1 && FN >= 1 && (!GATED || BN / WGN == 64), "tile");
+    static_assert(NS * S_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
+
+    TileCtx t;
+    if (!locate<BM, BN>(a, t, GATED ? BN / 2 : BN)) return;
+    const float *wg = reinterpret_cast<const float *>(t.w), *wu = wg;
+    if constexpr (GATED) {
+        wu = reinterpret_cast<const float *>(a.w[1]);
+#pragma unroll
+        for (int s2 = 1; s2 < kMaxGemmItems; s2++)
+            if ((int)t.it.slot + 1 == s2) wu = reinterpret_cast<const float *>(a.w[s2]);
+    }
+    const int n = t.it.n, m = t.it.m, K = t.it.k;
+    const float *X = reinterpret_cast<const float *>(a.x) + t.it.x_off;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, hf = lane >> 5;
+    const int wr = wave / WGN, wc = wave % WGN;
+
+    // sources of this lane's load instructions (k offset added per stage):
+    // load q of this wave covers tile rows 8 (L wave + q) .. + 7, lane l row
+    // + l/8, position l%8 holding chunk (l%8) ^ ((row >> 1) & 7)
+    const float *asrc[AL];
+#pragma unroll
+    for (int q = 0; q < AL; q++) {
+        const int r = 8 * (AL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        asrc[q] = X + (size_t)min(t.row0 + r, n - 1) * t.it.ldx + 4 * c;
+    }
+    const float *bsrc[BL];
+#pragma unroll
+    for (int q = 0; q < BL; q++) {
+        const int r = 8 * (BL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        const float *w = wg;
+        int col = t.col0 + r;
+        if constexpr (GATED) {
+            w = ((r >> 5) & 1) ? wu : wg;
+            col = t.col0 + (r >> 6) * 32 + (r & 31);
+        }
+        bsrc[q] = w + (size_t)min(col, m - 1) * K + 4 * c;
+    }
+    auto dma = [&](int s) {
+        uint8_t *buf = smem + (s % NS) * S_BYTES;
+        const int k0 = s * BK;
+#pragma unroll
+        for (int q = 0; q < AL; q++)
+            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(asrc[q] + k0), ENC_SHARED(buf + (AL * wave + q) * 1024), 16,
+                                             0, 0);
+#pragma unroll
+        for (int q = 0; q < BL; q++)
+            __builtin_amdgcn_global_load_lds(ENC_GLOBAL(bsrc[q] + k0),
+                                             ENC_SHARED(buf + A_BYTES + (BL * wave + q) * 1024), 16, 0, 0);
+    };
+
+    // fragment q (k = 16 hf + 4q .. + 3) of X row wr*(BM/WGM) + 32 i + li and
+    // of W row wc*(BN/WGN) + 32 j + li: chunk 4 hf + q; 32 rows = 4096 bytes
+    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t arow = lds0 + (uint32_t)(wr * (BM / WGM) + li) * 128u;
+    const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * (BN / WGN) + li) * 128u;
+    const int sw = (li >> 1) & 7;
+    uint32_t abase[4], bbase[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        abase[q] = arow + (uint32_t)(((4 * hf + q) ^ sw) * 16);
+        bbase[q] = brow + (uint32_t)(((4 * hf + q) ^ sw) * 16);
+    }
+    u32x4 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+    auto read = [&](u32x4 (&da)[FM], u32x4 (&db)[FN], int b, int q) {
+        const uint32_t so = (uint32_t)(b * S_BYTES);
+        ds_read16_run<0, 4096, FM>(da, abase[q] + so);
+        ds_read16_run<0, 4096, FN>(db, bbase[q] + so);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+    // k-steps 4q .. 4q+3 of the stage from fragment q.  (Each element is copied
+    // out before the reinterpretation: a bit_cast of a vector element
+    // expression compiles to element 0 here.)
+    auto mma = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN]) {
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++) {
+                    const uint32_t ua = fa[i][e], ub = fb[j][e];
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ua), __uint_as_float(ub),
+                                                                    acc[i][j], 0, 0, 0);
+                }
+    };
+
+    const int nst = K / BK;
+    dma(0);
+    if (nst > 1) dma(1);
+    if (nst > 2) dma(2);
+    if (nst > 2)
+        vm_wait<2 * NDMA>();
+    else if (nst > 1)
+        vm_wait<NDMA>();
+    else
+        vm_wait<0>();
+    block_barrier();
+    read(fa0, fb0, 0, 0);
+    for (int s = 0; s < nst; s++) {
+        const int b = s % NS;
+        read(fa1, fb1, b, 1);
+        lgkm_wait_n<FM + FN>();  // fragment 0 landed (fragment 1 may still be in flight)
+        frag_ready(fa0, fb0);
+        mma(fa0, fb0);
+        read(fa0, fb0, b, 2);
+        lgkm_wait_n<FM + FN>();
+        frag_ready(fa1, fb1);
+        mma(fa1, fb1);
+        read(fa1, fb1, b, 3);
+        lgkm_wait_n<FM + FN>();
+        frag_ready(fa0, fb0);
+        mma(fa0, fb0);
+        // stage s+1 landed (own loads), own reads of buffer b done; after the
+        // barrier every wave's are, so b takes stage s+3
+        if (s + 2 < nst)
+            vm_wait<NDMA>();
+        else
+            vm_wait<0>();
+        lgkm_wait_n<0>();
+        frag_ready(fa1, fb1);
+        block_barrier();
+        if (s + 3 < nst) dma(s + 3);
+        if (s + 1 < nst) read(fa0, fb0, (s + 1) % NS, 0);
+        mma(fa1, fb1);
+    }
+
+    if constexpr (!GATED) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                store_block<false>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
+                                   lane);
+    } else {
+        // lane holds gate and up of the same (row, column)
+        const int c = t.col0 + wc * 32 + li;
+        if (c >= m) return;
+        const float mg = a.alpha, mu = a.alpha;
+        const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
+        const float oc = a.ycol ? a.ycol[c] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (row >= n) continue;
+                const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
+                const float v = (gelu ? gelu_tanh(g) : silu(g)) * u * oc * a.yscale;
+                const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
+                if (f16)
+                    reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+                else
+                    reinterpret_cast<float *>(a.y)[off] = v;
+            }
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+hipError_t launch_f32d(GemmArgs g, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
+    if (!tiles) return hipSuccess;
+    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    return hipGetLastError();
+}
+
 }  // namespace gemm
 }  // namespace enc
