@@ -933,9 +933,10 @@ hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // f32 GEMM fed by direct global -> LDS loads, the counterpart of
-// gemm_q8d_kernel for the FP32 path.  Three LDS stages of 32 K each: the loads
-// of stage s+3 are issued once every wave has finished reading stage s, and no
-// register holds staged data.  X and W rows are 32 floats (128 bytes = 8
+// gemm_q8d_kernel for the FP32 path.  NS (3, or 2 for tiles whose stage is too
+// large for three) LDS stages of 32 K each: the loads of stage s+NS are issued
+// once every wave has finished reading stage s, and no register holds staged
+// data.  X and W rows are 32 floats (128 bytes = 8
 // chunks of 4 floats); row r keeps chunk c at position c ^ ((r >> 1) & 7), so
 // the 16 consecutive lanes of a fragment read hit 16 distinct bank groups.
 // Fragments are read with ds_read_b128 in inline assembly (one per-lane base
@@ -948,9 +949,10 @@ hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
 // == 0.  Rows past n and columns past m load clamped (finite) rows and are
 // never stored.  Gated: each wave column holds 32 gate and 32 up rows of the
 // same 32 output columns (BN / WGN == 64); the epilogue forms act(g) * u.
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArgs a) {
-    constexpr int NW = WGM * WGN, BK = 32, NS = 3;
+    constexpr int NW = WGM * WGN, BK = 32;
+    static_assert(NS == 2 || NS == 3, "stages");
     constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
     constexpr int A_BYTES = BM * BK * 4, S_BYTES = A_BYTES + BN * BK * 4;
     constexpr int AL = A_BYTES / 1024 / NW, BL = BN * BK * 4 / 1024 / NW;  // loads per wave per stage
@@ -1054,8 +1056,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     const int nst = K / BK;
     dma(0);
     if (nst > 1) dma(1);
-    if (nst > 2) dma(2);
-    if (nst > 2)
+    if (NS > 2 && nst > 2) dma(2);
+    if (NS > 2 && nst > 2)
         vm_wait<2 * NDMA>();
     else if (nst > 1)
         vm_wait<NDMA>();
@@ -1077,16 +1079,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
         lgkm_wait_n<FM + FN>();
         frag_ready(fa0, fb0);
         mma(fa0, fb0);
-        // stage s+1 landed (own loads), own reads of buffer b done; after the
-        // barrier every wave's are, so b takes stage s+3
-        if (s + 2 < nst)
+        // stage s+1 landed (own loads; with three stages, s+2's may fly), own
+        // reads of buffer b done; after the barrier every wave's are, so b
+        // takes stage s+NS
+        if (NS > 2 && s + 2 < nst)
             vm_wait<NDMA>();
         else
             vm_wait<0>();
         lgkm_wait_n<0>();
         frag_ready(fa1, fb1);
         block_barrier();
-        if (s + 3 < nst) dma(s + 3);
+        if (s + NS < nst) dma(s + NS);
         if (s + 1 < nst) read(fa0, fb0, (s + 1) % NS, 0);
         mma(fa1, fb1);
     }
@@ -1122,11 +1125,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 hipError_t launch_f32d(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS>), dim3(tiles), dim3(64 * WGM * WGN), 0, s,
+                       g);
     return hipGetLastError();
 }
 
