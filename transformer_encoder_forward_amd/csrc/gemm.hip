@@ -45,7 +45,9 @@ static bool kmul(const GemmArgs &a, uint32_t q) {
 //    by 4-12% on the ViT's;
 //  - gated GEMMs of large launches take the direct-to-LDS 256 x (128 + 128)
 //    tile of 16 waves with two 64 KB stages: 6% faster than the register-staged
-//    tile of the same shape, which in turn beats 128 x (64 + 64) by 6%.
+//    tile of the same shape, which in turn beats 128 x (64 + 64) by 6%; small
+//    ones (the 2176-row vision tower) the direct-to-LDS 64 x (64 + 64) tile, 7%
+//    faster than the register-staged one.
 hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
     const bool direct = kmul(a, 32);
     if (a.flags & (gemm::kGateGelu | gemm::kGateSilu)) {
@@ -53,7 +55,7 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
             return direct ? gemm::launch_f32d<256, 256, 4, 4, 1, true, 2>(a, s)
                           : gemm::launch_gated<256, 256, 32, 4, false, 1>(a, s);
         if (tiles_of(a, 128, 64) >= kBigTiles) return gemm::launch_gated<128, 128, 32, 2, false, 2>(a, s);
-        return gemm::launch_gated<64, 128, 32, 2, false, 4>(a, s);
+        return direct ? gemm::launch_f32d<64, 128, 2, 2, 4, true>(a, s) : gemm::launch_gated<64, 128, 32, 2, false, 4>(a, s);
     }
     if (tiles_of(a, 256, 128) >= kWideF32)
         return direct ? gemm::launch_f32d<256, 128, 4, 4, 1, false>(a, s) : gemm::launch<256, 128, 32, 4, 2, false, 1>(a, s);
