@@ -92,18 +92,24 @@ def test_gemm_f32_gelu_epilogue():
     assert row_rel_err(host(Y), ref) <= TOL_F32
 
 
-def test_gemm_packed_rows_bit_identical():
-    """A row's output bits do not depend on how many rows share the launch."""
-    rng = np.random.default_rng(6)
-    k, m = 512, 300
-    x = rng.normal(0, 1, (900, k)).astype(np.float32)
-    w = rng.normal(0, 0.02, (m, k)).astype(np.float32)
-    W = to_dev(w)
-    Yall = torch.empty((900, m), dtype=torch.float32, device=DEV)
-    B.gemm_items(to_dev(x), Yall, [W], [(900, m, k, k, m, 0, 0, 0)])
+@pytest.mark.parametrize("n,m,k,gated", [
+    (900, 300, 512, False),      # small launches only (64 x 64, direct loads)
+    (8192, 1536, 512, False),    # 256 x 128 direct-loaded tiles vs the 64 x 64 ones
+    (8192, 1536, 100, False),    # K % 32 != 0: the register-staged 256 x 128 vs 64 x 64
+    (8192, 2048, 512, True),     # gated: 256 x (128 + 128) direct vs 64 x (64 + 64) direct
+    (8192, 2048, 100, True)])    # gated, register-staged tiles
+def test_gemm_f32_packed_rows_bit_identical(n, m, k, gated):
+    """A row's output bits do not depend on how many rows share the launch, so
+    not on which tile shape or staging the launch size selects."""
+    rng = np.random.default_rng(6 + k)
+    x = rng.normal(0, 1, (n, k)).astype(np.float32)
+    ws = [to_dev(rng.normal(0, 0.02, (m, k)).astype(np.float32)) for _ in range(1 + gated)]
+    flags = B.ENC_EPI_GATE_GELU_TANH if gated else 0
+    Yall = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(to_dev(x), Yall, ws, [(n, m, k, k, m, 0, 0, 0)], flags=flags)
     for r0, r1 in ((0, 1), (129, 200), (700, 900)):
         Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
-        B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)])
+        B.gemm_items(to_dev(x[r0:r1]), Y, ws, [(r1 - r0, m, k, k, m, 0, 0, 0)], flags=flags)
         assert torch.equal(Y, Yall[r0:r1])
 
 

@@ -1,10 +1,10 @@
 // Launchers of the item-table GEMM (kernel templates in gemm_impl.h).
 //
-// The tile shape is chosen per launch from the problem size.  f32: large
-// problems take 256 x 128 tiles (gated: 256 rows x 128 outputs), middling ones
-// 128 x 128, small ones (too few 128 x 128 tiles to fill the 256 CUs twice
-// over) 64 x 64 tiles; plain GEMMs with K % 32 == 0 are fed by direct
-// global -> LDS loads.  int8 x f16: large problems take
+// The tile shape is chosen per launch from the problem size.  f32: launches
+// with about one 256 x 128 tile per CU or more take 256 x 128 tiles (gated: 256
+// rows x 128 outputs), smaller ones 64 x 64 (gated: 64 x 64 outputs); with
+// K % 32 == 0 the operands reach LDS by direct global -> LDS loads, otherwise
+// through registers.  int8 x f16: large problems take
 // the kernel fed by direct global -> LDS loads (256 x 256 tiles, or 128 x 256
 // when there are few of those), and K % 64 != 0 the register-staged 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
@@ -25,8 +25,7 @@ uint32_t tiles_of(const GemmArgs &a, int BM, int BN) {
     return t;
 }
 
-constexpr uint32_t kBigTiles = 1024;  // >= 4 tiles per CU at 128 x 128
-constexpr uint32_t kWideF32 = 240;    // about one 256 x 128 tile per CU
+constexpr uint32_t kWideF32 = 240;  // about one 256 x 128 tile per CU
 
 }  // namespace
 
@@ -54,12 +53,10 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
         if (tiles_of(a, 256, 128) >= kWideF32)
             return direct ? gemm::launch_f32d<256, 256, 4, 4, 1, true, 2>(a, s)
                           : gemm::launch_gated<256, 256, 32, 4, false, 1>(a, s);
-        if (tiles_of(a, 128, 64) >= kBigTiles) return gemm::launch_gated<128, 128, 32, 2, false, 2>(a, s);
         return direct ? gemm::launch_f32d<64, 128, 2, 2, 4, true>(a, s) : gemm::launch_gated<64, 128, 32, 2, false, 4>(a, s);
     }
     if (tiles_of(a, 256, 128) >= kWideF32)
         return direct ? gemm::launch_f32d<256, 128, 4, 4, 1, false>(a, s) : gemm::launch<256, 128, 32, 4, 2, false, 1>(a, s);
-    if (tiles_of(a, 128, 128) >= kBigTiles) return gemm::launch<128, 128, 32, 2, 4, false, 1>(a, s);
     return direct ? gemm::launch_f32d<64, 64, 2, 2, 4, false>(a, s) : gemm::launch_v2<64, 64, 32, 2, 2, false, 4>(a, s);
 }
 
