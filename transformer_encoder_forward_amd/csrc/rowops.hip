@@ -336,11 +336,13 @@ __global__ __launch_bounds__(256) void gated_act_kernel(ActArgs a) {
 }
 
 // out[i][j] = mean over item i's rows of a[r][j].  A block takes one item and
-// 64 columns; wave w sums rows t = w, w+4, ... (lane = column, coalesced
-// 256-byte loads), and the four partial sums are added in wave order:
-// deterministic.
-__global__ __launch_bounds__(256) void mean_pool_kernel(PoolArgs a) {
-    __shared__ float part[4][64];
+// 64 columns; wave w of 16 sums rows t = w, w+16, ... in that order (lane =
+// column, coalesced 256-byte loads, eight rows in flight per lane), and the 16
+// partial sums are added in wave order: deterministic, and independent of the
+// other items.
+__global__ __launch_bounds__(1024) void mean_pool_kernel(PoolArgs a) {
+    constexpr int NWV = 16, U = 8;  // waves per block; rows in flight per lane
+    __shared__ float part[NWV][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint32_t j = blockIdx.x * 64 + lane;
     // items beyond the grid's y extent (65 535) are taken in grid-stride order
@@ -349,16 +351,28 @@ __global__ __launch_bounds__(256) void mean_pool_kernel(PoolArgs a) {
         const uint32_t L = it.na + it.nb;
         float s = 0.0f;
         if (j < a.d) {
-            for (uint32_t t = wave; t < L; t += 4) {
-                const uint32_t r = t < it.na ? it.r0a + t : it.r0b + (t - it.na);
-                s += a.a[(size_t)r * a.d + j];
+            // wave w sums rows w, w + 16, w + 32, ... in that order, U loads at a time
+            for (uint32_t t0 = wave; t0 < L; t0 += NWV * U) {
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const uint32_t t = t0 + NWV * u;
+                    const uint32_t r = t < it.na ? it.r0a + t : it.r0b + (t - it.na);
+                    v[u] = t < L ? a.a[(size_t)r * a.d + j] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < U; u++)
+                    if (t0 + NWV * u < L) s += v[u];
             }
         }
         part[wave][lane] = s;
         __syncthreads();
-        if (wave == 0 && j < a.d)
-            a.out[(size_t)i * a.d + j] =
-                (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / (float)L;
+        if (wave == 0 && j < a.d) {
+            float tot = part[0][lane];
+#pragma unroll
+            for (int w = 1; w < NWV; w++) tot += part[w][lane];
+            a.out[(size_t)i * a.d + j] = tot / (float)L;
+        }
         __syncthreads();
     }
 }
@@ -480,7 +494,7 @@ hipError_t launch_amax_f16(const AmaxArgs &a, hipStream_t s) {
 
 hipError_t launch_mean_pool(const PoolArgs &a, hipStream_t s) {
     if (!a.nitems || !a.d) return hipSuccess;
-    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 63) / 64, a.nitems < 65535u ? a.nitems : 65535u), dim3(256),
+    hipLaunchKernelGGL(mean_pool_kernel, dim3((a.d + 63) / 64, a.nitems < 65535u ? a.nitems : 65535u), dim3(1024),
                        0, s, a);
     return hipGetLastError();
 }
