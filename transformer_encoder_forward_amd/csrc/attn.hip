@@ -1,11 +1,13 @@
 // Launchers of the flash attention.
 //
-// f16 path: hd 128 in attn_f16d_kernel (K/V by direct global -> LDS loads), hd 64
-// in the attn_kernel template (mask fast path, lazy rescale).
+// f16 path (attn_impl.h): hd 128 without a window in attn_f16s_kernel
+// (software-pipelined, K/V by direct global -> LDS loads), with a window in
+// attn_f16d_kernel, hd 64 in the attn_kernel template.
 // f32 path: the kernel below, the same S^T = K Q^T / O^T = V^T P^T scheme in its
 // plain form: with 64-cycle FP32 MFMAs the softmax VALU work is hidden anyway,
-// and the plain form keeps the register count at 128 (4 waves per SIMD).  V is
-// staged transposed, so the P V operand comes in 16-byte reads.
+// and the plain form keeps the register count low enough for three waves per
+// SIMD.  V is staged transposed, so the P V operand comes in 16-byte reads;
+// short windowless items are split over the keys (attn_combine_kernel merges).
 // What both compute: egemma2.rs (cortiq-engine 0.8.39), module doc "Attention"
 // and `att_plan`; zimage.rs (cortiq-engine 0.7.6), module doc and `PFa`.
 #include <math.h>

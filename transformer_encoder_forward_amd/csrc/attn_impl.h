@@ -13,12 +13,14 @@
 // TRANSPOSED scores S^T = K Q^T with 32x32 MFMAs, so lane l holds query l%32
 // and 16 of the block's keys: the row max and row sum are 16 lane-local steps
 // plus one exchange with lane l^32, and P^T is already in the B-operand layout
-// of O^T = V^T P^T.  K/V blocks are double-buffered in LDS and shared by the
-// block's waves.  VALU work per score is kept small: blocks that lie wholly
-// inside every query's window skip the mask, and the running output is
-// rescaled only when some query's running max actually grew (otherwise the
-// factor is exactly 1).  Waves whose queries see none of a block skip it.  The
-// softmax runs in base 2 with log2(e) folded into the scale.
+// of O^T = V^T P^T.  K/V blocks are staged in LDS (double-buffered through
+// registers in the template below, a ring of direct global -> LDS loads in
+// attn_f16d_kernel and attn_f16s_kernel) and shared by the block's waves.  VALU
+// work per score is kept small: blocks that lie wholly inside every query's
+// window skip the mask, and the running output is rescaled only when the
+// running max moves (otherwise the factor is exactly 1).  Waves whose queries
+// see none of a block skip it.  The softmax runs in base 2 with log2(e) folded
+// into the scale.
 //  - f32 path: v_mfma_f32_32x32x2_f32 for both products.
 //  - f16 path: v_mfma_f32_32x32x16_f16; V is staged transposed in LDS as key
 //    pairs (one 32-bit write per channel and pair), so the A operand of O^T is

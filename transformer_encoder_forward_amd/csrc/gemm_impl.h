@@ -8,17 +8,19 @@
 //
 // Design for CDNA4: a block of WGM x WGN waves owns a BM x BN output tile; each
 // wave owns (BM/WGM) x (BN/WGN) = FM x FN accumulator blocks of 32 x 32.  X and
-// W tiles of BK columns are staged through double-buffered LDS with one
-// barrier per K stage; the next stage's global loads are issued before the
-// current stage's MFMAs.  Inside a stage, lane half h owns the contiguous K
-// run [h*BK/2, (h+1)*BK/2), so every fragment read is a run of ds_read_b128.
+// W tiles of BK columns reach LDS either through registers (gemm_kernel,
+// gemm_kernel_v2, gemm_gated_kernel: double-buffered, the next stage's global
+// loads issued before the current stage's MFMAs) or by direct global -> LDS
+// loads into a ring of stages (gemm_f32d_kernel, gemm_q8d_kernel); one barrier
+// per K stage.  Inside a stage, lane half h owns the contiguous K run
+// [h*BK/2, (h+1)*BK/2), so every fragment read is a run of ds_read_b128.
 // The K order of an output element depends only on K and the instantiation,
 // never on the row count or the row's position, so packed and separate
 // batches give the same bits.
 //  - f32: v_mfma_f32_32x32x2_f32 (one k per lane half per step).
-//  - int8 x f16: W tiles are widened int8 -> f16 (exact) while being staged,
-//    X is f16; v_mfma_f32_32x32x16_f16 (8 k per lane half per step), f32
-//    accumulation.
+//  - int8 x f16: W tiles are widened int8 -> f16 (exact) while being staged
+//    through registers, or per fragment when W sits in LDS as int8; X is f16;
+//    v_mfma_f32_32x32x16_f16 (8 k per lane half per step), f32 accumulation.
 // Tiles are renumbered so that each XCD (blocks are dispatched round robin
 // over the 8 XCDs) owns a contiguous run, and inside an item the run walks
 // groups of GR row tiles column by column, so a group's X rows and the W
@@ -155,7 +157,7 @@ __device__ __forceinline__ void store_block(const GemmArgs &a, const TileCtx &t,
     }
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB, bool PRIO = false>
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) {
     using E = Elem<I8>;
     using T = typename E::T;
@@ -274,9 +276,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) 
 #pragma unroll
             for (int q = 0; q < NV; q++)
                 fb[j][q] = *reinterpret_cast<const V *>(&Bs[buf][wc * (BN / WGN) + j * 32 + li][HK * hf + CE * q]);
-        // the MFMA phase runs at raised wave priority, so a wave ready to issue
-        // matrix ops wins over a wave of the other block that is staging
-        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < NSTEP; kk++)
 #pragma unroll
@@ -289,7 +288,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_kernel(GemmArgs a) 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk / 4][kk % 4], fb[j][kk / 4][kk % 4],
                                                                         acc[i][j], 0, 0, 0);
                 }
-        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         if (s + 1 < nst) sstore(buf ^ 1);
         __syncthreads();
     }
@@ -315,11 +313,11 @@ inline uint32_t plan_tiles(GemmArgs &g, int BM, int BN) {
     return tiles;
 }
 
-template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB, bool PRIO = false>
+template <int BM, int BN, int BK, int WGM, int WGN, bool I8, int MINB>
 hipError_t launch(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WGM, WGN, I8, MINB, PRIO>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WGM, WGN, I8, MINB>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
     return hipGetLastError();
 }
 
