@@ -117,7 +117,8 @@ def test_gemm_f32_packed_rows_bit_identical(n, m, k, gated):
     (B.ENC_F32, "gelu", 1000, 2048, 512), (B.ENC_F32, "gelu", 37, 200, 128),
     (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64),
     (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192),
-    (B.ENC_I8F16, "silu", 77, 160, 80), (B.ENC_F32, "gelu", 8001, 2048, 512)])
+    (B.ENC_I8F16, "silu", 77, 160, 80), (B.ENC_F32, "gelu", 8001, 2048, 512),
+    (B.ENC_I8F16, "silu", 1300, 11000, 128)])   # >= 512 tiles: the 256 x (128 + 128) int8 tile
 def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
     bit for bit, and == the oracle within tolerance."""
@@ -174,10 +175,11 @@ def test_gemm_i8f16_integer_exact(n, m, k):
     assert np.array_equal(host(Y), ref)
 
 
-# shapes that take the direct-to-LDS kernel (K % 64 == 0): 256 x 256 tiles (>= 128
-# of them) and 128 x 256 tiles (fewer); one K stage, exactly the LDS ring, ring
+# shapes that take the direct-to-LDS kernel (K % 64 == 0): 256 x 256 tiles (>= 256
+# of them) and 64 x 256 tiles (fewer); one K stage, exactly the LDS ring, ring
 # wrap-around; ragged rows and columns
-@pytest.mark.parametrize("n,m,k", [(520, 17000, 64), (520, 17000, 192), (513, 17000, 320),
+@pytest.mark.parametrize("n,m,k", [(1300, 11000, 64), (1300, 11000, 192), (1283, 11000, 320),
+                                   (520, 17000, 64), (513, 17000, 320),
                                    (130, 1000, 64), (257, 3000, 192), (1, 300, 320)])
 def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
     say(f"gemm i8f16 wide integer n={n} m={m} k={k}")
@@ -194,15 +196,15 @@ def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
 
 def test_gemm_i8f16_kernel_choice_bit_identical():
     """Rows computed in a launch of 256 x 256 tiles and in small launches of
-    128 x 256 tiles give the same bits (one K order for every int8 kernel)."""
+    64 x 256 tiles give the same bits (one K order for every int8 kernel)."""
     rng = np.random.default_rng(77)
-    n, m, k = 520, 17000, 256
+    n, m, k = 1300, 11000, 256
     x = rng.normal(0, 1, (n, k)).astype(np.float16)
     W = to_dev(rng.integers(-127, 128, (m, k)).astype(np.int8))
     rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32))]
     Yall = torch.empty((n, m), dtype=torch.float32, device=DEV)
     B.gemm_items(to_dev(x), Yall, [W], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs)
-    for r0, r1 in ((0, 1), (250, 300), (450, 520)):
+    for r0, r1 in ((0, 1), (250, 300), (450, 520), (1100, 1300)):
         Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
         B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
                      row_scale=rs)

@@ -4,9 +4,10 @@
 // with about one 256 x 128 tile per CU or more take 256 x 128 tiles (gated: 256
 // rows x 128 outputs), smaller ones 64 x 64 (gated: 64 x 64 outputs); with
 // K % 32 == 0 the operands reach LDS by direct global -> LDS loads, otherwise
-// through registers.  int8 x f16: large problems take
-// the kernel fed by direct global -> LDS loads (256 x 256 tiles, or 128 x 256
-// when there are few of those), and K % 64 != 0 the register-staged 128 x 128.
+// through registers.  int8 x f16: the kernel fed by
+// direct global -> LDS loads (256 x 256 tiles for large launches, 64 x 256 /
+// gated 128 x 256 for smaller ones), and K % 64 != 0 the register-staged
+// 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
 // K order, so an output element is summed in the same order whatever tile it
 // falls in: the choice never changes a result bit, and packed and separate
@@ -62,23 +63,26 @@ hipError_t launch_gemm_f32(const GemmArgs &a, hipStream_t s) {
 
 namespace {
 
-// The direct-to-LDS int8 kernel needs K % 64 == 0.  256 x 256 tiles (8 waves of
-// 128 x 64, one block per CU) when the launch has at least 128 of them; fewer
-// (the output projections of a 1056-row DiT batch: 75 tiles) take 128 x 256
-// tiles (8 waves of 64 x 64), which measured 10-40% faster there.  Otherwise
+// The direct-to-LDS int8 kernel needs K % 64 == 0.  Plain GEMMs: 256 x 256
+// tiles (8 waves of 128 x 64, one block per CU) when the launch has at least
+// 256 of them; fewer (a 1056-row DiT batch: q|k|v 225 tiles, the output and
+// down projections 75) take 64 x 256 tiles of 8 waves (64 x 32 each, two
+// blocks per CU), measured 6% / 28% / 26% faster there and 15-25% slower at
+// 8448 rows.  Gated: 256 x (128 + 128) with at least 512 tiles of 256 x 128,
+// else 128 x (128 + 128) (6% faster at 1056 rows).  Otherwise (K % 64 != 0)
 // the register-staged 128 x 128 kernel.  All sum in the same K order.
-constexpr uint32_t kWideTiles = 128;
+constexpr uint32_t kWideTiles = 256, kWideGated = 512;
 
 }  // namespace
 
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
     if (kmul(a, 64)) {
-        if (tiles_of(a, 256, gated ? 128 : 256) >= kWideTiles)
-            return gated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
-                         : gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
-        return gated ? gemm::launch_q8d<128, 256, 2, 4, 1, true>(a, s)
-                     : gemm::launch_q8d<128, 256, 2, 4, 1, false>(a, s);
+        if (gated)
+            return tiles_of(a, 256, 128) >= kWideGated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
+                                                       : gemm::launch_q8d<128, 256, 2, 4, 1, true>(a, s);
+        return tiles_of(a, 256, 256) >= kWideTiles ? gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s)
+                                                   : gemm::launch_q8d<64, 256, 1, 8, 2, false>(a, s);
     }
     if (gated) return gemm::launch_gated<128, 128, 64, 2, true, 2>(a, s);
     return gemm::launch<128, 128, 64, 2, 2, true, 2>(a, s);
