@@ -471,11 +471,14 @@ def test_add_norm_fused_equals_unfused(d, f16):
     assert torch.equal(A, A2)  # the fused next pre-norm gives the same bits
 
 
-@pytest.mark.parametrize("hd,sections,f16", [(64, 1, False), (64, 2, False), (128, 2, True),
-                                             (128, 1, True), (64, 1, True), (128, 2, False)])
-def test_qk_norm_rope(hd, sections, f16):
-    rng = np.random.default_rng(hd + sections)
-    rows, nq, nkv = 97, 3, 2
+@pytest.mark.parametrize("hd,sections,f16,nq,nkv", [
+    (64, 1, False, 3, 2), (64, 2, False, 3, 2), (128, 2, True, 3, 2), (128, 1, True, 3, 2),
+    (64, 1, True, 3, 2), (128, 2, False, 3, 2),
+    # several head groups per row, the last one partial
+    (128, 2, True, 30, 30), (64, 1, False, 13, 5), (128, 1, False, 7, 3), (64, 2, True, 21, 4)])
+def test_qk_norm_rope(hd, sections, f16, nq, nkv):
+    rng = np.random.default_rng(hd + sections + nq)
+    rows = 97
     ld = (nq + 2 * nkv) * hd
     p = rng.normal(0, 2, (rows, ld)).astype(np.float16 if f16 else np.float32)
     qw = rng.normal(1, 0.02, hd).astype(np.float32)

@@ -22,6 +22,8 @@
 // rms_norm of the updated residual would.
 #include <math.h>
 
+#include <algorithm>
+
 #include "dev.h"
 #include "kern.h"
 
@@ -197,8 +199,9 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
     }
 }
 
-// One wave per row over all of its nq q heads and nkv k heads (and, with
-// v_norm, its nkv v heads: weightless RMS, no rotation).  A head is held by
+// A row's nq q heads and nkv k heads (and, with v_norm, its nkv v heads:
+// weightless RMS, no rotation) are split into groups of a few passes, one wave
+// per (row, group).  A head is held by
 // LH = hd / VE lanes, each owning VE consecutive channels (one 16-byte vector:
 // 4 f32 or 8 f16), so a wave covers 64 / LH heads per pass with fully
 // coalesced loads.  The per-head RMS is a butterfly inside the LH-lane group;
@@ -240,6 +243,12 @@ __device__ __forceinline__ void qk_store(const QkArgs &a, uint32_t row, uint32_t
     }
 }
 
+// The launch splits a row's passes into gridDim.y groups only when rows alone
+// give fewer waves than this (extra groups reload the gains and cos/sin, which
+// costs at large row counts).  Every head is normed and rotated by one wave
+// whatever the grouping, so the grouping changes no bit.
+constexpr uint32_t kQkWaveTarget = 8192;
+
 template <int HD, bool F16>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
     constexpr int VE = F16 ? 8 : 4;
@@ -275,15 +284,18 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(QkArgs a) {
         return hh < a.nq ? a.q_col + hh * HD
                          : hh < nqk ? a.k_col + (hh - a.nq) * HD : a.v_col + (hh - nqk) * HD;
     };
+    // this wave's heads: group blockIdx.y of gridDim.y, whole passes each
+    const uint32_t npass = (heads + HP - 1) / HP, gp = (npass + gridDim.y - 1) / gridDim.y;
+    const uint32_t hbeg = blockIdx.y * gp * HP, hend = min(heads, hbeg + gp * HP);
     float xn[VE];
-    qk_load<HD, F16>(a, row, col_of(hsub), c0, (uint32_t)hsub < heads, xn);
-    for (uint32_t h0 = 0; h0 < heads; h0 += HP) {
+    qk_load<HD, F16>(a, row, col_of(hbeg + hsub), c0, hbeg + hsub < hend, xn);
+    for (uint32_t h0 = hbeg; h0 < hend; h0 += HP) {
         const uint32_t hh = h0 + hsub;
-        const bool valid = hh < heads, isv = hh >= nqk;
+        const bool valid = hh < hend, isv = hh >= nqk;
         float x[VE];
 #pragma unroll
         for (int e = 0; e < VE; e++) x[e] = xn[e];
-        if (h0 + HP < heads) qk_load<HD, F16>(a, row, col_of(hh + HP), c0, hh + HP < heads, xn);
+        if (h0 + HP < hend) qk_load<HD, F16>(a, row, col_of(hh + HP), c0, hh + HP < hend, xn);
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < VE; e++) ss = fmaf(x[e], x[e], ss);
@@ -465,7 +477,12 @@ hipError_t launch_add_norm(const AddNormArgs &a, bool f16, hipStream_t s) {
 
 hipError_t launch_qk_norm_rope(const QkArgs &a, bool f16, hipStream_t s) {
     if (!a.rows || !(a.nq + a.nkv)) return hipSuccess;
-    const dim3 grid((a.rows + 3) / 4);
+    const uint32_t heads = a.nq + a.nkv + (a.v_norm ? a.nkv : 0);
+    const uint32_t hp = 64 / (a.hd / (f16 ? 8 : 4));  // heads per pass
+    const uint32_t npass = (heads + hp - 1) / hp;
+    const uint32_t want = std::min(npass, std::max(1u, (kQkWaveTarget + a.rows - 1) / a.rows));
+    const uint32_t gp = (npass + want - 1) / want;  // passes per group; no group is empty
+    const dim3 grid((a.rows + 3) / 4, (npass + gp - 1) / gp);
     if (a.hd == 64) {
         if (f16) hipLaunchKernelGGL((qk_norm_rope_kernel<64, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((qk_norm_rope_kernel<64, false>), grid, dim3(256), 0, s, a);
