@@ -173,28 +173,35 @@ __global__ __launch_bounds__(256) void add_norm_kernel(AddNormArgs a) {
         const float inv_h = rms_inv(h, a.d, a.eps);
         Row<NV> y = rms_apply(h, inv_h, a.w_next, a.d, lane);
         if (a.scale) mul_cols(y, a.scale, 1.0f, a.d, lane);  // adaLN: times (1 + s)
-        // copy z = y col_z oscale, formed slot by slot as it is stored (no
-        // second register row)
+        // copy z = y col_z oscale.  A column row is loaded whole before the
+        // first store: loads placed after stores the compiler cannot prove
+        // disjoint would each wait for the one before (h is dead by now, so
+        // the extra register row raises no peak).  The copies with and
+        // without a column row take separate store loops, so the stores of
+        // the plain copy carry no wait for column loads.
+        auto put = [&](size_t zo, const Row<NV> &v) {
+            if (F16)
+                store_row(v, reinterpret_cast<_Float16 *>(a.a) + zo, true, a.d, lane);
+            else
+                store_row(v, reinterpret_cast<float *>(a.a) + zo, false, a.d, lane);
+        };
         for (uint32_t z = 0; z < a.nout; z++) {
             const float *col = a.col[z];
             const size_t zo = off + z * a.a_stride;
+            Row<NV> v;
+            if (col) {
+                load_row(v, col, a.d, lane);
 #pragma unroll
-            for (int i = 0; i < NV; i++) {
-                const int c = (i * 64 + lane) * 4;
-                if (c >= (int)a.d) continue;
-                f32x4 v = y.v[i];
-                if (col) {
-                    const f32x4 m = ld4(col + c);
+                for (int i = 0; i < NV; i++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) v[e] *= m[e];
-                }
+                    for (int e = 0; e < 4; e++) v.v[i][e] = y.v[i][e] * v.v[i][e] * a.oscale;
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[e] *= a.oscale;  // a power of two: exact
-                if (F16)
-                    st4h(reinterpret_cast<_Float16 *>(a.a) + zo + c, v);
-                else
-                    st4(reinterpret_cast<float *>(a.a) + zo + c, v);
+                for (int i = 0; i < NV; i++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) v.v[i][e] = y.v[i][e] * a.oscale;  // a power of two: exact
             }
+            put(zo, v);
         }
     }
 }
