@@ -365,6 +365,40 @@ def test_attention_packed_equals_separate(path):
         assert torch.equal(o1, out[r0:r0 + n])
 
 
+WINDOW_ITEM_CASES = [
+    # (window, item lengths): windowed f32 launches over many items of mixed
+    # lengths; every row of every item must be written once, as alone
+    (128, [5, 130, 300, 1, 700, 129, 257, 90]),          # one q-tile of keys each side
+    (512, [1856, 194, 1100, 640, 37, 900, 385]),         # the text encoder's window
+    (2500, [2600, 300, 1500, 20]),                       # window beyond 15 q-tiles
+    (64, [int(n) for n in np.random.default_rng(5).integers(1, 200, 70)]),  # 64 items + a second launch
+]
+
+
+@pytest.mark.parametrize("window,lens", WINDOW_ITEM_CASES)
+def test_attention_f32_windowed_many_items(window, lens):
+    nq, nkv, hd = 2, 1, 64
+    say(f"attention f32 windowed items W={window} items={len(lens)} rows={sum(lens)}")
+    r0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(int)
+    items = [[(int(a), int(n))] for a, n in zip(r0, lens)]
+    rows = int(sum(lens))
+    rng = np.random.default_rng(window + rows)
+    p = _panel(rng, rows, nq, nkv, hd, qscale=0.5)
+    P = to_dev(p)
+    out = torch.full((rows, nq * hd), 7.0, dtype=torch.float32, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(P, out, items, nq, nkv, hd, scale, window)
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, scale, window)
+    err = row_rel_err(host(out), ref)
+    say(f"  err {err:.2e}")
+    assert err <= TOL_F32
+    for (a, n), in items[:12]:
+        o1 = torch.full((n, nq * hd), 7.0, dtype=torch.float32, device=DEV)
+        B.attention_items(to_dev(p[a:a + n]), o1, [[(0, n)]], nq, nkv, hd, scale, window)
+        assert torch.equal(o1, out[a:a + n])
+
+
 KEY_SPLIT_CASES = [
     # (path, items, nq, nkv, hd): each windowless item too short to fill the GPU alone
     (B.ENC_F32, [[(0, 1024)]], 12, 12, 64),             # the 1024-row ViT: 8 chunks of 128 keys
