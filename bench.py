@@ -202,8 +202,9 @@ def main():
                       if w.stages else {}),
                    "gemm_gflop": round(gflop / 1e9, 2), "attn_gflop": round(aflop / 1e9, 2),
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "GEMM class: gemm_kernel + gemm_gated_kernel ("
-                               + ("FP32" if dtype == "f32" else "int8 x f16") + " MFMA)",
+        "roofline": {"kernel": ("GEMM class: gemm_f32d_kernel plain and gated (FP32 MFMA)"
+                                if dtype == "f32" else
+                                "GEMM class: gemm_q8d_kernel plain and gated (int8 x f16 MFMA)"),
                      "bound": "mfma", "achieved": round(gemm_tf, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / peak, 4),
                      "traffic": measured_traffic(args.workload),
