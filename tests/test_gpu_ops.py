@@ -66,7 +66,9 @@ def test_gemm_f32_qkv_items_one_launch():
 
 
 @pytest.mark.parametrize("n,m,k", [(64, 384, 128), (1000, 1536, 512), (333, 512, 2048),
-                                   (1024, 3072, 768)])
+                                   (1024, 3072, 768),
+                                   # more tiles than resident blocks: blocks loop over tiles
+                                   (9001, 1536, 256), (4099, 1536, 512)])
 def test_gemm_f32_random(n, m, k):
     say(f"gemm f32 random n={n} m={m} k={k}")
     rng = np.random.default_rng(n + m + k)
@@ -77,6 +79,22 @@ def test_gemm_f32_random(n, m, k):
     err = row_rel_err(host(Y), O.linear(x, w))
     say(f"  err {err:.2e}")
     assert err <= TOL_F32
+
+
+def test_gemm_f32_items_of_different_k_many_tiles():
+    """Two items of different K in one launch with more tiles than resident
+    blocks, so that blocks work through tiles of both items in turn."""
+    rng = np.random.default_rng(12)
+    n, k0, k1, m0, m1 = 6000, 512, 2048, 1536, 512
+    x = rng.integers(-8, 9, (n, k1)).astype(np.float32)
+    w0 = rng.integers(-8, 9, (m0, k0)).astype(np.float32)
+    w1 = rng.integers(-8, 9, (m1, k1)).astype(np.float32)
+    ld = m0 + m1
+    Y = torch.full((n, ld), -7.0, dtype=torch.float32, device=DEV)
+    items = [(n, m0, k0, k1, ld, 0, 0, 0), (n, m1, k1, k1, ld, 1, 0, m0)]
+    B.gemm_items(to_dev(x), Y, [to_dev(w0), to_dev(w1)], items)
+    ref = np.concatenate([O.linear(x[:, :k0], w0), O.linear(x, w1)], 1)
+    assert np.array_equal(host(Y), ref)
 
 
 def test_gemm_f32_gelu_epilogue():

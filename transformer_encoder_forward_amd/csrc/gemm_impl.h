@@ -26,6 +26,8 @@
 // groups of GR row tiles column by column, so a group's X rows and the W
 // columns in flight stay in that XCD's L2.
 #pragma once
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "dev.h"
@@ -33,6 +35,23 @@
 
 namespace enc {
 namespace gemm {
+
+// Compute units of the current device (queried once per device).
+inline int device_cus() {
+    constexpr int kDevs = 64;
+    static std::atomic<int> cache[kDevs];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const bool cached = dev >= 0 && dev < kDevs;
+    if (cached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (cached) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 constexpr int GR = 8;  // row tiles per L2 group
 
@@ -49,10 +68,13 @@ struct TileCtx {
     int row0, col0;
 };
 
+// Item, weights and tile origin of linear tile `tile` (< a.total_tiles).
 template <int BM, int BN>
-__device__ __forceinline__ bool locate(const GemmArgs &a, TileCtx &t, int cols_per_tile = BN) {
-    const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
-    if (tile >= a.total_tiles) return false;
+__device__ __forceinline__ void locate_tile(const GemmArgs &a, uint32_t tile, TileCtx &t, int cols_per_tile) {
+    // uniform by construction; stated, so that the item lookup below stays a
+    // scalar load of the argument block (a per-lane index would copy the
+    // whole block to scratch)
+    tile = __builtin_amdgcn_readfirstlane(tile);
     int sel = 0;
 #pragma unroll
     for (int i = 1; i < kMaxGemmItems; i++)
@@ -79,6 +101,17 @@ __device__ __forceinline__ bool locate(const GemmArgs &a, TileCtx &t, int cols_p
     const uint32_t rows_g = min((uint32_t)GR, tiles_n - g * GR);
     t.row0 = (int)((g * GR + in_g % rows_g) * BM);
     t.col0 = (int)((in_g / rows_g) * cols_per_tile);
+}
+
+// The tile of this block in a launch of one block per tile: consecutive
+// blocks go to the eight XCDs in turn, so block b takes tile xcd_remap(b) and
+// each XCD works through one contiguous run of tiles (shared rows and columns
+// stay in its L2).
+template <int BM, int BN>
+__device__ __forceinline__ bool locate(const GemmArgs &a, TileCtx &t, int cols_per_tile = BN) {
+    const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
+    if (tile >= a.total_tiles) return false;
+    locate_tile<BM, BN>(a, tile, t, cols_per_tile);
     return true;
 }
 
@@ -947,6 +980,51 @@ hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
 // == 0.  Rows past n and columns past m load clamped (finite) rows and are
 // never stored.  Gated: each wave column holds 32 gate and 32 up rows of the
 // same 32 output columns (BN / WGN == 64); the epilogue forms act(g) * u.
+// The launch's argument block read in place (constant memory, scalar loads).
+// A per-tile lookup in a loop through the by-value kernel argument makes the
+// compiler keep a private copy of the whole block in scratch; the kernels
+// that look up more than one tile read the table through this reference.
+__device__ __forceinline__ const GemmArgs &kernarg_gemm() {
+    return *(const GemmArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// Per-lane sources of a tile's direct loads (k offset added per stage): load q
+// of wave w covers tile rows 8 (L w + q) .. + 7, lane l row + l/8, position
+// l%8 holding chunk (l%8) ^ ((row >> 1) & 7).  Rows past n and columns past m
+// are clamped to the last one (finite, never stored).
+template <int AL, int BL, bool GATED>
+__device__ __forceinline__ void f32d_sources(const float *x, const float *wg, const float *wu, const TileCtx &tc,
+                                             int wave, int lane, const float *(&asrc)[AL],
+                                             const float *(&bsrc)[BL]) {
+    const int n = tc.it.n, m = tc.it.m, K = tc.it.k;
+    const float *X = x + tc.it.x_off;
+#pragma unroll
+    for (int q = 0; q < AL; q++) {
+        const int r = 8 * (AL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        asrc[q] = X + (size_t)min(tc.row0 + r, n - 1) * tc.it.ldx + 4 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < BL; q++) {
+        const int r = 8 * (BL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
+        const float *w = wg;
+        int col = tc.col0 + r;
+        if constexpr (GATED) {
+            w = ((r >> 5) & 1) ? wu : wg;
+            col = tc.col0 + (r >> 6) * 32 + (r & 31);
+        }
+        bsrc[q] = w + (size_t)min(col, m - 1) * K + 4 * c;
+    }
+}
+
+// The up-projection weights of a gated tile: slot + 1 of the weight table.
+__device__ __forceinline__ const float *gated_up(const GemmArgs &a, uint32_t slot) {
+    const float *wu = reinterpret_cast<const float *>(a.w[1]);
+#pragma unroll
+    for (int s2 = 1; s2 < kMaxGemmItems; s2++)
+        if ((int)slot + 1 == s2) wu = reinterpret_cast<const float *>(a.w[s2]);
+    return wu;
+}
+
 template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArgs a) {
     constexpr int NW = WGM * WGN, BK = 32;
@@ -960,42 +1038,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     static_assert(NS * S_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
 
+    // persistent (tiles of one block per CU): block b takes tiles
+    // xcd_remap(b + i * gridDim.x), i = 0, 1, ... (a multiple of 8 blocks keeps
+    // each block on one XCD's run of tiles)
+    const uint32_t T = a.total_tiles;
+    uint32_t v = blockIdx.x;
+    if (v >= T) return;
+    constexpr int CPT = GATED ? BN / 2 : BN;  // output columns per tile
+    const GemmArgs &ka = kernarg_gemm();  // the same block as `a`
     TileCtx t;
-    if (!locate<BM, BN>(a, t, GATED ? BN / 2 : BN)) return;
-    const float *wg = reinterpret_cast<const float *>(t.w), *wu = wg;
-    if constexpr (GATED) {
-        wu = reinterpret_cast<const float *>(a.w[1]);
-#pragma unroll
-        for (int s2 = 1; s2 < kMaxGemmItems; s2++)
-            if ((int)t.it.slot + 1 == s2) wu = reinterpret_cast<const float *>(a.w[s2]);
-    }
-    const int n = t.it.n, m = t.it.m, K = t.it.k;
-    const float *X = reinterpret_cast<const float *>(a.x) + t.it.x_off;
+    locate_tile<BM, BN>(ka, xcd_remap(v, T), t, CPT);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hf = lane >> 5;
     const int wr = wave / WGN, wc = wave % WGN;
 
-    // sources of this lane's load instructions (k offset added per stage):
-    // load q of this wave covers tile rows 8 (L wave + q) .. + 7, lane l row
-    // + l/8, position l%8 holding chunk (l%8) ^ ((row >> 1) & 7)
     const float *asrc[AL];
-#pragma unroll
-    for (int q = 0; q < AL; q++) {
-        const int r = 8 * (AL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
-        asrc[q] = X + (size_t)min(t.row0 + r, n - 1) * t.it.ldx + 4 * c;
-    }
     const float *bsrc[BL];
-#pragma unroll
-    for (int q = 0; q < BL; q++) {
-        const int r = 8 * (BL * wave + q) + (lane >> 3), c = (lane & 7) ^ ((r >> 1) & 7);
-        const float *w = wg;
-        int col = t.col0 + r;
-        if constexpr (GATED) {
-            w = ((r >> 5) & 1) ? wu : wg;
-            col = t.col0 + (r >> 6) * 32 + (r & 31);
-        }
-        bsrc[q] = w + (size_t)min(col, m - 1) * K + 4 * c;
-    }
+    const float *x = reinterpret_cast<const float *>(a.x);
     auto dma = [&](int s) {
         uint8_t *buf = smem + (s % NS) * S_BYTES;
         const int k0 = s * BK;
@@ -1007,6 +1066,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
         for (int q = 0; q < BL; q++)
             __builtin_amdgcn_global_load_lds(ENC_GLOBAL(bsrc[q] + k0),
                                              ENC_SHARED(buf + A_BYTES + (BL * wave + q) * 1024), 16, 0, 0);
+    };
+    // the first min(NS, stages) stages of a tile
+    auto prologue = [&](int nst) {
+        dma(0);
+        if (nst > 1) dma(1);
+        if (NS > 2 && nst > 2) dma(2);
     };
 
     // fragment q (k = 16 hf + 4q .. + 3) of X row wr*(BM/WGM) + 32 i + li and
@@ -1029,12 +1094,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     };
 
     f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
     // k-steps 4q .. 4q+3 of the stage from fragment q.  (Each element is copied
     // out before the reinterpretation: a bit_cast of a vector element
     // expression compiles to element 0 here.)
@@ -1051,75 +1110,108 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
                 }
     };
 
-    const int nst = K / BK;
-    dma(0);
-    if (nst > 1) dma(1);
-    if (NS > 2 && nst > 2) dma(2);
+    f32d_sources<AL, BL, GATED>(x, reinterpret_cast<const float *>(t.w), GATED ? gated_up(ka, t.it.slot) : nullptr,
+                                t, wave, lane, asrc, bsrc);
+    int nst = t.it.k / BK;
+    prologue(nst);
     if (NS > 2 && nst > 2)
         vm_wait<2 * NDMA>();
     else if (nst > 1)
         vm_wait<NDMA>();
     else
         vm_wait<0>();
-    block_barrier();
-    read(fa0, fb0, 0, 0);
-    for (int s = 0; s < nst; s++) {
-        const int b = s % NS;
-        read(fa1, fb1, b, 1);
-        lgkm_wait_n<FM + FN>();  // fragment 0 landed (fragment 1 may still be in flight)
-        frag_ready(fa0, fb0);
-        mma(fa0, fb0);
-        read(fa0, fb0, b, 2);
-        lgkm_wait_n<FM + FN>();
-        frag_ready(fa1, fb1);
-        mma(fa1, fb1);
-        read(fa1, fb1, b, 3);
-        lgkm_wait_n<FM + FN>();
-        frag_ready(fa0, fb0);
-        mma(fa0, fb0);
-        // stage s+1 landed (own loads; with three stages, s+2's may fly), own
-        // reads of buffer b done; after the barrier every wave's are, so b
-        // takes stage s+NS
-        if (NS > 2 && s + 2 < nst)
-            vm_wait<NDMA>();
-        else
-            vm_wait<0>();
-        lgkm_wait_n<0>();
-        frag_ready(fa1, fb1);
+    for (;;) {
         block_barrier();
-        if (s + NS < nst) dma(s + NS);
-        if (s + 1 < nst) read(fa0, fb0, (s + 1) % NS, 0);
-        mma(fa1, fb1);
-    }
-
-    if constexpr (!GATED) {
+        read(fa0, fb0, 0, 0);
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
             for (int j = 0; j < FN; j++)
-                store_block<false>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32, t.col0 + wc * (BN / WGN) + j * 32,
-                                   lane);
-    } else {
-        // lane holds gate and up of the same (row, column)
-        const int c = t.col0 + wc * 32 + li;
-        if (c >= m) return;
-        const float mg = a.alpha, mu = a.alpha;
-        const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
-        const float oc = a.ycol ? a.ycol[c] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < FM; i++)
+                for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+        for (int s = 0; s < nst; s++) {
+            const int b = s % NS;
+            read(fa1, fb1, b, 1);
+            lgkm_wait_n<FM + FN>();  // fragment 0 landed (fragment 1 may still be in flight)
+            frag_ready(fa0, fb0);
+            mma(fa0, fb0);
+            read(fa0, fb0, b, 2);
+            lgkm_wait_n<FM + FN>();
+            frag_ready(fa1, fb1);
+            mma(fa1, fb1);
+            read(fa1, fb1, b, 3);
+            lgkm_wait_n<FM + FN>();
+            frag_ready(fa0, fb0);
+            mma(fa0, fb0);
+            // stage s+1 landed (own loads; with three stages, s+2's may fly), own
+            // reads of buffer b done; after the barrier every wave's are, so b
+            // takes stage s+NS
+            if (NS > 2 && s + 2 < nst)
+                vm_wait<NDMA>();
+            else
+                vm_wait<0>();
+            lgkm_wait_n<0>();
+            frag_ready(fa1, fb1);
+            block_barrier();
+            if (s + NS < nst) dma(s + NS);
+            if (s + 1 < nst) read(fa0, fb0, (s + 1) % NS, 0);
+            mma(fa1, fb1);
+        }
+
+        if constexpr (!GATED) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (row >= n) continue;
-                const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
-                const float v = (gelu ? gelu_tanh(g) : silu(g)) * u * oc * a.yscale;
-                const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
-                if (f16)
-                    reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
-                else
-                    reinterpret_cast<float *>(a.y)[off] = v;
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    store_block<false>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32,
+                                       t.col0 + wc * (BN / WGN) + j * 32, lane);
+        } else {
+            // lane holds gate and up of the same (row, column)
+            const int c = t.col0 + wc * 32 + li;
+            if (c < (int)t.it.m) {
+                const float mg = a.alpha, mu = a.alpha;
+                const bool f16 = a.flags & 1u, gelu = a.flags & kGateGelu;
+                const float oc = a.ycol ? a.ycol[c] : 1.0f;
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int row = t.row0 + wr * (BM / WGM) + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        if (row >= (int)t.it.n) continue;
+                        const float g = acc[i][0][r] * mg, u = acc[i][1][r] * mu;
+                        const float val = (gelu ? gelu_tanh(g) : silu(g)) * u * oc * a.yscale;
+                        const size_t off = t.it.y_off + (size_t)row * t.it.ldy + c;
+                        if (f16)
+                            reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)val;
+                        else
+                            reinterpret_cast<float *>(a.y)[off] = val;
+                    }
             }
+        }
+        // Every wave has passed the last barrier, so no LDS stage is read any
+        // more: once this tile's stores are issued, the next tile's first
+        // stages are loaded while they drain.  (Stores first: with the loads
+        // issued before them, the compiler waits for every load at the top of
+        // each k-step of the next tile.)
+        // (only the one-block-per-CU tiles loop; smaller ones run a block per tile)
+        const uint32_t vn = v + gridDim.x;
+        const bool more = MINB == 1 && vn < T;
+        TileCtx tn;
+        int nst_n = 0;
+        if (more) {
+            locate_tile<BM, BN>(ka, xcd_remap(vn, T), tn, CPT);
+            f32d_sources<AL, BL, GATED>(x, reinterpret_cast<const float *>(tn.w),
+                                        GATED ? gated_up(ka, tn.it.slot) : nullptr, tn, wave, lane, asrc, bsrc);
+            nst_n = tn.it.k / BK;
+            prologue(nst_n);
+        }
+
+        if (!more) break;
+        // the next tile's stages (and this tile's stores) have landed
+        vm_wait<0>();
+        t = tn;
+        v = vn;
+        nst = nst_n;
     }
 }
 
@@ -1127,8 +1219,12 @@ template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 hipError_t launch_f32d(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS>), dim3(tiles), dim3(64 * WGM * WGN), 0, s,
-                       g);
+    // tiles of one block per CU (MINB 1): one block per CU, each looping over
+    // its tiles; smaller tiles: one block per tile, the hardware fills the
+    // CUs as blocks end
+    const uint32_t slots = MINB == 1 ? (uint32_t)device_cus() : tiles;
+    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS>), dim3(std::min(tiles, slots)),
+                       dim3(64 * WGM * WGN), 0, s, g);
     return hipGetLastError();
 }
 
