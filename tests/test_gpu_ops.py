@@ -136,7 +136,8 @@ def test_gemm_f32_packed_rows_bit_identical(n, m, k, gated):
     (B.ENC_I8F16, "silu", 300, 1280, 256), (B.ENC_I8F16, "silu", 45, 96, 64),
     (B.ENC_I8F16, "silu", 520, 12800, 128), (B.ENC_I8F16, "gelu", 300, 25600, 192),
     (B.ENC_I8F16, "silu", 77, 160, 80), (B.ENC_F32, "gelu", 8001, 2048, 512),
-    (B.ENC_I8F16, "silu", 1300, 11000, 128)])   # >= 512 tiles: the 256 x (128 + 128) int8 tile
+    (B.ENC_I8F16, "silu", 1300, 11000, 128),    # >= 512 tiles: the 256 x (128 + 128) int8 tile
+    (B.ENC_I8F16, "silu", 200, 2560, 320), (B.ENC_I8F16, "silu", 200, 2560, 448)])
 def test_gemm_gated_equals_unfused(path, act, n, ff, d):
     """act(gate) * up formed in the GEMM epilogue == gate/up GEMM + enc_gated_act,
     bit for bit, and == the oracle within tolerance."""
@@ -198,7 +199,10 @@ def test_gemm_i8f16_integer_exact(n, m, k):
 # wrap-around; ragged rows and columns
 @pytest.mark.parametrize("n,m,k", [(1300, 11000, 64), (1300, 11000, 192), (1283, 11000, 320),
                                    (520, 17000, 64), (513, 17000, 320),
-                                   (130, 1000, 64), (257, 3000, 192), (1, 300, 320)])
+                                   (130, 1000, 64), (257, 3000, 192), (1, 300, 320),
+                                   # small launches, K stages 2 and 6 to 8 (deeper rings)
+                                   (130, 1000, 128), (200, 900, 384), (77, 1000, 448),
+                                   (257, 700, 512)])
 def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
     say(f"gemm i8f16 wide integer n={n} m={m} k={k}")
     rng = np.random.default_rng(n + m + k)

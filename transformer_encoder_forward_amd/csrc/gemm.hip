@@ -69,7 +69,8 @@ namespace {
 // down projections 75) take 64 x 256 tiles of 8 waves (64 x 32 each, two
 // blocks per CU), measured 6% / 28% / 26% faster there and 15-25% slower at
 // 8448 rows.  Gated: 256 x (128 + 128) with at least 512 tiles of 256 x 128,
-// else 128 x (128 + 128) (6% faster at 1056 rows).  Otherwise (K % 64 != 0)
+// else 128 x (128 + 128) (6% faster at 1056 rows) with a five-stage ring (the
+// whole LDS; 0.6% faster per forward than three).  Otherwise (K % 64 != 0)
 // the register-staged 128 x 128 kernel.  All sum in the same K order.
 constexpr uint32_t kWideTiles = 256, kWideGated = 512;
 
@@ -80,7 +81,7 @@ hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     if (kmul(a, 64)) {
         if (gated)
             return tiles_of(a, 256, 128) >= kWideGated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
-                                                       : gemm::launch_q8d<128, 256, 2, 4, 1, true>(a, s);
+                                                       : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
         return tiles_of(a, 256, 256) >= kWideTiles ? gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s)
                                                    : gemm::launch_q8d<64, 256, 1, 8, 2, false>(a, s);
     }

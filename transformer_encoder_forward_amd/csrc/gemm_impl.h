@@ -773,15 +773,31 @@ __device__ __forceinline__ void frag_ready(u32x4 (&a)[FM], u32x4 (&b)[FN]) {
     for (int j = 0; j < FN; j++) ready(b[j]);
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+// Wait until at most k stages of NDMA loads each are in flight, 0 <= k <= KMAX.
+template <int NDMA, int KMAX>
+__device__ __forceinline__ void vm_wait_stages(int k) {
+    if constexpr (KMAX > 0) {
+        if (k >= KMAX) {
+            vm_wait<KMAX * NDMA>();
+            return;
+        }
+        vm_wait_stages<NDMA, KMAX - 1>(k);
+    } else {
+        vm_wait<0>();
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs a) {
-    constexpr int NW = WGM * WGN, BK = 64, NS = 3;
+    constexpr int NW = WGM * WGN, BK = 64;
+    static_assert(NS >= 2, "stages");
     constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
     constexpr int A_BYTES = BM * BK * 2, S_BYTES = A_BYTES + BN * BK;
     constexpr int AL = A_BYTES / 1024 / NW, BL = BN * BK / 1024 / NW;  // loads per wave per stage
     constexpr int NDMA = AL + BL;
     static_assert(AL >= 1 && BL >= 1 && AL * 1024 * NW == A_BYTES && BL * 1024 * NW == BN * BK, "loads");
     static_assert(FM >= 1 && FN >= 1 && (!GATED || BN / WGN == 64), "tile");
+    static_assert(NS * S_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
 
     TileCtx t;
@@ -879,15 +895,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
     };
 
     const int nst = K / BK;
-    dma(0);
-    if (nst > 1) dma(1);
-    if (nst > 2) dma(2);
-    if (nst > 2)
-        vm_wait<2 * NDMA>();
-    else if (nst > 1)
-        vm_wait<NDMA>();
-    else
-        vm_wait<0>();
+    // the first min(NS, nst) stages; stage 0 awaited, the others may fly
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0++)
+        if (s0 < nst) dma(s0);
+    vm_wait_stages<NDMA, NS - 1>(min(NS, nst) - 1);
     block_barrier();
     read_a(fa0, 0, 0);
     read_b(fb0, 0, 0);
@@ -906,16 +918,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
         lgkm_wait_n<FM>();  // fa0, fb1 landed
         frag_ready(fa0, fb1);
         mma(fa0, fb1, 0);
-        // stage s+1 landed (own loads), own reads of buffer b done; after the
-        // barrier every wave's are, so b takes stage s+3
-        if (s + 2 < nst)
-            vm_wait<NDMA>();
-        else
-            vm_wait<0>();
+        // stage s+1 landed (own loads; stages s+2 .. s+NS-1 may fly), own
+        // reads of buffer b done; after the barrier every wave's are, so b
+        // takes stage s+NS
+        vm_wait_stages<NDMA, NS - 2>(min(NS - 2, nst - s - 2));
         lgkm_wait_n<0>();
         frag_ready(fa1, fb1);
         block_barrier();
-        if (s + 3 < nst) dma(s + 3);
+        if (s + NS < nst) dma(s + NS);
         if (s + 1 < nst) {
             read_a(fa0, (s + 1) % NS, 0);
             read_b(fb0, (s + 1) % NS, 0);
@@ -954,11 +964,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED>
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
 hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((gemm_q8d_kernel<BM, BN, WGM, WGN, MINB, GATED>), dim3(tiles), dim3(64 * WGM * WGN), 0, s, g);
+    hipLaunchKernelGGL((gemm_q8d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS>), dim3(tiles), dim3(64 * WGM * WGN), 0, s,
+                       g);
     return hipGetLastError();
 }
 
