@@ -30,10 +30,12 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // tanh(u) = sign(u) (1 - e) / (1 + e), e = exp(-2|u|): no cancellation for
-// small |u| beyond the f32 rounding of e.
+// small |u| beyond the f32 rounding of e.  The divisor lies in (1, 2], so the
+// quotient is taken as a product with the hardware reciprocal (within 1 ulp)
+// instead of the IEEE division sequence.
 __device__ __forceinline__ float tanh_f32(float u) {
     float e = __expf(-2.0f * fabsf(u));
-    float t = (1.0f - e) / (1.0f + e);
+    float t = (1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e);
     return copysignf(t, u);
 }
 
@@ -43,7 +45,9 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return 0.5f * x * (1.0f + tanh_f32(c * (x + 0.044715f * x * x * x)));
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x / (1 + exp(-x)); the divisor lies in (1, inf], where the
+// hardware reciprocal is within 1 ulp (and 0 at inf, as the division gives)
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
