@@ -29,7 +29,7 @@ CPU_LAYERS = 4
 def gemm_source_hash():
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm_impl.h", "gemm.hip"):
+    for f in ("gemm_impl.h", "gemm.hip", "dev.h"):  # dev.h: the epilogues' helpers
         with open(os.path.join(ROOT, "transformer_encoder_forward_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
