@@ -554,6 +554,29 @@ def test_qk_norm_rope(hd, sections, f16, nq, nkv):
     assert np.array_equal(got[:, (nq + nkv) * hd:], pp[:, (nq + nkv) * hd:])  # v untouched
 
 
+@pytest.mark.parametrize("hd,f16,sections", [(128, True, 2), (64, False, 1)])
+def test_qk_norm_rope_head_grouping_bit_identical(hd, f16, sections):
+    """Few rows split each row's heads over several waves, many rows take one wave
+    per row: a row's bits do not depend on which."""
+    rng = np.random.default_rng(17 + hd)
+    rows, nq, nkv = 9000, 30 if f16 else 8, 30 if f16 else 8
+    ld = (nq + 2 * nkv) * hd
+    p = rng.normal(0, 2, (rows, ld)).astype(np.float16 if f16 else np.float32)
+    qw = rng.normal(1, 0.02, hd).astype(np.float32)
+    kw = rng.normal(1, 0.02, hd).astype(np.float32)
+    pos = rng.integers(0, 2048, (rows, sections)).astype(np.int32)
+    cos, sin = B.rope_table(pos, hd, sections, 10000.0)
+    path = B.ENC_I8F16 if f16 else B.ENC_F32
+    Pall = to_dev(p)
+    B.qk_norm_rope(Pall, nq, nkv, hd, to_dev(qw), to_dev(kw), 1e-6, to_dev(cos), to_dev(sin),
+                   sections, path=path)
+    for r0, r1 in ((0, 500), (4321, 4400), (8999, 9000)):
+        P = to_dev(p[r0:r1])
+        B.qk_norm_rope(P, nq, nkv, hd, to_dev(qw), to_dev(kw), 1e-6, to_dev(cos[r0:r1]),
+                       to_dev(sin[r0:r1]), sections, path=path)
+        assert torch.equal(P, Pall[r0:r1])
+
+
 def test_rms_norm_prescale_and_add_norm_scalar():
     """rms(pre x) w (the per-layer input's norm) and h = (h + rms(t) w) post (the
     layer scalar) against the oracle's norms; pre = post = 1 is bit-identical to
