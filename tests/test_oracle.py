@@ -323,15 +323,21 @@ def test_pre_ln_layer_matches_torch_encoder_layer(oracle):
     assert np.abs(out - ref).max() / np.abs(ref).max() < 1e-13
 
 
-def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None):
+F16_SITES = ("A", "panel", "qk", "att", "A2", "hidden")
+
+
+def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None, skip=()):
     """Composition of torch f64 library ops in the sandwich order (independent check).
     GQA by repeating each kv head over its query group; the text-encoder options
     (v-norm, per-layer window, per-layer input from x0, layer scalar) as written
-    on the page."""
+    on the page.  With f16, the half sites round to binary16, except those named
+    in `skip` (used to show that the comparison notices a missing site)."""
     F = torch.nn.functional
     T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
     eps, hd, nq, nkv = c["eps"], c["hd"], c["nq"], c["nkv"]
-    r16 = (lambda a: a.to(torch.float16).to(torch.float64)) if f16 else (lambda a: a)
+
+    def r16(a, site):
+        return a if (not f16 or site in skip) else a.to(torch.float16).to(torch.float64)
     H = T(x)
     d = H.shape[1]
 
@@ -340,8 +346,8 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None):
             return a @ T(t[name]).T
         return (a @ T(t[name].astype(np.float64)).T) * T(t["s" + name[1:]])
 
-    A = r16(F.rms_norm(H, (d,), T(t["norm1_w"]), eps))
-    q, k, v = r16(lin(A, "wq")), r16(lin(A, "wk")), r16(lin(A, "wv"))
+    A = r16(F.rms_norm(H, (d,), T(t["norm1_w"]), eps), "A")
+    q, k, v = r16(lin(A, "wq"), "panel"), r16(lin(A, "wk"), "panel"), r16(lin(A, "wv"), "panel")
     cos, sin = pos_cos_sin
 
     def qk(z, wn, nh):
@@ -354,11 +360,12 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None):
             cs, sn = cos[s][:, None, :], sin[s][:, None, :]
             a, b = zz[..., :S // 2], zz[..., S // 2:]
             parts += [a * cs - b * sn, b * cs + a * sn]
-        return r16(torch.cat(parts, -1).reshape(z.shape[0], nh * hd))
+        return r16(torch.cat(parts, -1).reshape(z.shape[0], nh * hd), "qk")
 
     q, k = qk(q, t["q_norm_w"], nq), qk(k, t["k_norm_w"], nkv)
     if c.get("v_norm"):
-        v = r16(F.rms_norm(v.view(-1, nkv, hd), (hd,), None, eps).reshape(v.shape[0], nkv * hd))
+        v = r16(F.rms_norm(v.view(-1, nkv, hd), (hd,), None, eps).reshape(v.shape[0], nkv * hd),
+                "qk")
     att = torch.zeros_like(q)
     W = t.get("window", c["window"])
     for rr in items:
@@ -371,12 +378,12 @@ def _torch_sandwich_layer(c, t, x, pos_cos_sin, items, f16, x0=None):
         vh = v[idx].view(L, nkv, hd).transpose(0, 1).repeat_interleave(nq // nkv, 0)
         o = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=c["attn_scale"])
         att[idx] = o.transpose(0, 1).reshape(L, nq * hd)
-    att = r16(att)
+    att = r16(att, "att")
     H = H + F.rms_norm(lin(att, "wo"), (d,), T(t["post_attn_w"]), eps)
-    A = r16(F.rms_norm(H, (d,), T(t["norm2_w"]), eps))
+    A = r16(F.rms_norm(H, (d,), T(t["norm2_w"]), eps), "A2")
     g, u = lin(A, "w_gate"), lin(A, "w_up")
     act = F.gelu(g, approximate="tanh") if c["mlp"] == wl.MLP_GELU_GATED else F.silu(g)
-    m = r16(act * u)
+    m = r16(act * u, "hidden")
     H = H + F.rms_norm(lin(m, "w_down"), (d,), T(t["post_ff_w"]), eps)
     if c.get("n_ple"):
         P = F.rms_norm(c["ple_scale"] * (T(x0) @ T(t["ple_in"]).T), (c["n_ple"],),
@@ -413,10 +420,16 @@ def test_sandwich_layer_matches_torch_composition(oracle, name, kw):
     f16 = c["path"] == wl.PATH_I8F16
     ref = _torch_sandwich_layer(c, w.layers[0], w.x, ang, w.items, f16)
     out = oracle.forward(w)
-    # the f16 sites can flip a rounding where the two orders of the same sum differ
-    tol = 1e-3 if f16 else 1e-12
-    assert np.abs(out - ref).max() / np.abs(ref).max() < tol
+    err = lambda a: np.abs(out - a).max() / np.abs(a).max()
+    # both sides round the same f64 values to half at the same six sites; where
+    # the two summation orders put a value on either side of a half rounding
+    # point (one row of the DiT case) the result moves by ~1e-8
+    assert err(ref) < (1e-6 if f16 else 1e-12)
     if f16:
+        # each site matters: leaving any one out moves the result by > 1e-4
+        for site in F16_SITES:
+            alt = _torch_sandwich_layer(c, w.layers[0], w.x, ang, w.items, True, skip=(site,))
+            assert err(alt) > 1e-5, site
         out64 = oracle.forward(w, f16_sites=False)
         ref64 = _torch_sandwich_layer(c, w.layers[0], w.x, ang, w.items, False)
         assert np.abs(out64 - ref64).max() / np.abs(ref64).max() < 1e-12
@@ -627,6 +640,84 @@ def test_meanpool_of_identical_rows(oracle):
     assert np.allclose(out[0], oracle.rms_norm(w.x[:1], w.final_w, 1e-6)[0], rtol=1e-15)
     assert np.allclose(out[1], oracle.rms_norm(w.x[4:5], w.final_w, 1e-6)[0], rtol=1e-15)
     assert out.shape == (2, d)
+
+
+class _Tiny:
+    """A workload-like object with no layers: only the final stage acts."""
+
+    def __init__(self, rows, items, w, b=None, final=wl.FINAL_RMS_MEANPOOL, eps=0.0):
+        x = np.asarray(rows, np.float32)
+        self.cfg = dict(d=x.shape[1], final=final, eps=eps)
+        self.rows, self.items, self.grids = x.shape[0], items, [0] * len(items)
+        self.x, self.layers = x, []
+        self.final_w = np.asarray(w, np.float32)
+        self.final_b = None if b is None else np.asarray(b, np.float32)
+
+
+def test_final_rms_then_pool_hand_values(oracle):
+    """The text encoder's output: each row RMS-normed with the final weight, then the
+    mean over the item's rows (two-range items, unequal lengths).  Norming the pooled
+    mean instead gives other values (tests/golden/final_stage.json)."""
+    g = _gold("final_stage.json")["rms_then_pool"]
+    items = [[tuple(r) for r in it] for it in g["items"]]
+    out = oracle.forward(_Tiny(g["rows"], items, g["w"]), layers=0)
+    assert np.allclose(out, np.asarray(g["out"]), rtol=0, atol=1e-15)
+
+
+def test_final_rms_then_pool_matches_torch_f64(oracle):
+    """Random rows and items of unequal length: torch rms_norm per row, then the mean."""
+    rng = np.random.default_rng(11)
+    lens = [3, 17, 1, 40]
+    rows = rng.standard_normal((sum(lens), 24)).astype(np.float32) * 3
+    w = (1 + 0.1 * rng.standard_normal(24)).astype(np.float32)
+    items, r = [], 0
+    for n in lens:
+        items.append([(r, n)])
+        r += n
+    out = oracle.forward(_Tiny(rows, items, w, eps=1e-6), layers=0)
+    R = torch.nn.functional.rms_norm(torch.from_numpy(rows.astype(np.float64)), (24,),
+                                     torch.from_numpy(w.astype(np.float64)), 1e-6)
+    ref = np.stack([R[r0:r0 + n].mean(0).numpy() for (r0, n), in items])
+    assert np.abs(out - ref).max() < 1e-14
+
+
+def test_post_ln_stack_matches_torch_encoder(oracle):
+    """Two pre-LN layers and the final LayerNorm == torch.nn.TransformerEncoder with
+    norm=LayerNorm in f64 (the ViT's post-LN after the blocks)."""
+    w = wl.make("lfm2_vit_f32", layers=2, lengths=[40],
+                overrides=dict(d=128, nq=2, nkv=2, ff=256))
+    c = w.cfg
+    d = c["d"]
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    proto = torch.nn.TransformerEncoderLayer(
+        d, c["nq"], dim_feedforward=c["ff"], dropout=0.0,
+        activation=lambda x: torch.nn.functional.gelu(x, approximate="tanh"),
+        layer_norm_eps=c["eps"], batch_first=True, norm_first=True, dtype=torch.float64)
+    norm = torch.nn.LayerNorm(d, eps=c["eps"], dtype=torch.float64)
+    enc = torch.nn.TransformerEncoder(proto, 2, norm=norm, enable_nested_tensor=False)
+    with torch.no_grad():
+        for layer, t in zip(enc.layers, w.layers):
+            layer.self_attn.in_proj_weight.copy_(T(np.concatenate([t["wq"], t["wk"], t["wv"]])))
+            layer.self_attn.in_proj_bias.copy_(T(np.concatenate([t["bq"], t["bk"], t["bv"]])))
+            layer.self_attn.out_proj.weight.copy_(T(t["wo"]))
+            layer.self_attn.out_proj.bias.copy_(T(t["bo"]))
+            layer.linear1.weight.copy_(T(t["w_up"]))
+            layer.linear1.bias.copy_(T(t["b_up"]))
+            layer.linear2.weight.copy_(T(t["w_down"]))
+            layer.linear2.bias.copy_(T(t["b_down"]))
+            layer.norm1.weight.copy_(T(t["norm1_w"]))
+            layer.norm1.bias.copy_(T(t["norm1_b"]))
+            layer.norm2.weight.copy_(T(t["norm2_w"]))
+            layer.norm2.bias.copy_(T(t["norm2_b"]))
+        enc.norm.weight.copy_(T(w.final_w))
+        enc.norm.bias.copy_(T(w.final_b))
+        ref = enc(T(w.x)[None])[0].numpy()
+    out = oracle.forward(w)
+    assert np.abs(out - ref).max() / np.abs(ref).max() < 1e-13
+    # the final LN acts: without it the rows are not normalised
+    bare = dict(w.cfg, final=wl.FINAL_NONE)
+    w.cfg = bare
+    assert np.abs(oracle.forward(w) - out).max() > 1e-3
 
 
 def test_nonfinite_input_propagates(oracle):
