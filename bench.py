@@ -1,16 +1,19 @@
 """Throughput of the packed encoder forward on one MI355X.
 
-Default workload: the EmbeddingGemma-style text encoder (f32, 24 sandwich layers,
-d 512, 8x64 heads, qk-norm + 1-D RoPE, window 512, gated GELU 2048, 16 packed
-sequences of 32..2048 rows drawn from the seeded length stream, final RMS + mean
-pool), synthetic seeded inputs and random-init weights.  A step is one
+Default workload: the Z-Image-style DiT stack as a CFG batch-2 program (30
+sandwich layers, d 3840, 30x128 heads, int8 row-scaled weights x f16
+activations with f32 accumulation, qk-norm + 2-D RoPE over a 64x64 grid plus
+128 caption rows per item, SwiGLU 10240; rows [img0|img1|cap0|cap1] = 8448),
+synthetic seeded inputs and random-init weights.  Any other workload is taken
+with --workload (the text encoder: gemma_text_f32).  A step is one
 encoder_forward over the whole packed batch, inputs already resident in HBM.
 
 Prints one JSON line: value = encoder TFLOP/s, algorithmic (GEMM + attention)
 flops / wall time of K steps; the roofline of the dominant kernel class (the
 GEMMs) from per-launch HIP events recorded by the library on the stream the
 kernels run on; and the f64 oracle timed on the host cores on a bounded sample
-(the first layers of the same batch).
+of the same workload (the first layers of the f32 batches; layer 0 of the DiT
+model over 1024 of its image rows).
 """
 import argparse
 import json
@@ -50,12 +53,52 @@ def measured_traffic(workload):
     return float(val.group(1))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(name, cfg, w):
+    """The f64 oracle as it stands, timed on the host cores over a bounded sample of
+    the same workload (about 10-30 s): the f32 batches' first CPU_LAYERS layers over
+    the whole packed batch; for the int8 DiT, layer 0 of the same model over the
+    first 1024 image rows as one 32x32-grid item (each row's GEMM work is the full
+    workload's; attention sees 1024 keys instead of the item's own count)."""
+    import oracle
+
+    from transformer_encoder_forward_amd import workloads as wl
+
+    if cfg["path"] == wl.PATH_F32:
+        nl = min(CPU_LAYERS, cfg["layers"])
+        sample = wl.make(name, layers=nl)
+        sample.cfg["final"] = wl.FINAL_NONE
+        what = (f"first {nl} of {cfg['layers']} layers over the same {len(w.items)}-item batch "
+                f"({w.rows} rows)")
+    else:
+        sample = wl.make(name, layers=1, grid=32, ncap=0, cfg_pair=False)
+        what = (f"layer 0 of the same model ({cfg['layers']} layers) over its first "
+                f"{sample.rows} image rows as one 32x32-grid item, f16 sites on")
+    c0 = time.perf_counter()
+    oracle.forward(sample)
+    cdt = time.perf_counter() - c0
+    cfl = wl.gemm_flops(sample) + wl.attn_flops(sample)
+    return {"value": round(cfl / cdt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{what}: {cfl / 1e9:.1f} GFLOP in {cdt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gemma_text_f32")
+    ap.add_argument("--workload", default="zimage_dit_cfg_8448")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=None, help="(development) fewer layers")
     args = ap.parse_args()
@@ -152,24 +195,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        # a bounded sample of the same workload: its first CPU_LAYERS layers over the
-        # whole packed batch (about 10-20 s on 16 host cores)
-        nl = min(CPU_LAYERS, cfg["layers"])
-        sample = wl.make(args.workload, layers=nl, lazy_int8=False) if cfg["path"] == wl.PATH_F32 \
-            else None
-        if sample is not None:
-            sample.cfg["final"] = wl.FINAL_NONE
-            c0 = time.perf_counter()
-            oracle.forward(sample)
-            cdt = time.perf_counter() - c0
-            cfl = wl.gemm_flops(sample) + wl.attn_flops(sample)
-            cpu = {"value": round(cfl / cdt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.threads(),
-                   "kind": "oracle",
-                   "sample": f"first {nl} of {cfg['layers']} layers over the same "
-                             f"{len(w.items)}-item batch ({w.rows} rows), "
-                             f"{cfl / 1e9:.1f} GFLOP in {cdt:.1f} s"}
-
+        cpu = cpu_baseline(args.workload, cfg, w)
     res = {
         "metric": "encoder TFLOP/s (GEMM+attn) and % of MI355X MFMA peak; tokens/s per layer",
         "value": round(tflops, 3),

@@ -385,9 +385,22 @@ typedef struct {
  * batch.amax is set).  0 on null input. */
 ENC_API size_t enc_workspace_bytes(const enc_model *model, const enc_batch *batch);
 
-/* One layer in place on h (dev, f32 [rows][d]), computing its own pre-norm. */
-ENC_API enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_batch *batch,
-                                 float *h, void *ws, size_t ws_bytes, enc_stream stream);
+/* One layer in place on h (dev, f32 [rows][d]).
+ * a (dev, nullable): the layer's pre-normed input, the A that its q/k/v GEMM
+ * reads: for the sandwich block rms(h; norm1_w) (times 1 + mod_s_attn, the
+ * q/k/v column fields and 2^-guard_attn), one [rows][d] copy per column field
+ * (three with col_q/col_k/col_v, else one); for pre-LN LN(h; norm1_w, norm1_b).
+ * Half on the int8 path, f32 otherwise.  NULL: the layer computes it.
+ * next (host, nullable; needs a): the following layer, same block kind, path
+ * and width.  Its pre-normed input is then written into a from the updated h
+ * before return, by the sandwich block's last row op itself ([EG] `Prog::add_norm`:
+ * H = (H + rms(T) w) post, then A = rms(H) w2) and by one LN pass for pre-LN,
+ * so a chain of calls (a = NULL for the first, then a and next) gives the bits
+ * of encoder_forward.  a must then hold max(copies of this layer, copies of
+ * next) x rows x d elements.  Without next, a is read and left unchanged. */
+ENC_API enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_layer *next,
+                                         const enc_batch *batch, float *h, void *a, void *ws,
+                                         size_t ws_bytes, enc_stream stream);
 
 /* The whole forward: x (dev, f32 [rows][d], not modified unless out == x) ->
  * out (dev, f32, [rows][d] or [nitems][d] for RMS_MEANPOOL).  Each layer's last

@@ -82,18 +82,31 @@ def test_forward_vs_oracle(name, kw):
 ])
 def test_fused_chain_equals_layer_by_layer(name, kw):
     """encoder_forward (each layer's last row op writes the next pre-norm) gives
-    the same bits as encoder_layer_forward called per layer."""
+    the same bits as encoder_layer_forward called per layer, both with each layer
+    computing its own pre-norm and as a chain that hands the next layer's input
+    over in `a` (written by the last row op of the layer before)."""
     w = wl.make(name, **kw)
     w.cfg["final"] = wl.FINAL_NONE
     fused = run(w)
     dm = M.DeviceModel(w, DEV)
     db = M.DeviceBatch(w, DEV)
-    h = torch.from_numpy(w.x.copy()).to(DEV)
     x0 = torch.from_numpy(w.x.copy()).to(DEV)
     db.batch.ple_x = x0.data_ptr()  # the rows the per-layer inputs project
     ws = dm.workspace(db, DEV)
-    for li in range(w.cfg["layers"]):
+    nl = w.cfg["layers"]
+    h = torch.from_numpy(w.x.copy()).to(DEV)
+    for li in range(nl):
         M.encoder_layer_forward(dm, li, db, h, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, h)
+    # the chain: layer 0 computes its pre-norm; each call writes the next one's
+    copies = 3 if w.cfg.get("col_fields") else 1
+    esz = torch.float16 if w.cfg["path"] == wl.PATH_I8F16 else torch.float32
+    a = torch.full((copies * w.rows * w.cfg["d"],), float("nan"), dtype=esz, device=DEV)
+    h = torch.from_numpy(w.x.copy()).to(DEV)
+    M.layer_input(dm, 0, h, a)
+    for li in range(nl):
+        M.encoder_layer_forward(dm, li, db, h, ws, a=a, next_layer=li + 1 if li + 1 < nl else None)
     torch.cuda.synchronize()
     assert torch.equal(fused, h)
 

@@ -183,7 +183,8 @@ def lib():
     L.enc_workspace_bytes.restype = C.c_size_t
     L.enc_attention_workspace_bytes.argtypes = [C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32]
     L.enc_attention_workspace_bytes.restype = C.c_size_t
-    L.encoder_layer_forward.argtypes = [P, C.POINTER(Layer), C.POINTER(Batch), P, P, C.c_size_t, P]
+    L.encoder_layer_forward.argtypes = [P, C.POINTER(Layer), C.POINTER(Layer), C.POINTER(Batch), P,
+                                        P, P, C.c_size_t, P]
     L.encoder_forward.argtypes = [P, C.POINTER(Model), C.POINTER(Batch), P, P, P, C.c_size_t, P]
     L.encoder_stages_forward.argtypes = [P, C.POINTER(Stage), C.c_uint32, C.c_uint32, P, P, P,
                                          C.c_size_t, P]

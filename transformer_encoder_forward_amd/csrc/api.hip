@@ -841,20 +841,25 @@ hipError_t run_ple(const enc_layer &L, uint32_t rows, const float *x0, const flo
     return proj(b.z, np, L.ple_proj, d, b.t);
 }
 
-// One layer on h.  On entry, for the sandwich block, A holds the layer's q/k/v
-// input(s) (pre-LN computes its own LN).  On exit the last row op has written
-// the next inputs `nx` (sandwich only; none when nx.w == NULL).  amax: this
-// layer's five slots, or NULL.
+// One layer on h.  ain: for the sandwich block the layer's q/k/v input(s)
+// (its pre-norm, already computed); for pre-LN the LN1 output, or NULL for the
+// layer to compute it into b.a.  On exit the last row op of a sandwich layer
+// has written the next inputs `nx` into aout (none when nx.w == NULL); ain may
+// equal aout or b.a (each is read before it is written).  amax: this layer's
+// five slots, or NULL.
 hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, float *h, const Bufs &b,
-                     const NextIn &nx, float *amax, hipStream_t s) {
+                     const void *ain, void *aout, const NextIn &nx, float *amax, hipStream_t s) {
     const uint32_t rows = B->rows, d = L.d, hd = L.hd;
     const uint32_t qw = L.nq * hd, kw = L.nkv * hd, ld = qw + 2 * kw;
     const bool i8 = L.path == ENC_I8F16;
     const bool sandwich = L.block == ENC_SANDWICH_RMS;
     const int ga = L.guard_attn, gq = L.guard_qkv, gao = L.guard_ao, gf = L.guard_ffn, gh = L.guard_hid;
     const uint64_t rd = (uint64_t)rows * d;
-    if (!sandwich) TRY(pre_norm(L, rows, h, b.a, s));
-    if (amax) TRY(amax_site(b.a, rd * nout_attn(L), b.amax, amax + 0, s));
+    if (!ain) {
+        TRY(pre_norm(L, rows, h, b.a, s));
+        ain = b.a;
+    }
+    if (amax) TRY(amax_site(ain, rd * nout_attn(L), b.amax, amax + 0, s));
 
     // q|k|v projections: one launch, three items (each reading its own copy of
     // A when the weights carry column fields); 2^(ga - gq): undo the input
@@ -862,7 +867,7 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
     {
         enc_gemm_desc g{};
         g.path = L.path;
-        g.x = b.a;
+        g.x = ain;
         g.y = b.panel;
         g.w[0] = L.wq; g.w[1] = L.wk; g.w[2] = L.wv;
         g.row_scale[0] = L.sq; g.row_scale[1] = L.sk; g.row_scale[2] = L.sv;
@@ -978,11 +983,11 @@ hipError_t run_layer(const enc_layer &L, const enc_batch *B, const float *x0, fl
     if (sandwich) {
         const float scalar = L.scalar == 0.0f ? 1.0f : L.scalar;
         if (!L.n_ple) {
-            TRY(row_op(L, rows, h, b.t, L.post_ff_w, L.mod_g_ff, scalar, nx, b.a, i8, s));
+            TRY(row_op(L, rows, h, b.t, L.post_ff_w, L.mod_g_ff, scalar, nx, aout, i8, s));
         } else {
             TRY(row_op(L, rows, h, b.t, L.post_ff_w, L.mod_g_ff, 1.0f, NextIn{}, nullptr, false, s));
             TRY(run_ple(L, rows, x0, h, b, s));
-            TRY(row_op(L, rows, h, b.t, L.ple_post_w, nullptr, scalar, nx, b.a, false, s));
+            TRY(row_op(L, rows, h, b.t, L.ple_post_w, nullptr, scalar, nx, aout, false, s));
         }
     }
     return hipSuccess;
@@ -1002,7 +1007,9 @@ hipError_t run_stack(const enc_model *model, const enc_batch *batch, const float
             else if (fused_final(model))
                 nx.w = model->final_w;  // the final RMS (f32) written by the last row op
         }
-        TRY(run_layer(model->layers[l], batch, x0, h, b, nx, batch->amax ? batch->amax + 5 * l : nullptr, s));
+        const void *ain = L0.block == ENC_SANDWICH_RMS ? b.a : nullptr;
+        TRY(run_layer(model->layers[l], batch, x0, h, b, ain, b.a, nx, batch->amax ? batch->amax + 5 * l : nullptr,
+                      s));
     }
     return hipSuccess;
 }
@@ -1254,8 +1261,9 @@ size_t enc_attention_workspace_bytes(const enc_attn_desc *desc, const enc_item *
     return attn_ws_bytes(desc, items, nitems);
 }
 
-enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_batch *batch, float *h,
-                                 void *ws, size_t ws_bytes, enc_stream stream) {
+enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc_layer *next,
+                                 const enc_batch *batch, float *h, void *a, void *ws, size_t ws_bytes,
+                                 enc_stream stream) {
     Err e;
     if (!ctx) return ENC_EINVAL;
     CtxScope cs(ctx);
@@ -1263,23 +1271,37 @@ enc_status encoder_layer_forward(enc_ctx *ctx, const enc_layer *layer, const enc
         e.set(ENC_EINVAL, "encoder_layer_forward: null layer, h or workspace");
         return finish(ctx, e);
     }
-    enc_model M{1, layer, ENC_FINAL_NONE, nullptr, nullptr, 0.0f};
+    if (next && !a) {
+        e.set(ENC_EINVAL, "encoder_layer_forward: the next layer's input needs a (the buffer it is written to)");
+        return finish(ctx, e);
+    }
+    // the layer (and the next one, which must match its block kind, path and width)
+    const enc_layer pair[2] = {*layer, next ? *next : *layer};
+    enc_model M{next ? 2u : 1u, pair, ENC_FINAL_NONE, nullptr, nullptr, 0.0f};
     if (check_model(e, &M, batch) != ENC_OK) return finish(ctx, e);
     if (layer->n_ple && (!batch->ple_x || batch->ple_x == h)) {
         e.set(ENC_EINVAL, "encoder_layer_forward: the per-layer input needs batch ple_x (not h)");
         return finish(ctx, e);
     }
     const WsPlan p = plan_ws(&M, batch);
-    if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(h, 16)) {
-        e.set(ENC_EINVAL, "encoder_layer_forward: workspace needs %zu bytes, 256-byte aligned",
+    if (ws_bytes < p.total || !aligned(ws, 256) || !aligned(h, 16) || (a && !aligned(a, 16))) {
+        e.set(ENC_EINVAL, "encoder_layer_forward: workspace needs %zu bytes, 256-byte aligned (h, a 16-byte)",
               p.total);
         return finish(ctx, e);
     }
     const Bufs b = carve(ws, p);
     hipStream_t s = (hipStream_t)stream;
     hipError_t hr = hipSuccess;
-    if (layer->block == ENC_SANDWICH_RMS) hr = pre_norm(*layer, batch->rows, h, b.a, s);
-    if (hr == hipSuccess) hr = run_layer(*layer, batch, batch->ple_x, h, b, NextIn{}, batch->amax, s);
+    const bool sandwich = layer->block == ENC_SANDWICH_RMS;
+    const void *ain = a;
+    if (!ain && sandwich) {
+        hr = pre_norm(*layer, batch->rows, h, b.a, s);
+        ain = b.a;
+    }
+    const NextIn nx = next && sandwich ? attn_in(*next) : NextIn{};
+    if (hr == hipSuccess) hr = run_layer(*layer, batch, batch->ple_x, h, b, ain, a, nx, batch->amax, s);
+    // pre-LN: the next layer's LN1 of the updated rows
+    if (hr == hipSuccess && next && !sandwich) hr = pre_norm(*next, batch->rows, h, a, s);
     launch_status(e, hr, "encoder_layer_forward");
     return finish(ctx, e);
 }

@@ -131,11 +131,45 @@ def encoder_forward(model: DeviceModel, batch: DeviceBatch, x, out, ws, ctx=None
 
 
 def encoder_layer_forward(model: DeviceModel, layer: int, batch: DeviceBatch, h, ws, ctx=None,
-                          stream=None):
+                          stream=None, a=None, next_layer=None):
+    """Layer `layer` in place on h.  a: the layer's pre-normed input (None: the
+    layer computes it); next_layer: the index of the layer whose input the call
+    then writes into a (needs a)."""
     ctx = ctx or B.context()
-    ctx.check(B.lib().encoder_layer_forward(ctx.h, C.byref(model.layers[layer]),
-                                            C.byref(batch.batch), h.data_ptr(), ws.data_ptr(),
-                                            ws.numel(), B._stream(stream)))
+    nxt = C.byref(model.layers[next_layer]) if next_layer is not None else None
+    ctx.check(B.lib().encoder_layer_forward(ctx.h, C.byref(model.layers[layer]), nxt,
+                                            C.byref(batch.batch), h.data_ptr(),
+                                            a.data_ptr() if a is not None else None,
+                                            ws.data_ptr(), ws.numel(), B._stream(stream)))
+
+
+def layer_input(model: DeviceModel, layer: int, h, a, ctx=None, stream=None):
+    """The pre-normed input of layer `layer` from the rows h, into a: the first
+    call of a chain of encoder_layer_forward calls that hand each next layer's
+    input over in a.  Sandwich: enc_add_norm without a residual (rms(h) w (1 + s),
+    one copy per column field, times 2^-guard); pre-LN: enc_layer_norm."""
+    ctx = ctx or B.context()
+    L = model.layers[layer]
+    f16 = L.path == wl.PATH_I8F16
+    if L.block == wl.BLOCK_PRE_LN:
+        d = B.NormDesc()
+        d.rows, d.d, d.x, d.ldx = h.shape[0], h.shape[1], h.data_ptr(), h.stride(0)
+        d.w, d.b, d.eps = L.norm1_w, L.norm1_b, L.eps
+        d.y, d.ldy, d.flags = a.data_ptr(), h.shape[1], B.ENC_Y_F16 if f16 else 0
+        ctx.check(B.lib().enc_layer_norm(ctx.h, C.byref(d), B._stream(stream)))
+        return
+    d = B.AddNormDesc()
+    d.rows, d.d, d.h, d.t = h.shape[0], h.shape[1], h.data_ptr(), None
+    d.w_next, d.eps, d.a = L.norm1_w, L.eps, a.data_ptr()
+    d.flags = B.ENC_Y_F16 if f16 else 0
+    d.scale = L.mod_s_attn
+    cols = (L.col_q, L.col_k, L.col_v)
+    if any(cols):
+        for z, c in enumerate(cols):
+            d.col[z] = c
+        d.nout = 3
+    d.oscale = 2.0 ** -int(L.guard_attn)
+    ctx.check(B.lib().enc_add_norm(ctx.h, C.byref(d), B._stream(stream)))
 
 
 def out_rows(w: wl.Workload):
