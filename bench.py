@@ -13,7 +13,7 @@ flops / wall time of K steps; the roofline of the dominant kernel class (the
 GEMMs) from per-launch HIP events recorded by the library on the stream the
 kernels run on; and the f64 oracle timed on the host cores on a bounded sample
 of the same workload (the first layers of the f32 batches; layer 0 of the DiT
-model over 1024 of its image rows).
+model over 1600 of its image rows).
 """
 import argparse
 import json
@@ -68,8 +68,8 @@ def cpu_baseline(name, cfg, w):
     """The f64 oracle as it stands, timed on the host cores over a bounded sample of
     the same workload (about 10-30 s): the f32 batches' first CPU_LAYERS layers over
     the whole packed batch; for the int8 DiT, layer 0 of the same model over the
-    first 1024 image rows as one 32x32-grid item (each row's GEMM work is the full
-    workload's; attention sees 1024 keys instead of the item's own count)."""
+    first 1600 image rows as one 40x40-grid item (each row's GEMM work is the full
+    workload's; attention sees 1600 keys instead of the item's own 4224)."""
     import oracle
 
     from transformer_encoder_forward_amd import workloads as wl
@@ -81,9 +81,9 @@ def cpu_baseline(name, cfg, w):
         what = (f"first {nl} of {cfg['layers']} layers over the same {len(w.items)}-item batch "
                 f"({w.rows} rows)")
     else:
-        sample = wl.make(name, layers=1, grid=32, ncap=0, cfg_pair=False)
+        sample = wl.make(name, layers=1, grid=40, ncap=0, cfg_pair=False)
         what = (f"layer 0 of the same model ({cfg['layers']} layers) over its first "
-                f"{sample.rows} image rows as one 32x32-grid item, f16 sites on")
+                f"{sample.rows} image rows as one 40x40-grid item, f16 sites on")
     c0 = time.perf_counter()
     oracle.forward(sample)
     cdt = time.perf_counter() - c0

@@ -4,6 +4,8 @@ compute them one by one (GEMM rows, attention query rows, whole short items),
 whole outputs where a layer fits the oracle's budget, and the invariants that hold
 at any size (the CFG pair == two singles) where it does not."""
 import dataclasses
+import os
+import sys
 
 import numpy as np
 import pytest
@@ -16,6 +18,9 @@ from transformer_encoder_forward_amd import model as M
 from transformer_encoder_forward_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
+
+sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden"))
+import full_depth  # noqa: E402  (stored oracle outputs, written by tests/golden/full_depth.py)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -177,6 +182,23 @@ def test_text_encoder_full_batch_shortest_sequences(name):
         say(f"  sequence {i} (length {n}): error {err:.2e}")
         assert err <= TOL_F32
         assert np.array_equal(host(run(alone, x=x)), pooled[i:i + 1])
+
+
+@pytest.mark.parametrize("name", ["gemma_text_f32", "gemma_text_ple_f32"])
+def test_text_encoder_full_batch_every_sequence_vs_stored_oracle(name):
+    """The benchmark batch whole (16 sequences, 16 057 rows, 24 layers): every
+    pooled row, the two sequences longer than 1024 rows (where the 512-key
+    window masks) included, against the oracle's forward of the same packed
+    batch, stored by tests/golden/full_depth.py under a key of its inputs."""
+    w = wl.make(name)
+    rows, ref = full_depth.load(name, w)
+    pooled = host(run(w))
+    lens = [rr[0][1] for rr in w.items]
+    assert max(lens) > 1024
+    err = row_rel_err(pooled[rows], ref)
+    say(f"full text encoder {name}: {len(rows)} pooled rows, lengths {min(lens)}..{max(lens)}, "
+        f"error {err:.2e}")
+    assert err <= TOL_F32
 
 
 def test_vit_encoder_full_stack_vs_oracle():

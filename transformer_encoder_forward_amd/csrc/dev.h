@@ -74,6 +74,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)ENC_SHARED(const_cast<void *>(p));
 }
 
+// A direct load through a raw buffer: 16 bytes per lane from byte voff +
+// soff of the buffer into 1 KB of LDS at the wave-uniform lds.  The stage
+// offset soff and the LDS address stay in scalar registers.  (The host pass
+// of a kernel template does not take this builtin; only the device pass
+// compiles the call.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
+}
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t r, void *lds, uint32_t voff, uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ENC_SHARED(lds), 16, voff, soff, 0, 0);
+#else
+    (void)r, (void)lds, (void)voff, (void)soff;
+#endif
+}
+
 __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(ENC_GLOBAL(src), ENC_SHARED(lds_wave_base), 16, 0, 0);
 }

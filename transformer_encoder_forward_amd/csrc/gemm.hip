@@ -6,7 +6,7 @@
 // K % 32 == 0 the operands reach LDS by direct global -> LDS loads, otherwise
 // through registers.  int8 x f16: the kernel fed by
 // direct global -> LDS loads (256 x 256 tiles for large launches, 64 x 256 /
-// gated 128 x 256 for smaller ones), and K % 64 != 0 the register-staged
+// gated 128 x 256 for smaller ones), and otherwise the register-staged
 // 128 x 128.
 // Every instantiation of one path uses the same K stage and the same lane-half
 // K order, so an output element is summed in the same order whatever tile it
@@ -70,15 +70,27 @@ namespace {
 // blocks per CU), measured 6% / 28% / 26% faster there and 15-25% slower at
 // 8448 rows.  Gated: 256 x (128 + 128) with at least 512 tiles of 256 x 128,
 // else 128 x (128 + 128) (6% faster at 1056 rows) with a five-stage ring (the
-// whole LDS; 0.6% faster per forward than three).  Otherwise (K % 64 != 0)
-// the register-staged 128 x 128 kernel.  All sum in the same K order.
+// whole LDS; 0.6% faster per forward than three).  Otherwise (K % 64 != 0, or
+// an item too large for the direct loads' 32-bit offsets) the register-staged
+// 128 x 128 kernel.  All sum in the same K order.
 constexpr uint32_t kWideTiles = 256, kWideGated = 512;
 
 }  // namespace
 
+// The direct-load kernel addresses X and W by 32-bit byte offsets from the
+// item's X and the weight matrix: both must stay below 2^31.
+static bool offsets32(const GemmArgs &a) {
+    for (uint32_t i = 0; i < a.nitems; i++) {
+        const GemmItemK &it = a.items[i];
+        const uint64_t xb = ((uint64_t)(it.n ? it.n - 1 : 0) * it.ldx + it.k) * 2, wb = (uint64_t)it.m * it.k;
+        if (xb >= (1ull << 31) || wb >= (1ull << 31)) return false;
+    }
+    return true;
+}
+
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
-    if (kmul(a, 64)) {
+    if (kmul(a, 64) && offsets32(a)) {
         if (gated)
             return tiles_of(a, 256, 128) >= kWideGated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
                                                        : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
