@@ -183,6 +183,23 @@ ENC_API enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, cons
 ENC_API size_t enc_attention_workspace_bytes(const enc_attn_desc *desc, const enc_item *items,
                                              uint32_t nitems);
 
+/* attention_items for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and split plan, with the key-split partials in a
+ * static device array of ENC_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends, instead of a workspace.  The
+ * call allocates nothing.  desc->ws must be NULL and ws_bytes 0 (ENC_EINVAL
+ * otherwise); items whose splits need more than ENC_STATIC_SCRATCH_BYTES
+ * (enc_attention_workspace_bytes) are refused with ENC_EUNSUPPORTED before
+ * anything is enqueued.  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (two streams, or two threads) race on it.  Nothing
+ * in the array needs clearing: each split writes all of its partials before
+ * the merge reads them.  ENC_EDEVICE if the array's address could not be
+ * taken when ctx was created. */
+#define ENC_STATIC_SCRATCH_BYTES (32u << 20)
+ENC_API enc_status attention_items_static(enc_ctx *ctx, const enc_attn_desc *desc, const enc_item *items,
+                                          uint32_t nitems, enc_stream stream);
+
 /* ------------------------------------------------------------------ row ops */
 /* One wavefront per row (or per row and head); f32 statistics.  Geometry:
  * d % 4 == 0 and d <= 4096; strides multiples of 4 (f32) or 8 (f16). */

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "ENC_OK", 1: "ENC_EINVAL", 2: "ENC_ESHAPE", 3: "ENC_EUNSUPPOR
 
 # every symbol include/enc.h declares
 EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attention_items",
-           "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
+           "attention_items_static", "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
            "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
            "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak",
@@ -173,6 +173,7 @@ def lib():
     L.enc_last_error.restype = C.c_char_p
     L.gemm_items.argtypes = [P, C.POINTER(GemmDesc), C.POINTER(GemmItem), C.c_uint32, P]
     L.attention_items.argtypes = [P, C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32, P]
+    L.attention_items_static.argtypes = [P, C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32, P]
     L.enc_rms_norm.argtypes = [P, C.POINTER(NormDesc), P]
     L.enc_layer_norm.argtypes = [P, C.POINTER(NormDesc), P]
     L.enc_add_norm.argtypes = [P, C.POINTER(AddNormDesc), P]
@@ -200,7 +201,7 @@ def lib():
     L.enc_prof_enable.argtypes = [P, C.c_int]
     L.enc_prof_read.argtypes = [P, C.POINTER(ProfStat)]
     L.enc_mfma_peak.argtypes = [P, C.c_uint32, C.c_uint32, C.c_uint32, P, C.POINTER(C.c_double), P]
-    for f in ("gemm_items", "attention_items", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
+    for f in ("gemm_items", "attention_items", "attention_items_static", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
               "enc_qk_norm_rope", "enc_gated_act", "enc_mean_pool", "encoder_layer_forward",
               "encoder_forward", "encoder_stages_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
               "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read",
@@ -329,6 +330,22 @@ def attention_items(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_co
         d.ws, d.ws_bytes = ws.data_ptr(), ws.numel()
     arr = make_items(items)
     ctx.check(lib().attention_items(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
+
+
+def attention_items_static(qkv, out, items, nq, nkv, hd, scale, window=0, ld=None, q_col=0,
+                           k_col=None, v_col=None, ldo=None, path=ENC_F32, rows=None,
+                           out_col=None, out_scale=1.0, ctx=None, stream=None):
+    """attention_items with the key-split partials in the library's static
+    per-GPU scratch (no workspace, nothing allocated)."""
+    ctx = ctx or context()
+    d = attention_desc(qkv, out, nq, nkv, hd, scale, window, ld, q_col, k_col, v_col, ldo, path,
+                       rows)
+    d.out_col, d.out_scale = _ptr(out_col), out_scale
+    arr = make_items(items)
+    ctx.check(lib().attention_items_static(ctx.h, C.byref(d), arr, len(items), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 32 << 20  # ENC_STATIC_SCRATCH_BYTES
 
 
 def _norm(fn, x, w, b, eps, y, f16, ctx, stream, pre=1.0):

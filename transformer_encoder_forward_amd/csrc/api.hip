@@ -31,7 +31,16 @@ struct enc_ctx {
     bool prof = false;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
     std::vector<ProfRec> recs;
+    void *scratch = nullptr;   // this device's copy of `scratch` (attention_items_static)
+    std::string scratch_err;   // why it is missing, if it is
 };
+
+// Scratch of attention_items_static: the key-split partials, in a file-scope
+// device array rather than a caller workspace.  The runtime allocates one
+// copy on every device the library runs on, held until the process ends; in
+// host code `scratch` names a host-side stand-in, so its device address is
+// taken once per device (enc_create) and only that address is used.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[ENC_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -1063,6 +1072,21 @@ enc_status enc_create(int device, enc_ctx **out) {
     }
     enc_ctx *c = new enc_ctx;
     c->device = device;
+    // this device's copy of the static scratch, taken with the device current
+    int cur = 0;
+    h = hipGetDevice(&cur);
+    if (h == hipSuccess) h = hipSetDevice(device);
+    if (h == hipSuccess) {
+        void *ptr = nullptr;
+        h = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (h == hipSuccess) c->scratch = ptr;
+        const hipError_t back = hipSetDevice(cur);
+        if (h == hipSuccess) h = back;
+    }
+    if (h != hipSuccess) {
+        c->scratch = nullptr;
+        c->scratch_err = std::string("static scratch unavailable: ") + hipGetErrorString(h);
+    }
     *out = c;
     g_create_err.clear();
     return ENC_OK;
@@ -1149,6 +1173,43 @@ enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_it
     CtxScope cs(ctx);
     if (check_attn(e, desc, items, nitems) == ENC_OK)
         launch_status(e, run_attention(desc, items, nitems, (hipStream_t)stream), "attention_items");
+    return finish(ctx, e);
+}
+
+enc_status attention_items_static(enc_ctx *ctx, const enc_attn_desc *desc, const enc_item *items,
+                                  uint32_t nitems, enc_stream stream) {
+    Err e;
+    if (!ctx) return ENC_EINVAL;
+    CtxScope cs(ctx);
+    if (!desc) {
+        e.set(ENC_EINVAL, "attention_items_static: null descriptor");
+        return finish(ctx, e);
+    }
+    if (desc->ws || desc->ws_bytes) {
+        e.set(ENC_EINVAL, "attention_items_static: ws must be NULL (the call uses the library's static scratch)");
+        return finish(ctx, e);
+    }
+    if (!ctx->scratch) {
+        e.set(ENC_EDEVICE, "attention_items_static: %s", ctx->scratch_err.c_str());
+        return finish(ctx, e);
+    }
+    enc_attn_desc d = *desc;
+    d.ws = ctx->scratch;
+    d.ws_bytes = ENC_STATIC_SCRATCH_BYTES;
+    // the needed size first, so that the error names it rather than the
+    // workspace check's generic message
+    if (items || !nitems) {
+        const size_t need = attn_ws_bytes(&d, items, nitems);
+        if (need > ENC_STATIC_SCRATCH_BYTES) {
+            e.set(ENC_EUNSUPPORTED,
+                  "attention_items_static: the key splits of these items need %zu bytes of scratch, "
+                  "the static scratch holds %zu (use attention_items with a workspace)",
+                  need, (size_t)ENC_STATIC_SCRATCH_BYTES);
+            return finish(ctx, e);
+        }
+    }
+    if (check_attn(e, &d, items, nitems) == ENC_OK)
+        launch_status(e, run_attention(&d, items, nitems, (hipStream_t)stream), "attention_items_static");
     return finish(ctx, e);
 }
 
