@@ -230,6 +230,21 @@ def test_dit_1056_full_width_layer_vs_oracle():
     assert err <= TOL_I8F16
 
 
+@pytest.mark.parametrize("name", ["zimage_dit_1056"])
+def test_dit_full_stack_vs_stored_oracle(name):
+    """The DiT stack whole (every layer, every row of the batch), its output rows
+    sampled (each range's first, middle and last rows, tile edges, seeded draws)
+    against the oracle's forward of the same batch with its f16 sites, stored by
+    tests/golden/full_depth.py under a key of its inputs."""
+    w = wl.make(name, lazy_int8=True)
+    rows, ref = full_depth.load(name, w)
+    got = host(run(w))
+    assert np.isfinite(got).all()
+    err = row_rel_err(got[rows], ref)
+    say(f"DiT {name} full stack ({w.cfg['layers']} layers, {w.rows} rows): {len(rows)} rows, error {err:.2e}")
+    assert err <= TOL_I8F16
+
+
 def test_dit_modulated_full_width_layer_vs_oracle():
     """The modulated q8_2f DiT block with the Turbo guards at full width and rows
     (1056 x 3840), one layer; every output row against the oracle."""
