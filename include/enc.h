@@ -495,8 +495,11 @@ ENC_API enc_status enc_check_model(const enc_model *model, const enc_batch *batc
 /* RoPE positions (host int32 [rows][sections]).  1-D (sections 1): the row's
  * index t within its item, restarting at 0 per item ([EG] `TextGpu::forward`,
  * positions per sequence).  2-D (sections 2): grids[i] = G > 0 marks item i as
- * a G x G image in row-major order followed by captions: t < G*G sits at
- * (column t % G, row t / G); caption j = t - G*G at (G + j, G + j). */
+ * a G x G image in row-major order at the start of its first range: t < G*G
+ * sits at (column t % G, row t / G); rows of the first range past the image
+ * are its padding ([ZI] `prepare`: image rows padded to a multiple of 32 with
+ * the learned pad row) and sit at (0, 0); the rows of the second range are
+ * captions, caption j at (G + j, G + j). */
 ENC_API enc_status enc_positions(uint32_t rows, const enc_item *items, const uint32_t *grids,
                          uint32_t nitems, uint32_t sections, int32_t *pos);
 

@@ -245,6 +245,20 @@ def test_dit_full_stack_vs_stored_oracle(name):
     assert err <= TOL_I8F16
 
 
+def test_dit_padded_pair_full_width_layer_vs_oracle():
+    """The padded CFG pair at full width and rows (2 x (928 + 32) = 1920 rows:
+    30x30 images padded to 928 rows, 20 captions padded to 32), one layer; every
+    output row against the oracle with the same positions."""
+    from positions_ref import dit_positions
+    w = wl.make("zimage_dit_pad_cfg", layers=1)
+    pos = dit_positions(w.rows, w.items, w.grids)
+    got = host(run(w))
+    err = row_rel_err(got, O.forward(w, pos=pos))
+    say(f"padded DiT pair full-width layer: error {err:.2e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL_I8F16
+
+
 def test_dit_modulated_full_width_layer_vs_oracle():
     """The modulated q8_2f DiT block with the Turbo guards at full width and rows
     (1056 x 3840), one layer; every output row against the oracle."""

@@ -138,7 +138,7 @@ def test_packed_images_equal_separate():
 
 
 @pytest.mark.parametrize("name,grid,ncap", [("zimage_dit_cfg_8448", 4, 8), ("zimage_dit_mod_1056", 4, 8),
-                                            ("zimage_dit_cfg_8448", 32, 32)])
+                                            ("zimage_dit_cfg_8448", 32, 32), ("zimage_dit_pad_cfg", 7, 5)])
 def test_cfg_pair_equals_two_singles(name, grid, ncap):
     """The CFG batch-2 program gives each item the bits of its single forward
     (at 32x32 + 32 rows per item the attention takes key splits)."""
@@ -150,6 +150,24 @@ def test_cfg_pair_equals_two_singles(name, grid, ncap):
         single = wl.make(name, cfg_pair=False, **kw)
         alone = run(single, x=w.x[idx])
         assert torch.equal(alone, pair[torch.from_numpy(idx).to(DEV)]), f"item {i}"
+
+
+def test_padded_dit_pair_vs_oracle():
+    """The CFG pair with padded lengths (zimage.rs `prepare`: image and caption
+    ranges padded to 32 rows, the image's with the learned pad row): a 7x7 image
+    (49 rows + 15 pad rows) and 5 captions (+ 27 pad rows) per item, two layers;
+    the oracle takes the same positions (pad rows at (0, 0)) from the rule
+    written out in tests/positions_ref.py."""
+    from positions_ref import dit_positions
+    w = wl.make("zimage_dit_pad_cfg", layers=2, grid=7, ncap=5, overrides=DIT_SMALL)
+    assert w.items == [[(0, 64), (128, 32)], [(64, 64), (160, 32)]]
+    pos = dit_positions(w.rows, w.items, w.grids)
+    assert np.array_equal(B.positions(w.rows, w.items, w.grids, 2), pos)
+    got = host(run(w))
+    err = row_rel_err(got, O.forward(w, pos=pos))
+    say(f"padded DiT pair: rows {w.rows}, error {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL_I8F16
 
 
 def test_amax_per_site_vs_oracle():

@@ -320,3 +320,17 @@ def test_check_model_pool_needs_nonempty_items():
     assert st == B.ENC_EINVAL and "empty" in msg
     m.final_kind = 0  # no pool: an empty sequence is fine
     assert B.check_model(m, b)[0] == B.ENC_OK
+
+
+def test_positions_padded_dit_items():
+    """Padded CFG items ([img0 | img1 | cap0 | cap1], each range padded to 32):
+    image rows on the grid, image pad rows at (0, 0), captions on the diagonal
+    counted from the start of their range; unpadded items keep their tables."""
+    from positions_ref import dit_positions
+    for name, kw in [("zimage_dit_pad_cfg", {}), ("zimage_dit_pad_cfg", dict(grid=5, ncap=3)),
+                     ("zimage_dit_cfg_8448", dict(grid=6, ncap=5)), ("zimage_dit_1056", {})]:
+        w = wl.make(name, layers=1, lazy_int8=True, **kw)
+        got = B.positions(w.rows, w.items, w.grids, 2)
+        assert np.array_equal(got, dit_positions(w.rows, w.items, w.grids)), (name, kw)
+    w = wl.make("zimage_dit_pad_cfg", layers=1, lazy_int8=True)
+    assert w.items == [[(0, 928), (1856, 32)], [(928, 928), (1888, 32)]]

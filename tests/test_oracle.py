@@ -720,6 +720,29 @@ def test_post_ln_stack_matches_torch_encoder(oracle):
     assert np.abs(oracle.forward(w) - out).max() > 1e-3
 
 
+def test_padded_pair_equals_singles_and_pads_attend(oracle):
+    """Padded items (image and caption ranges padded to 32 with pad rows) are
+    ordinary rows of their item: the CFG pair still equals two singles bit for
+    bit, and a pad row is a key the real rows attend to (changing the pad row
+    changes them) while leaving the other item alone."""
+    from positions_ref import dit_positions
+    kw = dict(layers=1, grid=3, ncap=2, overrides=dict(d=128, nq=2, nkv=2, ff=256))
+    w = wl.make("zimage_dit_pad_cfg", **kw)
+    assert w.items == [[(0, 32), (64, 32)], [(32, 32), (96, 32)]]
+    pos = dit_positions(w.rows, w.items, w.grids)
+    pair = oracle.forward(w, pos=pos)
+    for rr in w.items:
+        idx = np.concatenate([np.arange(r0, r0 + n) for r0, n in rr])
+        single = wl.make("zimage_dit_pad_cfg", cfg_pair=False, **kw)
+        spos = dit_positions(single.rows, single.items, single.grids)
+        assert np.array_equal(oracle.forward(single, x=w.x[idx], pos=spos), pair[idx])
+    x2 = w.x.copy()
+    x2[20:32] += 1.0  # item 0's image pad rows
+    moved = oracle.forward(w, x=x2, pos=pos)
+    assert np.abs(moved[:9] - pair[:9]).max() > 1e-6  # item 0's image rows
+    assert np.array_equal(moved[32:64], pair[32:64]) and np.array_equal(moved[96:], pair[96:])
+
+
 def test_nonfinite_input_propagates(oracle):
     w = wl.make("gemma_text_f32", layers=1, lengths=[5, 6])
     w.cfg["final"] = wl.FINAL_NONE

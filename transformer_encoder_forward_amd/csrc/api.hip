@@ -1486,8 +1486,10 @@ enc_status enc_positions(uint32_t rows, const enc_item *items, const uint32_t *g
             } else if (t < G * G) {
                 pos[2 * row] = (int32_t)(t % G);      // column
                 pos[2 * row + 1] = (int32_t)(t / G);  // row
+            } else if (t < it.r[0].n) {
+                pos[2 * row] = pos[2 * row + 1] = 0;  // pad row of the image range
             } else {
-                pos[2 * row] = pos[2 * row + 1] = (int32_t)(G + (t - G * G));
+                pos[2 * row] = pos[2 * row + 1] = (int32_t)(G + (t - it.r[0].n));  // caption
             }
         }
     }

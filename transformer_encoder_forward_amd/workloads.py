@@ -110,6 +110,14 @@ CONFIGS = {
         attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
         grid=32, ncap=32, cfg_pair=False, modulated=True, col_fields=True,
         guards=[0, 1, 0, 0, 6], noise_refiner=2, context_refiner=2),
+    # the CFG pair with the page's padded lengths: a 30x30 image (900 rows) and
+    # 20 caption rows per item, each range padded to a multiple of 32 (928 and
+    # 32 rows) with one learned pad row (image) and one caption pad row
+    "zimage_dit_pad_cfg": dict(
+        num=10, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
+        hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
+        attn_scale=1.0 / math.sqrt(128.0), rope_base=10000.0, x_scale=1.0, biases=False,
+        grid=30, ncap=20, cfg_pair=True, pad_to=32),
     "zimage_dit_cfg_8448": dict(
         num=5, block=BLOCK_SANDWICH, path=PATH_I8F16, mlp=MLP_SWIGLU, d=3840, nq=30, nkv=30,
         hd=128, ff=10240, layers=30, window=0, rope_sections=2, final=FINAL_NONE, eps=1e-6,
@@ -260,6 +268,10 @@ def layout(cfg: dict, lengths=None, grid=None, ncap=None, cfg_pair=None):
         nc = cfg["ncap"] if ncap is None else ncap
         pair = cfg["cfg_pair"] if cfg_pair is None else cfg_pair
         ni = g * g
+        pad = cfg.get("pad_to", 0)
+        if pad:
+            # each range padded to a multiple of `pad` rows
+            ni, nc = -(-ni // pad) * pad, -(-nc // pad) * pad
         if not pair:
             return ni + nc, [[(0, ni), (ni, nc)] if nc else [(0, ni)]], [g]
         items = [[(0, ni), (2 * ni, nc)] if nc else [(0, ni)],
@@ -293,12 +305,20 @@ def make(name: str, layers=None, lengths=None, grid=None, ncap=None, cfg_pair=No
         # image rows are one draw shared by every item (one latent, CFG pair);
         # each item's caption rows are its own draw
         x = np.empty((rows, d), np.float32)
+        g = cfg["grid"] if grid is None else grid
+        nc_real = cfg["ncap"] if ncap is None else ncap
         for i, rr in enumerate(items):
             (r0, ni) = rr[0]
-            x[r0:r0 + ni] = _normal(seed, "x.img", (ni, d), cfg["x_scale"])
+            nimg = min(ni, g * g)
+            x[r0:r0 + nimg] = _normal(seed, "x.img", (nimg, d), cfg["x_scale"])
+            if ni > nimg:  # image padding: the learned pad row
+                x[r0 + nimg:r0 + ni] = _normal(seed, "x.pad", (d,), cfg["x_scale"])
             if len(rr) > 1:
                 (c0, nc) = rr[1]
-                x[c0:c0 + nc] = _normal(seed, f"x.cap{i}", (nc, d), cfg["x_scale"])
+                ncr = min(nc, nc_real)
+                x[c0:c0 + ncr] = _normal(seed, f"x.cap{i}", (ncr, d), cfg["x_scale"])
+                if nc > ncr:  # caption padding: the caption pad row
+                    x[c0 + ncr:c0 + nc] = _normal(seed, "x.cap_pad", (d,), cfg["x_scale"])
     else:
         x = _normal(seed, "x", (rows, d), cfg["x_scale"])
     w = Workload(name=name, cfg=cfg, rows=rows, items=items, grids=grids, x=x, seed=seed)
