@@ -730,6 +730,27 @@ def test_gated_act(kind, f16):
     assert row_rel_err(host(out), act(g) * u) <= (TOL_I8F16 if f16 else TOL_F32)
 
 
+@pytest.mark.parametrize("f16", [False, True])
+def test_swiglu_far_negative_gate(f16):
+    """silu at gates from -92 to -80, where 1 + e^-x passes 2^126 and the
+    reciprocal leaves the normal range: the outputs (below 1e-30 in magnitude)
+    stay within 1e-30 of the oracle's, and the rows' normal values within the
+    path's tolerance."""
+    rows, ff = 8, 512
+    g = np.linspace(-92.0, -80.0, rows * ff).reshape(rows, ff).astype(np.float32)
+    g[:, ::64] = 3.0  # a normal value per 64 so the row errors are relative to it
+    u = np.ones((rows, ff), np.float32)
+    out = torch.empty((rows, ff), dtype=torch.float16 if f16 else torch.float32, device=DEV)
+    B.gated_act(to_dev(g), to_dev(u), out, B.ENC_ACT_SWIGLU, f16=f16)
+    ref = np.vectorize(O.silu)(g.astype(np.float64))
+    if f16:
+        ref = np.vectorize(O.round_f16)(ref)
+    got = host(out)
+    tiny = g < 0
+    assert np.abs(got[tiny] - ref[tiny]).max() <= 1e-30
+    assert row_rel_err(got, ref) <= (TOL_I8F16 if f16 else TOL_F32)
+
+
 def test_mean_pool():
     rng = np.random.default_rng(9)
     rows, d = 300, 512

@@ -45,8 +45,10 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return 0.5f * x * (1.0f + tanh_f32(c * (x + 0.044715f * x * x * x)));
 }
 
-// silu(x) = x / (1 + exp(-x)); the divisor lies in (1, inf], where the
-// hardware reciprocal is within 1 ulp (and 0 at inf, as the division gives)
+// silu(x) = x / (1 + exp(-x)); the divisor lies in (1, inf].  Up to 2^126 the
+// hardware reciprocal is within 1 ulp; beyond (x below about -87.3) the
+// reciprocal is subnormal and may flush to 0, so silu gives -0 where the exact
+// value is under 2^-120 in magnitude (and 0 at inf, as the division gives).
 __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
