@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zimage_dit_cfg_8448")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--layers", type=int, default=None, help="(development) fewer layers")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -144,20 +146,33 @@ def main():
     print(f"[bench] {args.workload}: rows={w.rows} items={len(w.items)} layers={cfg['layers']} "
           f"setup {setup_s:.1f}s", file=sys.stderr, flush=True)
 
-    def step():
+    def step(st=stream):
         if w.stages:
-            M.stages_forward(prog, x, out, ws, ctx=ctx, stream=stream)
+            M.stages_forward(prog, x, out, ws, ctx=ctx, stream=st)
         else:
-            M.encoder_forward(dm, db, x, out, ws, ctx=ctx, stream=stream)
+            M.encoder_forward(dm, db, x, out, ws, ctx=ctx, stream=st)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    timed_step = step
+    if args.graph:
+        # the whole step as one graph, captured on a side stream (the library
+        # enqueues kernels and device-to-device copies only) and replayed on
+        # the timed stream
+        graph, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=cap):
+            step(cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        timed_step = graph.replay
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        step()
+        timed_step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -211,6 +226,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
+        "launch": "hip graph replay" if args.graph else "eager",
         "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
         "measured_mfma_peak": round(measured_peak, 1),
         "pct_of_measured_peak": round(100.0 * tflops / measured_peak, 2),

@@ -195,7 +195,8 @@ def test_gemm_i8f16_integer_exact(n, m, k):
 
 
 # shapes that take the direct-to-LDS kernel (K % 64 == 0): 256 x 256 tiles (>= 256
-# of them) and 64 x 256 tiles (fewer); one K stage, exactly the LDS ring, ring
+# of them), 128 x 256 tiles (the 520- and 513-row launches: more than 512 tiles of
+# 64 x 256) and 64 x 256 tiles; one K stage, exactly the LDS ring, ring
 # wrap-around; ragged rows and columns
 @pytest.mark.parametrize("n,m,k", [(1300, 11000, 64), (1300, 11000, 192), (1283, 11000, 320),
                                    (520, 17000, 64), (513, 17000, 320),
@@ -217,8 +218,9 @@ def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
 
 
 def test_gemm_i8f16_kernel_choice_bit_identical():
-    """Rows computed in a launch of 256 x 256 tiles and in small launches of
-    64 x 256 tiles give the same bits (one K order for every int8 kernel)."""
+    """Rows computed in a launch of 256 x 256 tiles, in an 800-row launch of
+    128 x 256 tiles (two-stage ring) and in small launches of 64 x 256 tiles
+    give the same bits (one K order for every int8 kernel)."""
     rng = np.random.default_rng(77)
     n, m, k = 1300, 11000, 256
     x = rng.normal(0, 1, (n, k)).astype(np.float16)
@@ -226,7 +228,7 @@ def test_gemm_i8f16_kernel_choice_bit_identical():
     rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32))]
     Yall = torch.empty((n, m), dtype=torch.float32, device=DEV)
     B.gemm_items(to_dev(x), Yall, [W], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs)
-    for r0, r1 in ((0, 1), (250, 300), (450, 520), (1100, 1300)):
+    for r0, r1 in ((0, 1), (250, 300), (450, 520), (1100, 1300), (300, 1100)):
         Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
         B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
                      row_scale=rs)

@@ -65,15 +65,22 @@ namespace {
 
 // The direct-to-LDS int8 kernel needs K % 64 == 0.  Plain GEMMs: 256 x 256
 // tiles (8 waves of 128 x 64, one block per CU) when the launch has at least
-// 256 of them; fewer (a 1056-row DiT batch: q|k|v 225 tiles, the output and
-// down projections 75) take 64 x 256 tiles of 8 waves (64 x 32 each, two
-// blocks per CU), measured 6% / 28% / 26% faster there and 15-25% slower at
-// 8448 rows.  Gated: 256 x (128 + 128) with at least 512 tiles of 256 x 128,
-// else 128 x (128 + 128) (6% faster at 1056 rows) with a five-stage ring (the
-// whole LDS; 0.6% faster per forward than three).  Otherwise (K % 64 != 0, or
-// an item too large for the direct loads' 32-bit offsets) the register-staged
-// 128 x 128 kernel.  All sum in the same K order.
-constexpr uint32_t kWideTiles = 256, kWideGated = 512;
+// 256 of them.  Fewer (a 1056-row DiT batch: q|k|v 225 tiles, the output and
+// down projections 75) take the smaller tiles that fill the CUs in one round
+// of two blocks each: 64 x 256 tiles of 8 waves (64 x 32 each) when there are
+// at most 512 of them (the output and down projections: 255; 56% and 48%
+// faster than 256 x 256 there), else 128 x 256 tiles of 8 waves (64 x 64
+// each) with a two-stage ring, so that two blocks fit a CU (q|k|v: 405 tiles,
+// 5% faster than 765 tiles of 64 x 256 and 11% faster than 256 x 256).
+// 32 x 256 and 64 x 128 tiles were measured no faster than 64 x 256 on the
+// output and down projections, and 8 waves of 64 x 128 in the 256 x 256 tile
+// 3% slower than 128 x 64 at 8448 rows.  Gated: 256 x (128 + 128) with at
+// least 512 tiles of 256 x 128, else 128 x (128 + 128) (6% faster at 1056
+// rows) with a five-stage ring (the whole LDS; 0.6% faster per forward than
+// three).  Otherwise (K % 64 != 0, or an item too large for the direct loads'
+// 32-bit offsets) the register-staged 128 x 128 kernel.  All sum in the same K
+// order.
+constexpr uint32_t kWideTiles = 256, kWideGated = 512, kSlots = 512;
 
 }  // namespace
 
@@ -94,8 +101,10 @@ hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
         if (gated)
             return tiles_of(a, 256, 128) >= kWideGated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
                                                        : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
-        return tiles_of(a, 256, 256) >= kWideTiles ? gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s)
-                                                   : gemm::launch_q8d<64, 256, 1, 8, 2, false>(a, s);
+        if (tiles_of(a, 256, 256) >= kWideTiles) return gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
+        if (tiles_of(a, 64, 256) > kSlots && tiles_of(a, 128, 256) <= kSlots)
+            return gemm::launch_q8d<128, 256, 2, 4, 2, false, 2>(a, s);
+        return gemm::launch_q8d<64, 256, 1, 8, 2, false>(a, s);
     }
     if (gated) return gemm::launch_gated<128, 128, 64, 2, true, 2>(a, s);
     return gemm::launch<128, 128, 64, 2, 2, true, 2>(a, s);
