@@ -518,11 +518,19 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 //    (in log2 units), and then to that block's max: p = 2^(s c - m) stays at
 //    most 256 (exact in f16's range), the output is rescaled only on such a
 //    move, and the quotient o / l does not depend on where m sits.
-// Iteration b computes the scores of block b+1 (a dependent MFMA chain,
-// interleaved with the exponentials of block b by scheduling groups), then
-// P V of block b; block b+3 is staged meanwhile.  Keys past the item occur only
-// in the last block and are masked there; rows past the item's queries are
-// computed on clamped data and never stored.
+// Step b: the row max of block b's scores; the V fragments of block b are read
+// while the K fragments of block b+1 (read at the end of step b-1) land; the
+// scores of block b+1 (a dependent MFMA chain) run interleaved with the
+// exponentials of block b by scheduling groups; then the first half of P V.
+// The step's one barrier comes after the wave's last LDS read of stage b, and
+// behind it the freed stage takes block b+4, block b+2's K fragments are read
+// and the second half of P V is issued: those MFMAs and the K reads overlap
+// the next step's row max instead of waiting on a fragment read at its top
+// (2-4% faster than reading K at the top of the step, the same bits).  Keys
+// past the item occur only in the last block and are masked there; rows past
+// the item's queries are computed on clamped data and never stored; the last
+// step's scores of a block past the end come from a stale stage and are never
+// used.
 template <int NW, int MINW>
 __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     constexpr int HD = 128, QT = 32 * NW, NS = 4;
@@ -608,17 +616,18 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
         for (int d = 0; d < HD / 32; d++) vaddr[d] = vrow + (uint32_t)(((4 * d + vc0) ^ vsw) * 16);
     }
     u32x4 kf[HD / 16];
-    auto kread = [&](auto st) {
-        constexpr int off = decltype(st)::value * SBYTES;
-#pragma unroll
-        for (int j = 0; j < HD / 16; j++) kf[j] = ds_read16_at<off>(kaddr[j]);
-    };
     u32x2 vf[HD / 32][2][2];
     auto vread = [&](auto st, int d, auto s2c) {
         constexpr int s2 = decltype(s2c)::value;
         constexpr int off = decltype(st)::value * SBYTES + 16 * s2 * 256;
         vf[d][s2][0] = ds_read8_tr16_at<off>(vaddr[d]);
         vf[d][s2][1] = ds_read8_tr16_at<off + 8 * 256>(vaddr[d]);
+    };
+
+    auto kread_to = [&](auto st, u32x4 (&k)[HD / 16]) {
+        constexpr int off = decltype(st)::value * SBYTES;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) k[j] = ds_read16_at<off>(kaddr[j]);
     };
 
     f32x16 o[HD / 32];
@@ -634,124 +643,135 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     if (nblk > 0) dma(IC<0>{}, 0);
     if (nblk > 1) dma(IC<1>{}, 1);
     if (nblk > 2) dma(IC<2>{}, 2);
-    if (nblk > 2)
-        vm_wait<2 * NDMA>();
-    else if (nblk > 1)
-        vm_wait<NDMA>();
-    else
-        vm_wait<0>();
+    if (nblk > 3) dma(IC<3>{}, 3);
+    {
+        const int fly = max(0, min(NS, nblk) - 2);  // stages 0 and 1 landed
+        if (fly >= 2)
+            vm_wait<2 * NDMA>();
+        else if (fly == 1)
+            vm_wait<NDMA>();
+        else
+            vm_wait<0>();
+    }
     block_barrier();
     f32x16 sA, sB;
 #pragma unroll
     for (int r = 0; r < 16; r++) sA[r] = 0.0f;
     if (wactive && nblk > 0) {
-        kread(IC<0>{});
+        kread_to(IC<0>{}, kf);
         lgkm_wait_n<0>();
 #pragma unroll
         for (int j = 0; j < HD / 16; j++) {
             ready(kf[j]);
             sA = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], sA, 0, 0, 0);
         }
+        if (nblk > 1) kread_to(IC<1>{}, kf);
     }
 
-    // block b (stage st): scores in s_cur; leaves block b+1's scores in s_nx
-    // (on the last block, products of a stale stage that nobody uses)
+    // block b (stage st): scores in s_cur, block b+1's K fragments in flight in
+    // kf; leaves block b+1's scores in s_nx and block b+2's K in flight
     auto step = [&](auto st, int b, f32x16 &s_cur, f32x16 &s_nx) {
         constexpr int S = decltype(st)::value;
-        if (b + 2 < nblk)
+        f16x8 pb[2];
+        if (wactive) {
+            const int kb = c.k_lo + b * KB;
+            if (kb + KB > c.k_hi) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    s_cur[r] = key < c.k_hi ? s_cur[r] : -INFINITY;
+                }
+            }
+            // row max (v_maximum3: no input quieting; a NaN score gives a NaN
+            // max, which reaches the output)
+            float mx = __builtin_elementwise_maximum(s_cur[0], s_cur[1]);
+#pragma unroll
+            for (int r = 2; r < 16; r++) mx = __builtin_elementwise_maximum(mx, s_cur[r]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            // the running max moves (to this block's max) only when it is
+            // passed by more than 8; the output and the row sum follow it then
+            const float mb = mx * cs;
+            const bool up = mb > m_run + 8.0f;
+            if (__any(up)) {
+                const float m_new = up ? mb : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_lane *= alpha;
+#pragma unroll
+                for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+
+            vread(st, 0, IC<0>{});
+            vread(st, 1, IC<0>{});
+            lgkm_wait_n<4>();  // K of block b+1 landed
+#pragma unroll
+            for (int j = 0; j < HD / 16; j++) ready(kf[j]);
+            vread(st, 2, IC<0>{});
+            vread(st, 3, IC<0>{});
+            vread(st, 0, IC<1>{});
+            vread(st, 1, IC<1>{});
+            vread(st, 2, IC<1>{});
+            // scores of block b+1 interleaved with the exponentials of block b
+            // (2^x as the bare v_exp_f32: results below 2^-126 flush to 0)
+#pragma unroll
+            for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < HD / 16; j++)
+                s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
+            float rs = 0.0f;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; s2++)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
+                                      (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
+                    pb[s2][e] = pr[0];
+                    pb[s2][e + 1] = pr[1];
+                    rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+                }
+#pragma unroll
+            for (int j = 0; j < HD / 16; j++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            l_lane += rs;
+            lgkm_wait_n<6>();  // the first half of V landed
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][0][0]);
+                ready(vf[d][0][1]);
+            }
+            vread(st, 3, IC<1>{});
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                const u32x4 vv = {vf[d][0][0][0], vf[d][0][0][1], vf[d][0][1][0], vf[d][0][1][1]};
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[0], o[d], 0, 0, 0);
+            }
+            lgkm_wait_n<0>();
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][1][0]);
+                ready(vf[d][1][1]);
+            }
+        }
+        // every wave: stage b+2 landed (b+3 may fly) and this wave's reads of
+        // stage b done; after the barrier stage b+2 is readable everywhere and
+        // stage b's buffer takes block b+4
+        if (b + 3 < nblk)
             vm_wait<NDMA>();
         else
             vm_wait<0>();
         block_barrier();
-        if (b + 3 < nblk) dma(IC<(S + 3) % NS>{}, b + 3);
+        if (b + 4 < nblk) dma(IC<S>{}, b + 4);
         if (!wactive) return;
-        const int kb = c.k_lo + b * KB;
-        if (kb + KB > c.k_hi) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-                s_cur[r] = key < c.k_hi ? s_cur[r] : -INFINITY;
-            }
-        }
-        // row max (v_maximum3: no input quieting; a NaN score gives a NaN max,
-        // which reaches the output)
-        float mx = __builtin_elementwise_maximum(s_cur[0], s_cur[1]);
-#pragma unroll
-        for (int r = 2; r < 16; r++) mx = __builtin_elementwise_maximum(mx, s_cur[r]);
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // the running max moves (to this block's max) only when it is passed by
-        // more than 8; the output and the row sum follow it then
-        const float mb = mx * cs;
-        const bool up = mb > m_run + 8.0f;
-        if (__any(up)) {
-            const float m_new = up ? mb : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_lane *= alpha;
-#pragma unroll
-            for (int d = 0; d < HD / 32; d++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) o[d][r] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-
-        // reads: block b+1's K (8) and the first half of block b's V group 0 (4)
-        kread(IC<(S + 1) % NS>{});
-        vread(st, 0, IC<0>{});
-        vread(st, 1, IC<0>{});
-        lgkm_wait_n<4>();
-#pragma unroll
-        for (int j = 0; j < HD / 16; j++) ready(kf[j]);
-        vread(st, 2, IC<0>{});
-        vread(st, 3, IC<0>{});
-        // scores of block b+1 (a dependent MFMA chain) interleaved with the
-        // exponentials of block b (2^x as the bare v_exp_f32: results below
-        // 2^-126 flush to 0)
-#pragma unroll
-        for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < HD / 16; j++)
-            s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
-        f16x8 pb[2];
-        float rs = 0.0f;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; s2++)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
-                                  (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
-                pb[s2][e] = pr[0];
-                pb[s2][e + 1] = pr[1];
-                rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-            }
-#pragma unroll
-        for (int j = 0; j < HD / 16; j++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
-        }
-        l_lane += rs;
-        lgkm_wait_n<0>();
-#pragma unroll
-        for (int d = 0; d < HD / 32; d++) {
-            ready(vf[d][0][0]);
-            ready(vf[d][0][1]);
-        }
-#pragma unroll
-        for (int d = 0; d < HD / 32; d++) vread(st, d, IC<1>{});
-#pragma unroll
-        for (int d = 0; d < HD / 32; d++) {
-            const u32x4 vv = {vf[d][0][0][0], vf[d][0][0][1], vf[d][0][1][0], vf[d][0][1][1]};
-            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[0], o[d], 0, 0, 0);
-        }
-        lgkm_wait_n<0>();
-#pragma unroll
-        for (int d = 0; d < HD / 32; d++) {
-            ready(vf[d][1][0]);
-            ready(vf[d][1][1]);
-        }
+        // into the registers block b+1's score MFMAs read (issued long before)
+        if (b + 2 < nblk) kread_to(IC<(S + 2) % NS>{}, kf);
 #pragma unroll
         for (int d = 0; d < HD / 32; d++) {
             const u32x4 vv = {vf[d][1][0][0], vf[d][1][0][1], vf[d][1][1][0], vf[d][1][1][1]};
