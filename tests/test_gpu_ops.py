@@ -29,7 +29,9 @@ def _lib():
 @pytest.mark.parametrize("n,m,k", [(1, 1, 4), (37, 70, 36), (130, 257, 128), (257, 128, 512),
                                    (64, 384, 128), (300, 96, 2048),
                                    (8001, 1000, 96),    # 256 x 128 tiles, ragged rows and columns
-                                   (4100, 4000, 64)])   # 128 x 128 tiles
+                                   (4100, 4000, 64),    # 128 x 128 tiles
+                                   # K split four ways inside the block (m <= 768, K >= 3072)
+                                   (300, 700, 3200), (1024, 768, 3072)])
 def test_gemm_f32_integer_exact(n, m, k):
     say(f"gemm f32 integer n={n} m={m} k={k}")
     rng = np.random.default_rng(n * 31 + m * 7 + k)
@@ -66,7 +68,7 @@ def test_gemm_f32_qkv_items_one_launch():
 
 
 @pytest.mark.parametrize("n,m,k", [(64, 384, 128), (1000, 1536, 512), (333, 512, 2048),
-                                   (1024, 3072, 768),
+                                   (1024, 3072, 768), (1024, 768, 3072), (77, 300, 4096),
                                    # more tiles than resident blocks: blocks loop over tiles
                                    (9001, 1536, 256), (4099, 1536, 512)])
 def test_gemm_f32_random(n, m, k):
@@ -97,6 +99,27 @@ def test_gemm_f32_items_of_different_k_many_tiles():
     assert np.array_equal(host(Y), ref)
 
 
+def test_gemm_f32_split_and_plain_items_one_launch():
+    """A launch mixing an item whose K is split inside the block (768 outputs,
+    K 3072) with plain items gives each item the bits it gets alone."""
+    rng = np.random.default_rng(21)
+    n, k = 700, 3072
+    x = rng.normal(0, 1, (n, k)).astype(np.float32)
+    ws = [rng.normal(0, 0.02, (768, k)).astype(np.float32), rng.normal(0, 0.02, (512, 512)).astype(np.float32)]
+    ld = 768 + 512
+    X, Wd = to_dev(x), [to_dev(w) for w in ws]
+    Y = torch.empty((n, ld), dtype=torch.float32, device=DEV)
+    items = [(n, 768, k, k, ld, 0, 0, 0), (n, 512, 512, k, ld, 1, 0, 768)]
+    B.gemm_items(X, Y, Wd, items)
+    for it in items:
+        alone = torch.empty((n, ld), dtype=torch.float32, device=DEV)
+        B.gemm_items(X, alone, Wd, [it])
+        c0, m = it[7], it[1]
+        assert torch.equal(alone[:, c0:c0 + m], Y[:, c0:c0 + m])
+    ref = np.concatenate([O.linear(x, ws[0]), O.linear(x[:, :512], ws[1])], 1)
+    assert row_rel_err(host(Y), ref) <= TOL_F32
+
+
 def test_gemm_f32_gelu_epilogue():
     rng = np.random.default_rng(5)
     n, m, k = 77, 200, 64
@@ -115,7 +138,8 @@ def test_gemm_f32_gelu_epilogue():
     (8192, 1536, 512, False),    # 256 x 128 direct-loaded tiles vs the 64 x 64 ones
     (8192, 1536, 100, False),    # K % 32 != 0: the register-staged 256 x 128 vs 64 x 64
     (8192, 2048, 512, True),     # gated: 256 x (128 + 128) direct vs 64 x (64 + 64) direct
-    (8192, 2048, 100, True)])    # gated, register-staged tiles
+    (8192, 2048, 100, True),     # gated, register-staged tiles
+    (1100, 768, 3072, False)])   # K split inside the block at every launch size
 def test_gemm_f32_packed_rows_bit_identical(n, m, k, gated):
     """A row's output bits do not depend on how many rows share the launch, so
     not on which tile shape or staging the launch size selects."""

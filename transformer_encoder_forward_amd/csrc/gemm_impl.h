@@ -1117,6 +1117,16 @@ hipError_t launch_q8d(GemmArgs g, hipStream_t s) {
 // == 0.  Rows past n and columns past m load clamped (finite) rows and are
 // never stored.  Gated: each wave column holds 32 gate and 32 up rows of the
 // same 32 output columns (BN / WGN == 64); the epilogue forms act(g) * u.
+//
+// KS > 1 splits K inside the block: the block holds KS groups of WGM x WGN
+// waves, group g sums k in [g K/KS, (g+1) K/KS) through a ring of its own, and
+// at the end groups 1 .. KS-1 pass their sums through the LDS to group 0,
+// which adds them in increasing g and stores.  An output is then
+// ((s_0 + s_1) + ...) + s_{KS-1} with each s_g summed in the order above, the
+// same for every row, so packed and separate batches stay bit-identical as
+// long as KS depends only on the weight shape (see launch_gemm_f32).  One
+// block per tile, plain epilogue only.
+//
 // The launch's argument block read in place (constant memory, scalar loads).
 // A per-tile lookup in a loop through the by-value kernel argument makes the
 // compiler keep a private copy of the whole block in scratch; the kernels
@@ -1179,18 +1189,21 @@ __device__ __forceinline__ const float *gated_up(const GemmArgs &a, uint32_t slo
     return wu;
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
-__global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArgs a) {
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3, int KS = 1>
+__global__ __launch_bounds__(64 * WGM * WGN * KS, MINB) void gemm_f32d_kernel(GemmArgs a) {
     constexpr int NW = WGM * WGN, BK = 32;
     static_assert(NS == 2 || NS == 3, "stages");
+    static_assert(KS == 1 || !GATED, "split K: plain epilogue");
+    constexpr bool kPersistent = MINB == 1 && KS == 1;  // one block per CU looping over tiles
     constexpr int FM = BM / WGM / 32, FN = BN / WGN / 32;
     constexpr int A_BYTES = BM * BK * 4, S_BYTES = A_BYTES + BN * BK * 4;
     constexpr int AL = A_BYTES / 1024 / NW, BL = BN * BK * 4 / 1024 / NW;  // loads per wave per stage
     constexpr int NDMA = AL + BL;
     static_assert(AL >= 1 && BL >= 1 && AL * 1024 * NW == A_BYTES && BL * 1024 * NW == BN * BK * 4, "loads");
     static_assert(FM >= 1 && FN >= 1 && (!GATED || BN / WGN == 64), "tile");
-    static_assert(NS * S_BYTES <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
+    static_assert(KS * NS * S_BYTES <= 160 * 1024, "LDS");
+    static_assert(KS == 1 || (KS - 1) * NW * FM * FN * 4096 <= KS * NS * S_BYTES, "split-K exchange");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KS * NS * S_BYTES];
 
     // persistent (tiles of one block per CU): block b takes tiles
     // xcd_remap(b + i * gridDim.x), i = 0, 1, ... (a multiple of 8 blocks keeps
@@ -1202,16 +1215,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     const GemmArgs &ka = kernarg_gemm();  // the same block as `a`
     TileCtx t;
     locate_tile<BM, BN>(ka, xcd_remap(v, T), t, CPT);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane(tid >> 6) / NW : 0;  // K group
+    const int wave = (tid >> 6) - grp * NW;                                       // wave in the group
     const int li = lane & 31, hf = lane >> 5;
     const int wr = wave / WGN, wc = wave % WGN;
+    uint8_t *const ring = smem + grp * NS * S_BYTES;
 
     const float *asrc[AL];
     const float *bsrc[BL];
     const float *x = reinterpret_cast<const float *>(a.x);
+    int kg0 = 0;  // first k of this group
     auto dma = [&](int s) {
-        uint8_t *buf = smem + (s % NS) * S_BYTES;
-        const int k0 = s * BK;
+        uint8_t *buf = ring + (s % NS) * S_BYTES;
+        const int k0 = kg0 + s * BK;
 #pragma unroll
         for (int q = 0; q < AL; q++)
             __builtin_amdgcn_global_load_lds(ENC_GLOBAL(asrc[q] + k0), ENC_SHARED(buf + (AL * wave + q) * 1024), 16,
@@ -1230,7 +1247,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
 
     // fragment q (k = 16 hf + 4q .. + 3) of X row wr*(BM/WGM) + 32 i + li and
     // of W row wc*(BN/WGN) + 32 j + li: chunk 4 hf + q; 32 rows = 4096 bytes
-    const uint32_t lds0 = lds_offset(smem);
+    const uint32_t lds0 = lds_offset(ring);
     const uint32_t arow = lds0 + (uint32_t)(wr * (BM / WGM) + li) * 128u;
     const uint32_t brow = lds0 + A_BYTES + (uint32_t)(wc * (BN / WGN) + li) * 128u;
     const int sw = (li >> 1) & 7;
@@ -1266,7 +1283,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
 
     f32d_sources<AL, BL, GATED>(x, reinterpret_cast<const float *>(t.w), GATED ? gated_up(ka, t.it.slot) : nullptr,
                                 t, wave, lane, asrc, bsrc);
-    int nst = t.it.k / BK;
+    int nst = t.it.k / BK / KS;
+    kg0 = grp * nst * BK;
     prologue(nst);
     if (NS > 2 && nst > 2)
         vm_wait<2 * NDMA>();
@@ -1312,7 +1330,40 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
             mma(fa1, fb1);
         }
 
-        if constexpr (!GATED) {
+        if constexpr (KS > 1) {
+            // groups 1 .. KS-1 hand their sums to group 0 through the LDS (every
+            // wave is past its last ring read once the barrier is passed);
+            // group 0 adds them in increasing group order
+            block_barrier();
+            float *xch = reinterpret_cast<float *>(smem);
+            auto slot = [&](int g, int i, int j) {  // 16 floats per lane, lane-minor
+                return xch + ((((g - 1) * NW + wave) * FM + i) * FN + j) * 1024 + lane;
+            };
+            if (grp > 0) {
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+#pragma unroll
+                        for (int r = 0; r < 16; r++) slot(grp, i, j)[64 * r] = acc[i][j][r];
+            }
+            block_barrier();
+            if (grp == 0) {
+                for (int g = 1; g < KS; g++)
+#pragma unroll
+                    for (int i = 0; i < FM; i++)
+#pragma unroll
+                        for (int j = 0; j < FN; j++)
+#pragma unroll
+                            for (int r = 0; r < 16; r++) acc[i][j][r] += slot(g, i, j)[64 * r];
+#pragma unroll
+                for (int i = 0; i < FM; i++)
+#pragma unroll
+                    for (int j = 0; j < FN; j++)
+                        store_block<false>(a, t, acc[i][j], t.row0 + wr * (BM / WGM) + i * 32,
+                                           t.col0 + wc * (BN / WGN) + j * 32, lane);
+            }
+        } else if constexpr (!GATED) {
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -1349,7 +1400,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
         // each k-step of the next tile.)
         // (only the one-block-per-CU tiles loop; smaller ones run a block per tile)
         const uint32_t vn = v + gridDim.x;
-        const bool more = MINB == 1 && vn < T;
+        const bool more = kPersistent && vn < T;
         TileCtx tn;
         int nst_n = 0;
         if (more) {
@@ -1369,16 +1420,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_f32d_kernel(GemmArg
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3>
+template <int BM, int BN, int WGM, int WGN, int MINB, bool GATED, int NS = 3, int KS = 1>
 hipError_t launch_f32d(GemmArgs g, hipStream_t s) {
     const uint32_t tiles = plan_tiles(g, BM, GATED ? BN / 2 : BN);
     if (!tiles) return hipSuccess;
     // tiles of one block per CU (MINB 1): one block per CU, each looping over
     // its tiles; smaller tiles: one block per tile, the hardware fills the
     // CUs as blocks end
-    const uint32_t slots = MINB == 1 ? (uint32_t)device_cus() : tiles;
-    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS>), dim3(std::min(tiles, slots)),
-                       dim3(64 * WGM * WGN), 0, s, g);
+    const uint32_t slots = MINB == 1 && KS == 1 ? (uint32_t)device_cus() : tiles;
+    hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, MINB, GATED, NS, KS>), dim3(std::min(tiles, slots)),
+                       dim3(64 * WGM * WGN * KS), 0, s, g);
     return hipGetLastError();
 }
 
