@@ -42,7 +42,20 @@ from transformer_encoder_forward_amd import workloads as wl  # noqa: E402  (draw
 ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
 SYNTH_SRC = os.path.join(ROOT, "transformer_encoder_forward_amd", "synth.py")
 
-WORKLOADS = ("gemma_text_f32", "gemma_text_ple_f32", "zimage_dit_1056", "zimage_dit_cfg_8448")
+WORKLOADS = ("gemma_text_f32", "gemma_text_ple_f32", "zimage_dit_1056", "zimage_dit_cfg_8448",
+             "zimage_dit_pad_cfg")
+
+
+def positions(w):
+    """The rows' positions when the workload needs the padded-item rule stated in
+    tests/positions_ref.py (pad rows at (0, 0)), else None (the oracle's own)."""
+    if not w.cfg.get("pad_to"):
+        return None
+    tests_dir = os.path.dirname(HERE)
+    if tests_dir not in sys.path:
+        sys.path.insert(0, tests_dir)
+    from positions_ref import dit_positions
+    return dit_positions(w.rows, w.items, w.grids)
 
 
 def path_for(name: str) -> str:
@@ -54,10 +67,13 @@ def _file_sha(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def key(w) -> str:
+def key(w, pos=None) -> str:
     """SHA-256 identifying the oracle source, the draw module and every input of
-    workload `w` (built with or without its int8 weights in host memory)."""
+    workload `w` (built with or without its int8 weights in host memory), and
+    the positions when they are given explicitly."""
     h = hashlib.sha256()
+    if pos is not None:
+        h.update(np.ascontiguousarray(pos, np.int32).tobytes())
     h.update(_file_sha(ORACLE_SRC).encode())
     h.update(_file_sha(SYNTH_SRC).encode())
     h.update(json.dumps(w.cfg, sort_keys=True).encode())
@@ -109,7 +125,7 @@ def load(name: str, w):
     if not os.path.exists(p):
         raise FileNotFoundError(f"{p} is missing: run python tests/golden/full_depth.py {name}")
     z = np.load(p, allow_pickle=False)
-    k = key(w)
+    k = key(w, positions(w))
     if str(z["key"]) != k:
         raise ValueError(f"{p} is stale (inputs or oracle changed): rerun "
                          f"python tests/golden/full_depth.py {name}")
@@ -121,12 +137,13 @@ def write(name: str) -> None:
 
     O.build(force=False)
     w = wl.make(name)
-    k = key(w)
+    pos = positions(w)
+    k = key(w, pos)
     rows = sample_rows(w)
     print(f"{name}: {w.rows} rows, {w.cfg['layers']} layers, {len(rows)} stored rows, "
           f"oracle threads {O.threads()}", flush=True)
     t0 = time.time()
-    out = O.forward(w)
+    out = O.forward(w, pos=pos)
     dt = time.time() - t0
     print(f"{name}: oracle forward {dt:.1f} s", flush=True)
     np.savez_compressed(path_for(name), key=np.array(k), rows=rows, out=out[rows],
