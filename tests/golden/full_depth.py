@@ -43,7 +43,7 @@ ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
 SYNTH_SRC = os.path.join(ROOT, "transformer_encoder_forward_amd", "synth.py")
 
 WORKLOADS = ("gemma_text_f32", "gemma_text_ple_f32", "zimage_dit_1056", "zimage_dit_cfg_8448",
-             "zimage_dit_pad_cfg")
+             "zimage_dit_pad_cfg", "zimage_dit_mod_1056")
 
 
 def positions(w):
