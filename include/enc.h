@@ -24,6 +24,11 @@
  *  - One enc_ctx per host thread, or callers serialise their calls on a ctx.
  *  - Item arrays are host memory copied into the kernel arguments at enqueue;
  *    the caller may free them as soon as the call returns.
+ *  - A call enqueues kernels and device-to-device copies only (no memset, no
+ *    allocation, no host synchronisation), so it may be recorded into a HIP
+ *    graph by stream capture and replayed; a replay reads the item tables as
+ *    they were at capture.  (enc_prof_enable's events are the exception: keep
+ *    profiling off while capturing.)
  */
 #ifndef ENC_H
 #define ENC_H
