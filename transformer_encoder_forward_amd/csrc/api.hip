@@ -392,6 +392,7 @@ hipError_t run_attention(const enc_attn_desc *d, const enc_item *items, uint32_t
         a.part_ml = part_ml;
         a.ocol = d->out_col;
         a.oscale = d->out_scale == 0.0f ? 1.0f : d->out_scale;
+        a.rows = d->rows;
         CombineArgs cb;
         memset(&cb, 0, sizeof cb);
         cb.part_o = part_o;

@@ -508,7 +508,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 //    arithmetic per block), and the scores of consecutive blocks alternate
 //    between two register sets instead of being copied;
 //  - a block that lies inside one row range of the item is staged from a
-//    wave-uniform row base plus per-lane byte offsets fixed at the start;
+//    wave-uniform row base plus per-lane byte offsets fixed at the start; when
+//    every byte offset of the panel fits 31 bits (BUF) these are raw buffer
+//    loads with the row base as their scalar offset, so a block's staging
+//    costs no address arithmetic in vector registers (2-5% faster on the DiT
+//    item tables than 64-bit per-lane addresses, the same bits);
 //  - the row sum adds the f16 probabilities that the P V product consumes, two
 //    at a time (v_dot2_f32_f16 with ones, f32 accumulation), so numerator and
 //    denominator see the same rounded p;
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 // the item's queries are computed on clamped data and never stored; the last
 // step's scores of a block past the end come from a stale stage and are never
 // used.
-template <int NW, int MINW>
+template <int NW, int MINW, bool BUF>
 __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     constexpr int HD = 128, QT = 32 * NW, NS = 4;
     constexpr int TBYTES = KB * HD * 2;   // one K or V block: 8 KB
@@ -577,16 +581,26 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
         vso[q] = 2 * (r + a.v_col + 8 * (pl ^ (4 * (ti & 3))));
     }
     const int na = (int)c.it.na;
+    const __amdgpu_buffer_rsrc_t pres = raw_buffer(P);
     auto dma = [&](auto st, int b) {
         uint8_t *buf = smem + decltype(st)::value * SBYTES;
         const int kb = c.k_lo + b * KB;
         if (kb + KB <= c.k_hi && (kb + KB <= na || kb >= na)) {
             const int r0 = kb < na ? (int)c.it.r0a + kb : (int)c.it.r0b + (kb - na);
-            const char *base = reinterpret_cast<const char *>(P + (size_t)r0 * a.ld);
+            if constexpr (BUF) {
+                const uint32_t soff = (uint32_t)r0 * a.ld * 2u;
 #pragma unroll
-            for (int q = 0; q < NI; q++) {
-                dma16(base + kso[q], buf + (wave * NI + q) * 1024);
-                dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+                for (int q = 0; q < NI; q++) {
+                    buffer_dma16(pres, buf + (wave * NI + q) * 1024, kso[q], soff);
+                    buffer_dma16(pres, buf + TBYTES + (wave * NI + q) * 1024, vso[q], soff);
+                }
+            } else {
+                const char *base = reinterpret_cast<const char *>(P + (size_t)r0 * a.ld);
+#pragma unroll
+                for (int q = 0; q < NI; q++) {
+                    dma16(base + kso[q], buf + (wave * NI + q) * 1024);
+                    dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+                }
             }
         } else {
             // the block crosses into the second row range or past the item:
@@ -828,7 +842,10 @@ template <int NW, int MINW>
 hipError_t launch_f16s(AttnArgs a, hipStream_t s) {
     const uint32_t tiles = plan_tiles(a, 32 * NW);
     if (!tiles) return hipSuccess;
-    hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    if ((uint64_t)a.rows * a.ld * 2u <= 0x7fffffffu)
+        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, true>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    else
+        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, false>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ struct AttnArgs {
     float *part_ml;  // [records][2] running max (base 2) and sum
     const float *ocol;   // output channel multiplier [nq*hd] (nullable)
     float oscale;        // output scale
+    uint32_t rows;       // rows of the q/k/v panel
     AttnItemK items[kMaxAttnItems];
 };
 
