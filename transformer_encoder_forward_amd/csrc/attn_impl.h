@@ -501,9 +501,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 
 // The attention without a window at hd 128, software-pipelined within each
 // wave, with K/V staged as in attn_f16d_kernel (direct global -> LDS loads, a
-// ring of four stages, the same LDS swizzles) and the per-block overhead cut
+// ring of four or six stages, the same LDS swizzles) and the per-block overhead cut
 // down to the softmax itself:
-//  - the loop is unrolled over the four LDS stages, so every fragment read is a
+//  - the loop is unrolled over the LDS stages, so every fragment read is a
 //    loop-invariant per-lane address plus an immediate offset (no address
 //    arithmetic per block), and the scores of consecutive blocks alternate
 //    between two register sets instead of being copied;
@@ -530,20 +530,27 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 // behind it the freed stage takes block b+4, block b+2's K fragments are read
 // and the second half of P V is issued: those MFMAs and the K reads overlap
 // the next step's row max instead of waiting on a fragment read at its top
-// (2-4% faster than reading K at the top of the step, the same bits).  Keys
+// (2-4% faster than reading K at the top of the step, the same bits).  With
+// PAIR (8-wave blocks, one per CU) the ring has six stages and the barrier
+// comes after odd blocks only: blocks b+1 .. b+3 have landed by then and the
+// stages of blocks b-2 and b-1 take blocks b+4 and b+5, so each load still
+// has two steps to land and the block synchronises half as often (1% on the
+// 8448-row DiT table and the long-sequence steady state, the same bits).  The
+// LDS holds the stages' K blocks, then their V blocks.  Keys
 // past the item occur only in the last block and are masked there; rows past
 // the item's queries are computed on clamped data and never stored; the last
 // step's scores of a block past the end come from a stale stage and are never
 // used.
-template <int NW, int MINW, bool BUF>
+template <int NW, int MINW, bool BUF, bool PAIR>
 __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
-    constexpr int HD = 128, QT = 32 * NW, NS = 4;
+    constexpr int HD = 128, QT = 32 * NW, NS = PAIR ? 6 : 4;
     constexpr int TBYTES = KB * HD * 2;   // one K or V block: 8 KB
     constexpr int SBYTES = 2 * TBYTES;    // a stage: K then V
+    constexpr int VREG = NS * TBYTES;     // K blocks of the stages, then their V blocks
     constexpr int NI = TBYTES / 1024 / NW;
     constexpr int NDMA = 2 * NI;
     static_assert(TBYTES / 1024 % NW == 0, "waves");
-    static_assert(NS * SBYTES <= 65536, "immediate LDS offsets");
+    static_assert(VREG <= 65536, "immediate LDS offsets");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * SBYTES];
 
     const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
@@ -583,7 +590,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     const int na = (int)c.it.na;
     const __amdgpu_buffer_rsrc_t pres = raw_buffer(P);
     auto dma = [&](auto st, int b) {
-        uint8_t *buf = smem + decltype(st)::value * SBYTES;
+        uint8_t *buf = smem + decltype(st)::value * TBYTES;
         const int kb = c.k_lo + b * KB;
         if (kb + KB <= c.k_hi && (kb + KB <= na || kb >= na)) {
             const int r0 = kb < na ? (int)c.it.r0a + kb : (int)c.it.r0b + (kb - na);
@@ -592,14 +599,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
 #pragma unroll
                 for (int q = 0; q < NI; q++) {
                     buffer_dma16(pres, buf + (wave * NI + q) * 1024, kso[q], soff);
-                    buffer_dma16(pres, buf + TBYTES + (wave * NI + q) * 1024, vso[q], soff);
+                    buffer_dma16(pres, buf + VREG + (wave * NI + q) * 1024, vso[q], soff);
                 }
             } else {
                 const char *base = reinterpret_cast<const char *>(P + (size_t)r0 * a.ld);
 #pragma unroll
                 for (int q = 0; q < NI; q++) {
                     dma16(base + kso[q], buf + (wave * NI + q) * 1024);
-                    dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+                    dma16(base + vso[q], buf + VREG + (wave * NI + q) * 1024);
                 }
             }
         } else {
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
                 const int t = min(kb + ti, c.k_hi - 1);
                 const char *base = reinterpret_cast<const char *>(P + ((ptrdiff_t)row_of(c.it, t) - ti) * a.ld);
                 dma16(base + kso[q], buf + (wave * NI + q) * 1024);
-                dma16(base + vso[q], buf + TBYTES + (wave * NI + q) * 1024);
+                dma16(base + vso[q], buf + VREG + (wave * NI + q) * 1024);
             }
         }
     };
@@ -624,7 +631,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     for (int j = 0; j < HD / 16; j++) kaddr[j] = lds0 + (uint32_t)li * 256u + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16);
     {
         const int g = lane >> 4, src = lane & 15;
-        const uint32_t vrow = lds0 + TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
+        const uint32_t vrow = lds0 + VREG + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
         const int vc0 = 2 * (g & 1) + ((src & 3) >> 1), vsw = 4 * (src >> 2);
 #pragma unroll
         for (int d = 0; d < HD / 32; d++) vaddr[d] = vrow + (uint32_t)(((4 * d + vc0) ^ vsw) * 16);
@@ -633,13 +640,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     u32x2 vf[HD / 32][2][2];
     auto vread = [&](auto st, int d, auto s2c) {
         constexpr int s2 = decltype(s2c)::value;
-        constexpr int off = decltype(st)::value * SBYTES + 16 * s2 * 256;
+        constexpr int off = decltype(st)::value * TBYTES + 16 * s2 * 256;
         vf[d][s2][0] = ds_read8_tr16_at<off>(vaddr[d]);
         vf[d][s2][1] = ds_read8_tr16_at<off + 8 * 256>(vaddr[d]);
     };
 
     auto kread_to = [&](auto st, u32x4 (&k)[HD / 16]) {
-        constexpr int off = decltype(st)::value * SBYTES;
+        constexpr int off = decltype(st)::value * TBYTES;
 #pragma unroll
         for (int j = 0; j < HD / 16; j++) k[j] = ds_read16_at<off>(kaddr[j]);
     };
@@ -658,8 +665,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     if (nblk > 1) dma(IC<1>{}, 1);
     if (nblk > 2) dma(IC<2>{}, 2);
     if (nblk > 3) dma(IC<3>{}, 3);
+    if constexpr (PAIR) {
+        if (nblk > 4) dma(IC<4>{}, 4);
+    }
     {
-        const int fly = max(0, min(NS, nblk) - 2);  // stages 0 and 1 landed
+        // landed before the first barrier: blocks 0 and 1, and with PAIR
+        // block 2 too (no barrier follows step 0)
+        const int fly = PAIR ? max(0, min(5, nblk) - 3) : max(0, min(NS, nblk) - 2);
         if (fly >= 2)
             vm_wait<2 * NDMA>();
         else if (fly == 1)
@@ -777,12 +789,24 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
         // every wave: stage b+2 landed (b+3 may fly) and this wave's reads of
         // stage b done; after the barrier stage b+2 is readable everywhere and
         // stage b's buffer takes block b+4
-        if (b + 3 < nblk)
-            vm_wait<NDMA>();
-        else
-            vm_wait<0>();
-        block_barrier();
-        if (b + 4 < nblk) dma(IC<S>{}, b + 4);
+        if constexpr (PAIR) {
+            // one barrier per two blocks, after odd blocks: blocks b+1 .. b+3
+            // landed (everything issued so far) and every wave done with the
+            // stages of blocks b-2 and b-1, which take blocks b+4 and b+5
+            if constexpr (S & 1) {
+                vm_wait<0>();
+                block_barrier();
+                if (b + 4 < nblk) dma(IC<(S + 4) % NS>{}, b + 4);
+                if (b + 5 < nblk) dma(IC<(S + 5) % NS>{}, b + 5);
+            }
+        } else {
+            if (b + 3 < nblk)
+                vm_wait<NDMA>();
+            else
+                vm_wait<0>();
+            block_barrier();
+            if (b + 4 < nblk) dma(IC<S>{}, b + 4);
+        }
         if (!wactive) return;
         // into the registers block b+1's score MFMAs read (issued long before)
         if (b + 2 < nblk) kread_to(IC<(S + 2) % NS>{}, kf);
@@ -800,6 +824,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
         step(IC<2>{}, b + 2, sA, sB);
         if (b + 3 >= nblk) break;
         step(IC<3>{}, b + 3, sB, sA);
+        if constexpr (PAIR) {
+            if (b + 4 >= nblk) break;
+            step(IC<4>{}, b + 4, sA, sB);
+            if (b + 5 >= nblk) break;
+            step(IC<5>{}, b + 5, sB, sA);
+        }
     }
     const float l_run = l_lane + __shfl_xor(l_lane, 32, 64);
     if (qvalid) {
@@ -842,10 +872,11 @@ template <int NW, int MINW>
 hipError_t launch_f16s(AttnArgs a, hipStream_t s) {
     const uint32_t tiles = plan_tiles(a, 32 * NW);
     if (!tiles) return hipSuccess;
+    constexpr bool PAIR = NW == 8;
     if ((uint64_t)a.rows * a.ld * 2u <= 0x7fffffffu)
-        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, true>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, true, PAIR>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     else
-        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, false>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+        hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, false, PAIR>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
