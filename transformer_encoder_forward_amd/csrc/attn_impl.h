@@ -522,10 +522,13 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16d_kernel(AttnArgs a) {
 //    (in log2 units), and then to that block's max: p = 2^(s c - m) stays at
 //    most 256 (exact in f16's range), the output is rescaled only on such a
 //    move, and the quotient o / l does not depend on where m sits.
-// Step b: the row max of block b's scores; the V fragments of block b are read
-// while the K fragments of block b+1 (read at the end of step b-1) land; the
-// scores of block b+1 (a dependent MFMA chain) run interleaved with the
-// exponentials of block b by scheduling groups; then the first half of P V.
+// Step b: the row max of block b's scores; the first half of block b's V
+// fragments is read while the K fragments of block b+1 (read at the end of
+// step b-1) land; the scores of block b+1 (a dependent MFMA chain) run
+// interleaved with the exponentials of block b, each MFMA waiting only for its
+// own K fragment (4% on the 1056-row DiT table, where one wave per SIMD leaves
+// the read latency exposed); then the second half of V is read and the first
+// half of P V issued.
 // The step's one barrier comes after the wave's last LDS read of stage b, and
 // behind it the freed stage takes block b+4, block b+2's K fragments are read
 // and the second half of P V is issued: those MFMAs and the K reads overlap
@@ -733,47 +736,49 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
             }
             const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
+            // the first half of block b's V fragments; then the scores of
+            // block b+1 fragment by fragment as its K reads land (DS reads
+            // complete in order: K fragment j has landed once at most 15 - j
+            // reads are in flight), each MFMA behind a pair of block b's
+            // exponentials, which need no fragment
             vread(st, 0, IC<0>{});
             vread(st, 1, IC<0>{});
-            lgkm_wait_n<4>();  // K of block b+1 landed
-#pragma unroll
-            for (int j = 0; j < HD / 16; j++) ready(kf[j]);
             vread(st, 2, IC<0>{});
             vread(st, 3, IC<0>{});
+#pragma unroll
+            for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
+            float rs = 0.0f;
+            auto group = [&](auto jc) {
+                constexpr int j = decltype(jc)::value, s2 = j / 4, e = 2 * (j % 4);
+                const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
+                                  (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
+                pb[s2][e] = pr[0];
+                pb[s2][e + 1] = pr[1];
+                rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+                __builtin_amdgcn_sched_barrier(0);
+                lgkm_wait_n<15 - j>();
+                ready(kf[j]);
+                s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
+            };
+            group(IC<0>{});
+            group(IC<1>{});
+            group(IC<2>{});
+            group(IC<3>{});
+            group(IC<4>{});
+            group(IC<5>{});
+            group(IC<6>{});
+            group(IC<7>{});
+            l_lane += rs;
             vread(st, 0, IC<1>{});
             vread(st, 1, IC<1>{});
             vread(st, 2, IC<1>{});
-            // scores of block b+1 interleaved with the exponentials of block b
-            // (2^x as the bare v_exp_f32: results below 2^-126 flush to 0)
-#pragma unroll
-            for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < HD / 16; j++)
-                s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
-            float rs = 0.0f;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; s2++)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
-                                      (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
-                    pb[s2][e] = pr[0];
-                    pb[s2][e + 1] = pr[1];
-                    rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
-                }
-#pragma unroll
-            for (int j = 0; j < HD / 16; j++) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
-            l_lane += rs;
-            lgkm_wait_n<6>();  // the first half of V landed
+            vread(st, 3, IC<1>{});
+            lgkm_wait_n<8>();  // the first half of V landed
 #pragma unroll
             for (int d = 0; d < HD / 32; d++) {
                 ready(vf[d][0][0]);
                 ready(vf[d][0][1]);
             }
-            vread(st, 3, IC<1>{});
 #pragma unroll
             for (int d = 0; d < HD / 32; d++) {
                 const u32x4 vv = {vf[d][0][0][0], vf[d][0][0][1], vf[d][0][1][0], vf[d][0][1][1]};
