@@ -259,6 +259,29 @@ def test_gemm_i8f16_kernel_choice_bit_identical():
         assert torch.equal(Y, Yall[r0:r1])
 
 
+def test_gemm_i8f16_beyond_31_bit_offsets_bit_identical():
+    """An item whose X spans more than 2^31 bytes (300 000 rows of K 3840) takes
+    the register-staged kernel (the direct loads address by 32-bit offsets);
+    its first and last rows equal the same rows computed alone by the
+    direct-loaded kernel, bit for bit."""
+    n, m, k = 300_000, 128, 3840
+    assert (n - 1) * k * 2 >= 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn((n, k), generator=g, device=DEV).to(torch.float16)
+    rng = np.random.default_rng(78)
+    W = to_dev(rng.integers(-127, 128, (m, k)).astype(np.int8))
+    rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32))]
+    Y = torch.empty((n, m), dtype=torch.float32, device=DEV)
+    B.gemm_items(x, Y, [W], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs)
+    for r0, r1 in ((0, 64), (n - 100, n)):
+        Ys = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
+        B.gemm_items(x[r0:r1].contiguous(), Ys, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
+                     row_scale=rs)
+        assert torch.equal(Ys, Y[r0:r1]), (r0, r1)
+    del x, Y
+    torch.cuda.empty_cache()
+
+
 def test_gemm_i8f16_f16_output_and_items():
     rng = np.random.default_rng(12)
     n, d, f = 96, 256, 384
@@ -375,6 +398,65 @@ def test_attention_f16_wide_launch_two_range_sampled():
     err = row_rel_err(host(out)[sel], ref)
     say(f"  {len(sel)} sampled queries, err {err:.2e}")
     assert err <= TOL_I8F16
+
+
+def test_attention_f16_eight_wave_blocks_short_items():
+    """Items of 1 to 10 key blocks (every count of blocks modulo the six-stage
+    ring of the 8-wave f16 kernel, ragged last blocks) in a launch wide enough
+    for 256-query blocks (nq 32, GQA 4:1): every row against the oracle, and
+    three items alone (a narrower launch, 128-query blocks) give the packed
+    rows' bits."""
+    lens = [1, 31, 32, 33, 64, 65, 96, 97, 128, 160, 161, 192, 193, 224, 255, 256, 257, 300]
+    items, r = [], 0
+    for n in lens:
+        items.append([(r, n)])
+        r += n
+    rows, nq, nkv, hd = r, 32, 8, 128
+    rng = np.random.default_rng(21)
+    p = _panel(rng, rows, nq, nkv, hd, f16=True, qscale=0.5)
+    P = to_dev(p)
+    out = torch.zeros((rows, nq * hd), dtype=torch.float16, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(P, out, items, nq, nkv, hd, scale, 0, path=B.ENC_I8F16)
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, scale, 0)  # f64; the output's f16 rounding is in the bar
+    err = row_rel_err(host(out), ref)
+    say(f"  {len(items)} items, err {err:.2e}")
+    assert err <= TOL_I8F16
+    for i in (0, 9, 17):
+        (r0, n), = items[i]
+        o1 = torch.zeros((n, nq * hd), dtype=torch.float16, device=DEV)
+        B.attention_items(to_dev(p[r0:r0 + n]), o1, [[(0, n)]], nq, nkv, hd, scale, 0, path=B.ENC_I8F16)
+        assert torch.equal(o1, out[r0:r0 + n]), f"item {i} ({n} rows)"
+
+
+@pytest.mark.parametrize("nq", [4, 128])
+def test_attention_f16_panel_beyond_31_bit_offsets(nq):
+    """Items at the end of a q/k/v panel of more than 2^31 bytes are staged by
+    64-bit per-lane addresses instead of raw buffer loads (nq 4: 128-query
+    blocks; nq 128: 256-query blocks with the six-stage ring); their rows equal
+    the same items in a small panel, bit for bit."""
+    hd = 128
+    ld = 3 * nq * hd
+    rows = (2 ** 31) // (ld * 2) + 1200
+    lens = [300, 257, 33, 256]
+    r0 = rows - sum(lens)
+    items, r = [], r0
+    for n in lens:
+        items.append([(r, n)])
+        r += n
+    g = torch.Generator(device=DEV).manual_seed(9)
+    P = (torch.randn((rows, ld), generator=g, device=DEV) * 0.5).to(torch.float16)
+    out = torch.zeros((rows, nq * hd), dtype=torch.float16, device=DEV)
+    B.attention_items(P, out, items, nq, nq, hd, hd ** -0.5, 0, path=B.ENC_I8F16)
+    small = P[r0:].contiguous()
+    o1 = torch.zeros((rows - r0, nq * hd), dtype=torch.float16, device=DEV)
+    B.attention_items(small, o1, [[(a - r0, n)] for (a, n), in items], nq, nq, hd, hd ** -0.5, 0,
+                      path=B.ENC_I8F16)
+    assert torch.equal(o1, out[r0:])
+    assert torch.isfinite(o1.float()).all()
+    del P, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("path", [B.ENC_F32, B.ENC_I8F16])
