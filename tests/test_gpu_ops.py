@@ -282,6 +282,25 @@ def test_gemm_i8f16_beyond_31_bit_offsets_bit_identical():
     torch.cuda.empty_cache()
 
 
+def test_gemm_i8f16_gated_kernel_choice_bit_identical():
+    """Gated int8 rows computed in a launch of 256 x (128 + 128) tiles (1300
+    rows), of 192 x (128 + 128) tiles (1000 rows, a ragged last tile) and of
+    128 x (128 + 128) tiles (200 rows and fewer) give the same bits."""
+    rng = np.random.default_rng(79)
+    n, ff, d = 1300, 11000, 256
+    x = rng.normal(0, 1, (n, d)).astype(np.float16)
+    W = [to_dev(rng.integers(-127, 128, (ff, d)).astype(np.int8)) for _ in range(2)]
+    rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, ff))).astype(np.float32)) for _ in range(2)]
+    flags = B.ENC_EPI_GATE_SILU | B.ENC_Y_F16
+    Yall = torch.empty((n, ff), dtype=torch.float16, device=DEV)
+    B.gemm_items(to_dev(x), Yall, W, [(n, ff, d, d, ff, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs, flags=flags)
+    for r0, r1 in ((0, 1000), (300, 500), (1299, 1300), (100, 490)):
+        Y = torch.empty((r1 - r0, ff), dtype=torch.float16, device=DEV)
+        B.gemm_items(to_dev(x[r0:r1]), Y, W, [(r1 - r0, ff, d, d, ff, 0, 0, 0)], path=B.ENC_I8F16,
+                     row_scale=rs, flags=flags)
+        assert torch.equal(Y, Yall[r0:r1]), (r0, r1)
+
+
 def test_gemm_i8f16_f16_output_and_items():
     rng = np.random.default_rng(12)
     n, d, f = 96, 256, 384

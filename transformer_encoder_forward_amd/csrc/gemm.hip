@@ -105,9 +105,12 @@ namespace {
 // 32 x 256 and 64 x 128 tiles were measured no faster than 64 x 256 on the
 // output and down projections, and 8 waves of 64 x 128 in the 256 x 256 tile
 // 3% slower than 128 x 64 at 8448 rows.  Gated: 256 x (128 + 128) with at
-// least 512 tiles of 256 x 128, else 128 x (128 + 128) (6% faster at 1056
-// rows) with a five-stage ring (the whole LDS; 0.6% faster per forward than
-// three).  Otherwise (K % 64 != 0, or an item too large for the direct loads'
+// least 512 tiles of 256 x 128; else, for items of more than 384 rows,
+// 192 x (128 + 128) with a four-stage ring (the whole LDS): at 1056 rows its
+// 480 tiles take two rounds of the CUs where 720 tiles of 128 rows take
+// three, and its waves of 96 rows widen each W fragment for 96 rows instead of
+// 64 (10% faster than 128 x (128 + 128), which was 6% faster than
+// 256 x (128 + 128)); else 128 x (128 + 128) with a five-stage ring.  Otherwise (K % 64 != 0, or an item too large for the direct loads'
 // 32-bit offsets) the register-staged 128 x 128 kernel.  All sum in the same K
 // order.
 constexpr uint32_t kWideTiles = 256, kWideGated = 512, kSlots = 512;
@@ -128,9 +131,13 @@ static bool offsets32(const GemmArgs &a) {
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
     if (kmul(a, 64) && offsets32(a)) {
-        if (gated)
-            return tiles_of(a, 256, 128) >= kWideGated ? gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s)
-                                                       : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
+        if (gated) {
+            if (tiles_of(a, 256, 128) >= kWideGated) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
+            uint32_t maxn = 0;
+            for (uint32_t i = 0; i < a.nitems; i++) maxn = std::max(maxn, a.items[i].n);
+            return maxn > 384 ? gemm::launch_q8d<192, 256, 2, 4, 1, true, 4>(a, s)
+                              : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
+        }
         if (tiles_of(a, 256, 256) >= kWideTiles) return gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
         if (tiles_of(a, 64, 256) > kSlots && tiles_of(a, 128, 256) <= kSlots)
             return gemm::launch_q8d<128, 256, 2, 4, 2, false, 2>(a, s);
