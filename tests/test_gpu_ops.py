@@ -242,17 +242,18 @@ def test_gemm_i8f16_wide_tiles_integer_exact(n, m, k):
 
 
 def test_gemm_i8f16_kernel_choice_bit_identical():
-    """Rows computed in a launch of 256 x 256 tiles, in an 800-row launch of
-    128 x 256 tiles (two-stage ring) and in small launches of 64 x 256 tiles
+    """Rows computed in a launch of 256 x 256 tiles (1600 rows), a 1300-row
+    launch of 128 x 256 tiles, an 800-row launch of 96 x 256 tiles (both
+    two-stage rings, two blocks per CU) and small launches of 64 x 256 tiles
     give the same bits (one K order for every int8 kernel)."""
     rng = np.random.default_rng(77)
-    n, m, k = 1300, 11000, 256
+    n, m, k = 1600, 11000, 256
     x = rng.normal(0, 1, (n, k)).astype(np.float16)
     W = to_dev(rng.integers(-127, 128, (m, k)).astype(np.int8))
     rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, m))).astype(np.float32))]
     Yall = torch.empty((n, m), dtype=torch.float32, device=DEV)
     B.gemm_items(to_dev(x), Yall, [W], [(n, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs)
-    for r0, r1 in ((0, 1), (250, 300), (450, 520), (1100, 1300), (300, 1100)):
+    for r0, r1 in ((0, 1), (250, 300), (450, 520), (1100, 1600), (100, 1400), (300, 1100)):
         Y = torch.empty((r1 - r0, m), dtype=torch.float32, device=DEV)
         B.gemm_items(to_dev(x[r0:r1]), Y, [W], [(r1 - r0, m, k, k, m, 0, 0, 0)], path=B.ENC_I8F16,
                      row_scale=rs)
@@ -284,10 +285,10 @@ def test_gemm_i8f16_beyond_31_bit_offsets_bit_identical():
 
 def test_gemm_i8f16_gated_kernel_choice_bit_identical():
     """Gated int8 rows computed in a launch of 256 x (128 + 128) tiles (1300
-    rows), of 192 x (128 + 128) tiles (1000 rows, a ragged last tile) and of
-    128 x (128 + 128) tiles (200 rows and fewer) give the same bits."""
+    rows), of 192 x (128 + 128) tiles (1000 and 390 rows, ragged last tiles)
+    and of 128 x (128 + 128) tiles (200 rows and fewer) give the same bits."""
     rng = np.random.default_rng(79)
-    n, ff, d = 1300, 11000, 256
+    n, ff, d = 1300, 10240, 256
     x = rng.normal(0, 1, (n, d)).astype(np.float16)
     W = [to_dev(rng.integers(-127, 128, (ff, d)).astype(np.int8)) for _ in range(2)]
     rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, ff))).astype(np.float32)) for _ in range(2)]

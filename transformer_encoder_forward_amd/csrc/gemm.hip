@@ -95,25 +95,30 @@ namespace {
 
 // The direct-to-LDS int8 kernel needs K % 64 == 0.  Plain GEMMs: 256 x 256
 // tiles (8 waves of 128 x 64, one block per CU) when the launch has at least
-// 256 of them.  Fewer (a 1056-row DiT batch: q|k|v 225 tiles, the output and
-// down projections 75) take the smaller tiles that fill the CUs in one round
-// of two blocks each: 64 x 256 tiles of 8 waves (64 x 32 each) when there are
-// at most 512 of them (the output and down projections: 255; 56% and 48%
-// faster than 256 x 256 there), else 128 x 256 tiles of 8 waves (64 x 64
-// each) with a two-stage ring, so that two blocks fit a CU (q|k|v: 405 tiles,
-// 5% faster than 765 tiles of 64 x 256 and 11% faster than 256 x 256).
-// 32 x 256 and 64 x 128 tiles were measured no faster than 64 x 256 on the
-// output and down projections, and 8 waves of 64 x 128 in the 256 x 256 tile
-// 3% slower than 128 x 64 at 8448 rows.  Gated: 256 x (128 + 128) with at
-// least 512 tiles of 256 x 128; else, for items of more than 384 rows,
-// 192 x (128 + 128) with a four-stage ring (the whole LDS): at 1056 rows its
-// 480 tiles take two rounds of the CUs where 720 tiles of 128 rows take
-// three, and its waves of 96 rows widen each W fragment for 96 rows instead of
-// 64 (10% faster than 128 x (128 + 128), which was 6% faster than
-// 256 x (128 + 128)); else 128 x (128 + 128) with a five-stage ring.  Otherwise (K % 64 != 0, or an item too large for the direct loads'
-// 32-bit offsets) the register-staged 128 x 128 kernel.  All sum in the same K
-// order.
-constexpr uint32_t kWideTiles = 256, kWideGated = 512, kSlots = 512;
+// 384 of them, or at least 256 that the smaller tiles below cannot take in
+// one round of two blocks per CU (with 256 to 383 tiles of 256 x 256 the
+// second round leaves most CUs idle: 1300 rows' q|k|v ran at 183 us on
+// 270 tiles).  Fewer take tiles that fill the CUs in one round of two blocks
+// each: 96 x 256 tiles of 4 waves (96 x 64 each: each W fragment widened for
+// 96 rows) with a two-stage ring when at most 512 of them cover the launch
+// (the 1056-row q|k|v: 495 tiles, 10% faster than 405 tiles of 128 x 256);
+// else 128 x 256 tiles of 8 waves (64 x 64 each) with a two-stage ring when
+// at most 512 of them do; else 64 x 256 tiles of 8 waves (64 x 32 each; the
+// 1056-row output and down projections: 255 tiles, 56% and 48% faster than
+// 256 x 256 there).  32 x 256 and 64 x 128 tiles were measured no faster than
+// 64 x 256 on the output and down projections, and 8 waves of 64 x 128 in the
+// 256 x 256 tile 3% slower than 128 x 64 at 8448 rows.  Gated: 256 x (128 +
+// 128) with at least 512 tiles of 256 x 128; else the one of 256, 192 and 128
+// rows (one block per CU each; 192 and 128 with four- and five-stage rings,
+// the whole LDS) with the fewest rounds of the CUs times rows per tile over
+// the tile's relative rate (1, 0.95, 0.8: the larger the wave's row span, the
+// fewer widenings per MFMA).  At 1056 rows that is 192 x (128 + 128): 480
+// tiles in two rounds, 10% faster than 720 tiles of 128 rows (three rounds),
+// which were 6% faster than 400 tiles of 256 rows.  Otherwise (K % 64 != 0,
+// or an item too large for the direct loads' 32-bit offsets) the
+// register-staged 128 x 128 kernel.  All sum in the same K order, so the
+// choice never changes a bit.
+constexpr uint32_t kWideTiles = 256, kWideGated = 512, kSlots = 512, kCUs = 256;
 
 }  // namespace
 
@@ -133,12 +138,23 @@ hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     if (kmul(a, 64) && offsets32(a)) {
         if (gated) {
             if (tiles_of(a, 256, 128) >= kWideGated) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
-            uint32_t maxn = 0;
-            for (uint32_t i = 0; i < a.nitems; i++) maxn = std::max(maxn, a.items[i].n);
-            return maxn > 384 ? gemm::launch_q8d<192, 256, 2, 4, 1, true, 4>(a, s)
-                              : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
+            // one block per CU for every gated tile: rounds of the CUs times
+            // the tile's rows over its measured relative rate
+            const auto cost = [&](int bm, double rate) {
+                return (double)((tiles_of(a, bm, 128) + kCUs - 1) / kCUs) * bm / rate;
+            };
+            const double c256 = cost(256, 1.0), c192 = cost(192, 0.95), c128 = cost(128, 0.8);
+            if (c256 <= c192 && c256 <= c128) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
+            return c192 <= c128 ? gemm::launch_q8d<192, 256, 2, 4, 1, true, 4>(a, s)
+                                : gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(a, s);
         }
-        if (tiles_of(a, 256, 256) >= kWideTiles) return gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
+        // 256 x 256 unless it leaves most CUs idle in a second round that the
+        // two-per-CU 128 x 256 tiles avoid
+        const uint32_t t256 = tiles_of(a, 256, 256);
+        if (t256 >= kWideTiles && (t256 >= kWideTiles * 3 / 2 || tiles_of(a, 128, 256) > kSlots))
+            return gemm::launch_q8d<256, 256, 2, 4, 1, false>(a, s);
+        if (tiles_of(a, 64, 256) > kSlots && tiles_of(a, 96, 256) <= kSlots)
+            return gemm::launch_q8d<96, 256, 1, 4, 2, false, 2>(a, s);
         if (tiles_of(a, 64, 256) > kSlots && tiles_of(a, 128, 256) <= kSlots)
             return gemm::launch_q8d<128, 256, 2, 4, 2, false, 2>(a, s);
         return gemm::launch_q8d<64, 256, 1, 8, 2, false>(a, s);
