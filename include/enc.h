@@ -496,6 +496,10 @@ ENC_API enc_status enc_check_attention(const enc_attn_desc *desc, const enc_item
                                uint32_t nitems, char *msg, size_t msg_len);
 ENC_API enc_status enc_check_model(const enc_model *model, const enc_batch *batch, char *msg,
                            size_t msg_len);
+/* The model and batch check alone, by the name the boundary's design gives it:
+ * enc_check_model without the message (the same checks encoder_forward and
+ * encoder_layer_forward run first, so a model it accepts is one they take). */
+ENC_API enc_status enc_validate_model(const enc_model *model, const enc_batch *batch);
 
 /* RoPE positions (host int32 [rows][sections]).  1-D (sections 1): the row's
  * index t within its item, restarting at 0 per item ([EG] `TextGpu::forward`,

@@ -179,6 +179,18 @@ def test_check_model_rejects():
     assert B.check_model(m, b)[0] == B.ENC_EINVAL
 
 
+def test_validate_model_gives_check_model_status():
+    w, m, b, keep = _fake_model("gemma_text_f32", lengths=[5, 7])
+    V = lambda: B.lib().enc_validate_model(C.byref(m), C.byref(b))  # noqa: E731
+    assert V() == B.ENC_OK
+    b.rows = 13
+    assert V() == B.check_model(m, b)[0] == B.ENC_ESHAPE
+    b.rows = 12
+    m.layers[1].hd = 96
+    assert V() == B.check_model(m, b)[0] == B.ENC_EUNSUPPORTED
+    assert B.lib().enc_validate_model(None, None) == B.check_model(None, None)[0] != B.ENC_OK
+
+
 def test_check_model_text_encoder_options():
     w, m, b, keep = _fake_model("gemma_text_ple_f32", lengths=[5, 7])
     st, msg = B.check_model(m, b)

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "ENC_OK", 1: "ENC_EINVAL", 2: "ENC_ESHAPE", 3: "ENC_EUNSUPPOR
 EXPORTS = ["enc_create", "enc_destroy", "enc_last_error", "gemm_items", "attention_items",
            "attention_items_static", "enc_rms_norm", "enc_layer_norm", "enc_add_norm", "enc_qk_norm_rope", "enc_gated_act",
            "enc_mean_pool", "enc_workspace_bytes", "encoder_layer_forward", "encoder_forward",
-           "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_positions",
+           "enc_check_gemm", "enc_check_attention", "enc_check_model", "enc_validate_model", "enc_positions",
            "enc_rope_table", "enc_prof_enable", "enc_prof_read", "enc_mfma_peak",
            "enc_attention_workspace_bytes", "encoder_stages_forward", "enc_stages_workspace_bytes"]
 CLASS_NAMES = ["gemm", "attn", "rows"]
@@ -196,6 +196,7 @@ def lib():
     L.enc_check_attention.argtypes = [C.POINTER(AttnDesc), C.POINTER(Item), C.c_uint32,
                                       C.c_char_p, C.c_size_t]
     L.enc_check_model.argtypes = [C.POINTER(Model), C.POINTER(Batch), C.c_char_p, C.c_size_t]
+    L.enc_validate_model.argtypes = [C.POINTER(Model), C.POINTER(Batch)]
     L.enc_positions.argtypes = [C.c_uint32, C.POINTER(Item), P, C.c_uint32, C.c_uint32, P]
     L.enc_rope_table.argtypes = [C.c_uint32, C.c_uint32, C.c_uint32, P, C.c_double, P, P]
     L.enc_prof_enable.argtypes = [P, C.c_int]
@@ -204,6 +205,7 @@ def lib():
     for f in ("gemm_items", "attention_items", "attention_items_static", "enc_rms_norm", "enc_layer_norm", "enc_add_norm",
               "enc_qk_norm_rope", "enc_gated_act", "enc_mean_pool", "encoder_layer_forward",
               "encoder_forward", "encoder_stages_forward", "enc_check_gemm", "enc_check_attention", "enc_check_model",
+              "enc_validate_model",
               "enc_positions", "enc_rope_table", "enc_prof_enable", "enc_prof_read",
               "enc_mfma_peak"):
         getattr(L, f).restype = S

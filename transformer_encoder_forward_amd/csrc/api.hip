@@ -1157,6 +1157,10 @@ enc_status enc_check_model(const enc_model *model, const enc_batch *batch, char 
     return e.st;
 }
 
+enc_status enc_validate_model(const enc_model *model, const enc_batch *batch) {
+    return enc_check_model(model, batch, nullptr, 0);
+}
+
 enc_status gemm_items(enc_ctx *ctx, const enc_gemm_desc *desc, const enc_gemm_item *items,
                       uint32_t nitems, enc_stream stream) {
     Err e;
