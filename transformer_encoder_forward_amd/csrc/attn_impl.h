@@ -548,8 +548,8 @@ template <int NW, int MINW, bool BUF, bool PAIR>
 __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     constexpr int HD = 128, QT = 32 * NW, NS = PAIR ? 6 : 4;
     constexpr int TBYTES = KB * HD * 2;   // one K or V block: 8 KB
-    constexpr int SBYTES = 2 * TBYTES;    // a stage: K then V
-    constexpr int VREG = NS * TBYTES;     // K blocks of the stages, then their V blocks
+    constexpr int SBYTES = 2 * TBYTES;    // a stage's K and V blocks
+    constexpr int VREG = NS * TBYTES;     // the stages' K blocks, then from VREG their V blocks
     constexpr int NI = TBYTES / 1024 / NW;
     constexpr int NDMA = 2 * NI;
     static_assert(TBYTES / 1024 % NW == 0, "waves");
