@@ -118,7 +118,6 @@ namespace {
 // or an item too large for the direct loads' 32-bit offsets) the
 // register-staged 128 x 128 kernel.  All sum in the same K order, so the
 // choice never changes a bit.
-constexpr uint32_t kWideTiles = 256, kWideGated = 512, kSlots = 512, kCUs = 256;
 
 }  // namespace
 
@@ -136,12 +135,16 @@ static bool offsets32(const GemmArgs &a) {
 hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
     const bool gated = a.flags & (gemm::kGateGelu | gemm::kGateSilu);
     if (kmul(a, 64) && offsets32(a)) {
+        // the thresholds are in units of the device's CUs (256 on MI355X):
+        // one block per CU for the 256-row tiles, two for the smaller ones
+        const uint32_t cus = (uint32_t)gemm::device_cus(), kWideTiles = cus, kWideGated = 2 * cus,
+                       kSlots = 2 * cus;
         if (gated) {
             if (tiles_of(a, 256, 128) >= kWideGated) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
             // one block per CU for every gated tile: rounds of the CUs times
             // the tile's rows over its measured relative rate
             const auto cost = [&](int bm, double rate) {
-                return (double)((tiles_of(a, bm, 128) + kCUs - 1) / kCUs) * bm / rate;
+                return (double)((tiles_of(a, bm, 128) + cus - 1) / cus) * bm / rate;
             };
             const double c256 = cost(256, 1.0), c192 = cost(192, 0.95), c128 = cost(128, 0.8);
             if (c256 <= c192 && c256 <= c128) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
