@@ -108,11 +108,11 @@ __device__ __forceinline__ void locate_tile(const GemmArgs &a, uint32_t tile, Ti
 // blocks go to the eight XCDs in turn, so block b takes tile xcd_remap(b) and
 // each XCD works through one contiguous run of tiles (shared rows and columns
 // stay in its L2).
-template <int BM, int BN>
+template <int BM, int BN, int G = GR>
 __device__ __forceinline__ bool locate(const GemmArgs &a, TileCtx &t, int cols_per_tile = BN) {
     const uint32_t tile = xcd_remap(blockIdx.x, gridDim.x);
     if (tile >= a.total_tiles) return false;
-    locate_tile<BM, BN>(a, tile, t, cols_per_tile);
+    locate_tile<BM, BN, G>(a, tile, t, cols_per_tile);
     return true;
 }
 
@@ -897,8 +897,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINB) void gemm_q8d_kernel(GemmArgs
     static_assert(NS * S_BYTES <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * S_BYTES];
 
+    // groups of four row tiles: an XCD's 32 concurrent tiles are 4 row tiles by
+    // 8 column tiles, whose X slabs (two bytes per value) and W slabs (one)
+    // together stream least from beyond the L2 (8448 rows: 16-21% fewer bytes
+    // fetched per launch than groups of eight, and 0-1% faster)
     TileCtx t;
-    if (!locate<BM, BN>(a, t, GATED ? BN / 2 : BN)) return;
+    if (!locate<BM, BN, 4>(a, t, GATED ? BN / 2 : BN)) return;
     const int8_t *wg = reinterpret_cast<const int8_t *>(t.w), *wu = wg;
     const float *rg = t.rs, *ru = t.rs;
     if constexpr (GATED) {
