@@ -420,12 +420,11 @@ def test_attention_f16_wide_launch_two_range_sampled():
     assert err <= TOL_I8F16
 
 
-def test_attention_f16_eight_wave_blocks_short_items():
-    """Items of 1 to 10 key blocks (every count of blocks modulo the six-stage
-    ring of the 8-wave f16 kernel, ragged last blocks) in a launch wide enough
-    for 256-query blocks (nq 32, GQA 4:1): every row against the oracle, and
-    three items alone (a narrower launch, 128-query blocks) give the packed
-    rows' bits."""
+def test_attention_f16_split_keys_short_items():
+    """Items of 1 to 10 key blocks, which take the kernel that splits each
+    query's keys two ways inside the block (every count of blocks per half,
+    an empty second half at one block, ragged last blocks, GQA 4:1): every row
+    against the oracle, and three items alone give the packed rows' bits."""
     lens = [1, 31, 32, 33, 64, 65, 96, 97, 128, 160, 161, 192, 193, 224, 255, 256, 257, 300]
     items, r = [], 0
     for n in lens:
@@ -450,16 +449,53 @@ def test_attention_f16_eight_wave_blocks_short_items():
         assert torch.equal(o1, out[r0:r0 + n]), f"item {i} ({n} rows)"
 
 
+def test_attention_f16_long_items_ring_and_split_boundary():
+    """At nq 32 items of more than 1024 rows (more than 16 blocks of 64
+    queries per head) take the pipelined kernel: 33 and 50 to 55 key blocks
+    (every count modulo its six-stage ring, ragged last blocks) in a launch
+    wide enough for 256-query blocks (GQA 4:1), next to a 1024-row item that
+    takes the split-key kernel; sampled query rows of every item against the
+    oracle, and items alone give the packed rows' bits (the 1025-row one alone
+    runs 128-query blocks)."""
+    lens = [1024, 1025, 1569, 1601, 1664, 1665, 1727, 1760]
+    items, r = [], 0
+    for n in lens:
+        items.append([(r, n)])
+        r += n
+    rows, nq, nkv, hd = r, 32, 8, 128
+    rng = np.random.default_rng(23)
+    p = _panel(rng, rows, nq, nkv, hd, f16=True, qscale=0.5)
+    out = torch.zeros((rows, nq * hd), dtype=torch.float16, device=DEV)
+    scale = 1.0 / np.sqrt(hd)
+    B.attention_items(to_dev(p), out, items, nq, nkv, hd, scale, 0, path=B.ENC_I8F16)
+    sel = []
+    for (r0, n), in items:
+        sel += [r0, r0 + 31, r0 + 32, r0 + n // 2, r0 + n - 33, r0 + n - 1]
+    sel = np.unique(np.array(sel + list(rng.integers(0, rows, 16))))
+    q, k, v = _split(p, nq, nkv, hd)
+    ref = O.attention(items, q, k, v, nq, nkv, hd, scale, 0, query_rows=sel)[sel]
+    err = row_rel_err(host(out)[sel], ref)
+    say(f"  {len(sel)} sampled queries, err {err:.2e}")
+    assert err <= TOL_I8F16
+    for i in (0, 1, 7):
+        (r0, n), = items[i]
+        o1 = torch.zeros((n, nq * hd), dtype=torch.float16, device=DEV)
+        B.attention_items(to_dev(p[r0:r0 + n]), o1, [[(0, n)]], nq, nkv, hd, scale, 0, path=B.ENC_I8F16)
+        assert torch.equal(o1, out[r0:r0 + n]), f"item {i} ({n} rows)"
+
+
 @pytest.mark.parametrize("nq", [4, 128])
 def test_attention_f16_panel_beyond_31_bit_offsets(nq):
     """Items at the end of a q/k/v panel of more than 2^31 bytes are staged by
-    64-bit per-lane addresses instead of raw buffer loads (nq 4: 128-query
-    blocks; nq 128: 256-query blocks with the six-stage ring); their rows equal
-    the same items in a small panel, bit for bit."""
+    64-bit per-lane addresses instead of raw buffer loads (nq 4: the last item
+    takes 128-query blocks, the others the split-key kernel; nq 128: the 33-
+    and 256-row items the split-key kernel, the others 256-query blocks with
+    the six-stage ring); their rows equal the same items in a small panel, bit
+    for bit."""
     hd = 128
     ld = 3 * nq * hd
-    rows = (2 ** 31) // (ld * 2) + 1200
-    lens = [300, 257, 33, 256]
+    lens = [300, 257, 33, 256, 8300 if nq == 4 else 1600]
+    rows = (2 ** 31) // (ld * 2) + sum(lens) + 300
     r0 = rows - sum(lens)
     items, r = [], r0
     for n in lens:
@@ -596,13 +632,14 @@ def test_attention_key_split(path, items, nq, nkv, hd):
     assert torch.equal(out, out2), "key-split attention is not deterministic"
 
 
-@pytest.mark.parametrize("path,hd", [(B.ENC_F32, 64), (B.ENC_I8F16, 128)])
-def test_attention_packed_equals_separate_long_items(path, hd):
-    """Items long enough for the f32 key split (the f16 path runs them unsplit)."""
+@pytest.mark.parametrize("path,hd,nq", [(B.ENC_F32, 64, 4), (B.ENC_I8F16, 128, 32)])
+def test_attention_packed_equals_separate_long_items(path, hd, nq):
+    """Items long enough for the f32 key split across blocks; on the f16 path
+    (nq 32) the 1800-row item takes the unsplit kernel and the others the
+    split-key one, in two launches."""
     f16 = path == B.ENC_I8F16
-    nq = 4
-    items = [[(0, 1024)], [(1024, 700)], [(1724, 90)]]
-    rows = 1814
+    items = [[(0, 1800)], [(1800, 700)], [(2500, 90)]]
+    rows = 2590
     rng = np.random.default_rng(11)
     p = _panel(rng, rows, nq, nq, hd, f16=f16)
     dt = torch.float16 if f16 else torch.float32

@@ -340,19 +340,48 @@ hipError_t launch_attn_combine(const CombineArgs &a, bool f16_out, hipStream_t s
     return hipGetLastError();
 }
 
-// hd 128 takes the direct-to-LDS kernels.  Without a window: the pipelined
-// one, in blocks of 256 queries (8 waves, one block per CU, each K/V block
-// staged once for twice the queries) when the launch still has two such blocks
-// per CU, else 128.  With a window, a block's first key depends on its query
-// tile, so the tile size must not change between launches of the same item:
-// always 128 queries.  Every choice sums each query's keys in the same order.
+// hd 128 takes the direct-to-LDS kernels.  With a window, a block's first key
+// depends on its query tile, so the tile size must not change between launches
+// of the same item: always 128 queries.  Without one, an item whose 64-query
+// blocks times heads number at most 512 (alone, it would fill one round of two
+// such blocks per CU of a 256-CU device: up to 1088 rows at 30 heads) takes
+// the kernel that splits each query's keys two ways inside the block.  The
+// choice follows the item alone (its length and head count; a launch with both
+// kinds of item is issued as two), so an item's bits never depend on the batch.
+// Longer items take the pipelined kernel, in blocks of 256 queries (8 waves,
+// one block per CU, each K/V block staged once for twice the queries) when the
+// launch still has two such blocks per CU, else 128, which sum each query's
+// keys in the same order.
+// Measured per launch at 30 heads: one 1056-row item 39.3 -> 30.4 us split;
+// a 1536-row item (720 blocks, not split) 62.6 unsplit against 64.4 split; two
+// 960-row items are split (450 blocks each) and run 46.2 -> 51.6 us: unsplit
+// their 480 blocks of 128 queries already give each SIMD two waves.
+constexpr uint32_t kSplitBlocks = 512;
+
+static bool f16_split_item(const AttnItemK &it, uint32_t nq) {
+    return (uint64_t)((it.na + it.nb + 63) / 64) * nq <= kSplitBlocks;
+}
+
 hipError_t launch_attn_f16(const AttnArgs &a, uint32_t hd, hipStream_t s) {
     if (hd == 64) return attn::launch<64, true, 4, 4, true>(a, s);
     if (a.window) return attn::launch_f16d<4, 2>(a, s);
+    AttnArgs sp = a, lo = a;
+    sp.nitems = lo.nitems = 0;
+    for (uint32_t i = 0; i < a.nitems; i++) {
+        if (f16_split_item(a.items[i], a.nq))
+            sp.items[sp.nitems++] = a.items[i];
+        else
+            lo.items[lo.nitems++] = a.items[i];
+    }
+    if (sp.nitems) {
+        const hipError_t h = attn::launch_f16k(sp, s);
+        if (h != hipSuccess || !lo.nitems) return h;
+    }
+    if (!lo.nitems) return hipSuccess;
     uint32_t t256 = 0;
-    for (uint32_t i = 0; i < a.nitems; i++) t256 += (a.items[i].na + a.items[i].nb + 255) / 256;
-    if (t256 * a.nq >= 512) return attn::launch_f16s<8, 1>(a, s);
-    return attn::launch_f16s<4, 2>(a, s);
+    for (uint32_t i = 0; i < lo.nitems; i++) t256 += (lo.items[i].na + lo.items[i].nb + 255) / 256;
+    if (t256 * lo.nq >= 512) return attn::launch_f16s<8, 1>(lo, s);
+    return attn::launch_f16s<4, 2>(lo, s);
 }
 
 }  // namespace enc

@@ -14,8 +14,9 @@
 // and 16 of the block's keys: the row max and row sum are 16 lane-local steps
 // plus one exchange with lane l^32, and P^T is already in the B-operand layout
 // of O^T = V^T P^T.  K/V blocks are staged in LDS (double-buffered through
-// registers in the template below, a ring of direct global -> LDS loads in
-// attn_f16d_kernel and attn_f16s_kernel) and shared by the block's waves.  VALU
+// registers in the template below, rings of direct global -> LDS loads in
+// attn_f16d_kernel, attn_f16s_kernel and attn_f16k_kernel) and shared by the
+// block's waves (attn_f16k_kernel: by the two waves of each key half).  VALU
 // work per score is kept small: blocks that lie wholly inside every query's
 // window skip the mask, and the running output is rescaled only when the
 // running max moves (otherwise the factor is exactly 1).  Waves whose queries
@@ -852,6 +853,318 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
     }
 }
 
+// f16 flash attention at head dim 128 for short items, with each query's keys
+// split two ways inside the block.  An item of 1056 rows has 33 groups of 32
+// queries per head: 990 waves of 32 queries for 30 heads on 1024 SIMDs, one
+// wave per SIMD with nothing to hide its latencies.  Here a block of four waves
+// takes 64 queries of one item and one head: waves 0 and 1 (part 0) run the
+// first ceil(n/2) of the item's n key blocks for their 32 queries each, waves
+// 2 and 3 (part 1) the rest, and at the end part 1 hands its unnormalised
+// output, running max and row sums to part 0 through the LDS.  The result is
+// part 0's sums plus part 1's, each rescaled to the larger of the two running
+// maxima: the split follows the item's length alone, so an item gets the same
+// bits in any batch.
+// Each part has its own two-stage K ring and two-stage V ring (32 KB; 64 KB a
+// block, so two blocks share a CU and each SIMD holds two waves).  Step b of a
+// part: the row max of block b; V(b) read from its stage; the scores of block
+// b+1 interleaved with block b's exponentials (as in attn_f16s_kernel); the
+// first half of P V; one barrier, behind which the freed stages take K(b+3)
+// and V(b+2), K(b+2) is read into registers and the second half of P V is
+// issued.  A load has one step to land.
+template <bool BUF>
+__global__ __launch_bounds__(256, 2) void attn_f16k_kernel(AttnArgs a) {
+    constexpr int HD = 128, QT = 64;
+    constexpr int TBYTES = KB * HD * 2;    // one K or V block: 8 KB
+    constexpr int PBYTES = 4 * TBYTES;     // a part's K stages 0, 1, then its V stages 0, 1
+    constexpr int NI = TBYTES / 1024 / 2;  // load instructions per wave per K or V block
+    constexpr int XW = HD / 32 * 16 + 2;   // floats a lane hands over: o, running max, row sum
+    static_assert(2 * XW * 64 * 4 <= 2 * PBYTES, "hand-over fits the ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * PBYTES];
+
+    const uint32_t head = blockIdx.x % a.nq, tile = blockIdx.x / a.nq;
+    ItemCtx c;
+    locate<QT>(a, tile, c);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the part's values stay scalar
+    const int qg = wave & 1, part = wave >> 1;
+    const int li = lane & 31, hf = lane >> 5;
+    const int kvh = head / a.group;
+    const _Float16 *P = reinterpret_cast<const _Float16 *>(a.qkv);
+
+    const int tq = c.q_lo + qg * 32 + li;
+    const bool qvalid = tq < c.q_hi;
+    const bool wactive = c.q_lo + qg * 32 < c.q_hi;  // waves without queries only join the barriers
+
+    // this part's key blocks: [g0, g0 + nmine) of the item's nblk
+    const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
+    const int n0 = (nblk + 1) / 2;
+    const int g0 = part ? n0 : 0;
+    const int nmine = part ? nblk - n0 : n0;
+    uint8_t *const pbuf = smem + part * PBYTES;
+
+    f16x8 qf[HD / 16];
+    {
+        const _Float16 *qp = P + (size_t)row_of(c.it, qvalid ? tq : c.q_lo) * a.ld + a.q_col + head * HD + 64 * hf;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) qf[j] = *reinterpret_cast<const f16x8 *>(qp + 8 * j);
+        vm_wait<0>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) ready(qf[j]);
+    }
+
+    // staging (as attn_f16s_kernel, over the part's two waves): instruction q
+    // of this wave covers keys 4 (qg NI + q) .. +3 of a block
+    const int kl = lane >> 4, pl = lane & 15;
+    uint32_t kso[NI], vso[NI];
+#pragma unroll
+    for (int q = 0; q < NI; q++) {
+        const uint32_t ti = 4 * (qg * NI + q) + kl;
+        const uint32_t r = ti * a.ld + kvh * HD;
+        kso[q] = 2 * (r + a.k_col + 8 * (pl ^ (ti & 15)));
+        vso[q] = 2 * (r + a.v_col + 8 * (pl ^ (4 * (ti & 3))));
+    }
+    const int na = (int)c.it.na;
+    const __amdgpu_buffer_rsrc_t pres = raw_buffer(P);
+    // key block b of the item (K with V = false) into the 8 KB at buf
+    auto dma = [&](uint8_t *buf, bool v, int b) {
+        const int kb = c.k_lo + b * KB;
+        if (kb + KB <= c.k_hi && (kb + KB <= na || kb >= na)) {
+            const int r0 = kb < na ? (int)c.it.r0a + kb : (int)c.it.r0b + (kb - na);
+            if constexpr (BUF) {
+                const uint32_t soff = (uint32_t)r0 * a.ld * 2u;
+#pragma unroll
+                for (int q = 0; q < NI; q++) buffer_dma16(pres, buf + (qg * NI + q) * 1024, v ? vso[q] : kso[q], soff);
+            } else {
+                const char *base = reinterpret_cast<const char *>(P + (size_t)r0 * a.ld);
+#pragma unroll
+                for (int q = 0; q < NI; q++) dma16(base + (v ? vso[q] : kso[q]), buf + (qg * NI + q) * 1024);
+            }
+        } else {
+            // the block crosses into the second row range or past the item:
+            // rows per lane, keys past the item clamped to its last row (masked)
+#pragma unroll
+            for (int q = 0; q < NI; q++) {
+                const int ti = 4 * (qg * NI + q) + kl;
+                const int t = min(kb + ti, c.k_hi - 1);
+                const char *base = reinterpret_cast<const char *>(P + ((ptrdiff_t)row_of(c.it, t) - ti) * a.ld);
+                dma16(base + (v ? vso[q] : kso[q]), buf + (qg * NI + q) * 1024);
+            }
+        }
+    };
+    auto dmaK = [&](auto st, int b) { dma(pbuf + decltype(st)::value * TBYTES, false, b); };
+    auto dmaV = [&](auto st, int b) { dma(pbuf + (2 + decltype(st)::value) * TBYTES, true, b); };
+
+    // fragment addresses in the part's ring (as attn_f16s_kernel)
+    const uint32_t lds0 = lds_offset(pbuf);
+    uint32_t kaddr[HD / 16], vaddr[HD / 32];
+#pragma unroll
+    for (int j = 0; j < HD / 16; j++) kaddr[j] = lds0 + (uint32_t)li * 256u + (uint32_t)(((8 * hf + j) ^ (li & 15)) * 16);
+    {
+        const int g = lane >> 4, src = lane & 15;
+        const uint32_t vrow = lds0 + 2 * TBYTES + (uint32_t)(4 * (g >> 1) + (src >> 2)) * 256u + 8u * (src & 1);
+        const int vc0 = 2 * (g & 1) + ((src & 3) >> 1), vsw = 4 * (src >> 2);
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) vaddr[d] = vrow + (uint32_t)(((4 * d + vc0) ^ vsw) * 16);
+    }
+    u32x4 kf[HD / 16];
+    u32x2 vf[HD / 32][2][2];
+    auto vread = [&](auto st, int d, auto s2c) {
+        constexpr int s2 = decltype(s2c)::value;
+        constexpr int off = decltype(st)::value * TBYTES + 16 * s2 * 256;
+        vf[d][s2][0] = ds_read8_tr16_at<off>(vaddr[d]);
+        vf[d][s2][1] = ds_read8_tr16_at<off + 8 * 256>(vaddr[d]);
+    };
+    auto kread_to = [&](auto st, u32x4 (&k)[HD / 16]) {
+        constexpr int off = decltype(st)::value * TBYTES;
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) k[j] = ds_read16_at<off>(kaddr[j]);
+    };
+
+    f32x16 o[HD / 32];
+#pragma unroll
+    for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
+    float m_run = -INFINITY, l_lane = 0.0f;
+    const float cs = a.scale_log2;
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+    // K(0), V(0), K(1); after K(0) is read everywhere, K(2) and V(1)
+    if (nmine > 0) {
+        dmaK(IC<0>{}, g0);
+        dmaV(IC<0>{}, g0);
+    }
+    if (nmine > 1) dmaK(IC<1>{}, g0 + 1);
+    vm_wait<0>();
+    block_barrier();
+    f32x16 sA, sB;
+#pragma unroll
+    for (int r = 0; r < 16; r++) sA[r] = 0.0f;
+    if (wactive && nmine > 0) {
+        kread_to(IC<0>{}, kf);
+        lgkm_wait_n<0>();
+#pragma unroll
+        for (int j = 0; j < HD / 16; j++) {
+            ready(kf[j]);
+            sA = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], sA, 0, 0, 0);
+        }
+        if (nmine > 1) kread_to(IC<1>{}, kf);
+    }
+    block_barrier();
+    if (nmine > 2) dmaK(IC<0>{}, g0 + 2);
+    if (nmine > 1) dmaV(IC<1>{}, g0 + 1);
+
+    // part block b (K and V stage S = b % 2): scores in s_cur, block b+1's K
+    // fragments in flight in kf; leaves block b+1's scores in s_nx and block
+    // b+2's K in flight
+    auto step = [&](auto st, int b, f32x16 &s_cur, f32x16 &s_nx) {
+        constexpr int S = decltype(st)::value;
+        f16x8 pb[2];
+        const bool act = wactive && b < nmine;
+        if (act) {
+            const int kb = c.k_lo + (g0 + b) * KB;
+            if (kb + KB > c.k_hi) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    const int key = kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    s_cur[r] = key < c.k_hi ? s_cur[r] : -INFINITY;
+                }
+            }
+            float mx = __builtin_elementwise_maximum(s_cur[0], s_cur[1]);
+#pragma unroll
+            for (int r = 2; r < 16; r++) mx = __builtin_elementwise_maximum(mx, s_cur[r]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            const float mb = mx * cs;
+            const bool up = mb > m_run + 8.0f;
+            if (__any(up)) {
+                const float m_new = up ? mb : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_lane *= alpha;
+#pragma unroll
+                for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) o[d][r] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+
+            vread(st, 0, IC<0>{});
+            vread(st, 1, IC<0>{});
+            vread(st, 2, IC<0>{});
+            vread(st, 3, IC<0>{});
+#pragma unroll
+            for (int r = 0; r < 16; r++) s_nx[r] = 0.0f;
+            float rs = 0.0f;
+            // K fragment j of block b+1 has landed once at most 15 - j reads
+            // are in flight (its 8 reads, then V's 8; DS reads complete in order)
+            auto group = [&](auto jc) {
+                constexpr int j = decltype(jc)::value, s2 = j / 4, e = 2 * (j % 4);
+                const f16x2 pr = {(_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e], cs, -m_use)),
+                                  (_Float16)__builtin_amdgcn_exp2f(fmaf(s_cur[8 * s2 + e + 1], cs, -m_use))};
+                pb[s2][e] = pr[0];
+                pb[s2][e + 1] = pr[1];
+                rs = __builtin_amdgcn_fdot2(pr, ones, rs, false);
+                __builtin_amdgcn_sched_barrier(0);
+                lgkm_wait_n<15 - j>();
+                ready(kf[j]);
+                s_nx = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kf[j]), qf[j], s_nx, 0, 0, 0);
+            };
+            group(IC<0>{});
+            group(IC<1>{});
+            group(IC<2>{});
+            group(IC<3>{});
+            group(IC<4>{});
+            group(IC<5>{});
+            group(IC<6>{});
+            group(IC<7>{});
+            l_lane += rs;
+            vread(st, 0, IC<1>{});
+            vread(st, 1, IC<1>{});
+            vread(st, 2, IC<1>{});
+            vread(st, 3, IC<1>{});
+            lgkm_wait_n<8>();  // the first half of V landed
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][0][0]);
+                ready(vf[d][0][1]);
+            }
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                const u32x4 vv = {vf[d][0][0][0], vf[d][0][0][1], vf[d][0][1][0], vf[d][0][1][1]};
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[0], o[d], 0, 0, 0);
+            }
+            lgkm_wait_n<0>();
+#pragma unroll
+            for (int d = 0; d < HD / 32; d++) {
+                ready(vf[d][1][0]);
+                ready(vf[d][1][1]);
+            }
+        }
+        // every wave: K(b+2) and V(b+1) landed and this wave's reads of K(b+1)
+        // and V(b) done; behind the barrier K stage S + 1 takes K(b+3) and V
+        // stage S takes V(b+2)
+        vm_wait<0>();
+        block_barrier();
+        if (b + 3 < nmine) dmaK(IC<(S + 1) % 2>{}, g0 + b + 3);
+        if (b + 2 < nmine) dmaV(st, g0 + b + 2);
+        if (!act) return;
+        if (b + 2 < nmine) kread_to(st, kf);
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++) {
+            const u32x4 vv = {vf[d][1][0][0], vf[d][1][0][1], vf[d][1][1][0], vf[d][1][1][1]};
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv), pb[1], o[d], 0, 0, 0);
+        }
+    };
+    // both parts take n0 steps (the barriers); part 1 idles through the last
+    // one when nblk is odd
+    for (int b = 0; b < n0; b += 2) {
+        step(IC<0>{}, b, sA, sB);
+        if (b + 1 >= n0) break;
+        step(IC<1>{}, b + 1, sB, sA);
+    }
+
+    // hand-over (ordinary LDS stores and loads, so barriers with fences): no
+    // read of the ring is pending after the last step's barrier (its K read
+    // needs b + 2 < nmine)
+    __syncthreads();
+    float *const xch = reinterpret_cast<float *>(smem) + qg * XW * 64 + lane;
+    if (part == 1) {
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) xch[(16 * d + r) * 64] = o[d][r];
+        xch[(XW - 2) * 64] = m_run;
+        xch[(XW - 1) * 64] = l_lane;
+    }
+    __syncthreads();
+    if (part == 1) return;
+    const float m1 = xch[(XW - 2) * 64], l1 = xch[(XW - 1) * 64];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+    const float l_m = l_lane * a0 + l1 * a1;
+    const float l_run = l_m + __shfl_xor(l_m, 32, 64);
+    if (qvalid) {
+        const float inv = 1.0f / l_run;
+        _Float16 *out = reinterpret_cast<_Float16 *>(a.out) + (size_t)row_of(c.it, tq) * a.ldo + head * HD;
+#pragma unroll
+        for (int d = 0; d < HD / 32; d++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int ch = 32 * d + 8 * q + 4 * hf;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int r = 4 * q + e;
+                    v[e] = (o[d][r] * a0 + xch[(16 * d + r) * 64] * a1) * inv;
+                }
+                st4h(out + ch, out_scale(a, head * HD + ch, v));
+            }
+    }
+}
+
 // Tiles of the launch for QT queries per block (fills tile0, ntiles): q-tiles
 // times key splits per item.  Only the f32 kernel reads the split fields; the
 // host gives every item of an f16 launch nsplit = 1.
@@ -882,6 +1195,16 @@ hipError_t launch_f16s(AttnArgs a, hipStream_t s) {
         hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, true, PAIR>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
     else
         hipLaunchKernelGGL((attn_f16s_kernel<NW, MINW, false, PAIR>), dim3(tiles * a.nq), dim3(64 * NW), 0, s, a);
+    return hipGetLastError();
+}
+
+inline hipError_t launch_f16k(AttnArgs a, hipStream_t s) {
+    const uint32_t tiles = plan_tiles(a, 64);
+    if (!tiles) return hipSuccess;
+    if ((uint64_t)a.rows * a.ld * 2u <= 0x7fffffffu)
+        hipLaunchKernelGGL((attn_f16k_kernel<true>), dim3(tiles * a.nq), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((attn_f16k_kernel<false>), dim3(tiles * a.nq), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
