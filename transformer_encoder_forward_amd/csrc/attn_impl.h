@@ -662,6 +662,10 @@ __global__ __launch_bounds__(64 * NW, MINW) void attn_f16s_kernel(AttnArgs a) {
         for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
     float m_run = -INFINITY, l_lane = 0.0f;
     const float cs = a.scale_log2;
+    // the scalar load of the scale lands here, on every path into the loop: a
+    // load still pending at the loop head makes the compiler wait for every LDS
+    // read in flight (lgkmcnt(0)) at the scale's first use in each step
+    asm volatile("" ::"s"(cs));
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     const int nblk = (c.k_hi - c.k_lo + KB - 1) / KB;
@@ -987,6 +991,10 @@ __global__ __launch_bounds__(256, 2) void attn_f16k_kernel(AttnArgs a) {
         for (int r = 0; r < 16; r++) o[d][r] = 0.0f;
     float m_run = -INFINITY, l_lane = 0.0f;
     const float cs = a.scale_log2;
+    // the scalar load of the scale lands here, on every path into the loop: a
+    // load still pending at the loop head makes the compiler wait for every LDS
+    // read in flight (lgkmcnt(0)) at the scale's first use in each step
+    asm volatile("" ::"s"(cs));
     const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
     // K(0), V(0), K(1); after K(0) is read everywhere, K(2) and V(1)
