@@ -22,8 +22,9 @@ range, its first two, middle and last two rows, the rows at offsets 127, 128,
 255 and 256 of a range (the edges of the GEMM and attention tiles) and four
 seeded draws per item.
 
-The CFG pair at 8448 rows stores its first item only, and the oracle runs that
-item alone (its 4224 rows, as the single-item layout orders them): a packed
+The CFG pairs (8448 rows; the padded pair) store their first item only, and
+the oracle runs that item alone (its rows, as the single-item layout orders
+them, with the pair's positions of those rows where they are explicit): a packed
 item shares no row with another in attention and every other step is
 row-local, so by the definition of a packed batch the item's rows of the pair's
 forward are the forward of the item alone.  That halves an oracle run of
@@ -51,7 +52,7 @@ SYNTH_SRC = os.path.join(ROOT, "transformer_encoder_forward_amd", "synth.py")
 
 WORKLOADS = ("gemma_text_f32", "gemma_text_ple_f32", "zimage_dit_1056", "zimage_dit_cfg_8448",
              "zimage_dit_pad_cfg", "zimage_dit_mod_1056")
-FIRST_ITEM_ONLY = ("zimage_dit_cfg_8448",)  # the oracle runs item 0 alone (module doc)
+FIRST_ITEM_ONLY = ("zimage_dit_cfg_8448", "zimage_dit_pad_cfg")  # the oracle runs item 0 alone (module doc)
 
 
 def positions(w):
@@ -157,8 +158,8 @@ def write(name: str) -> None:
           f"oracle threads {O.threads()}", flush=True)
     t0 = time.time()
     if name in FIRST_ITEM_ONLY:
-        # item 0 alone, in the single-item layout of the same model
-        assert pos is None
+        # item 0 alone, in the single-item layout of the same model (with the
+        # pair's positions of its rows, when they are explicit)
         idx = item_rows(w.items[0])
         srows, sitems, sgrids = wl.layout(w.cfg, cfg_pair=False)
         assert srows == len(idx)
@@ -166,7 +167,7 @@ def write(name: str) -> None:
                              x=w.x[idx], seed=w.seed)
         single.layers, single.final_w, single.final_b = w.layers, w.final_w, w.final_b
         out = np.zeros((w.rows, w.cfg["d"]))
-        out[idx] = O.forward(single)
+        out[idx] = O.forward(single, pos=None if pos is None else pos[idx])
         assert np.isin(rows, idx).all()
     else:
         out = O.forward(w, pos=pos)
