@@ -302,6 +302,29 @@ def test_gemm_i8f16_gated_kernel_choice_bit_identical():
         assert torch.equal(Y, Yall[r0:r1]), (r0, r1)
 
 
+def test_gemm_i8f16_gated_last_row_tile_peel_bit_identical():
+    """A one-item gated launch of 8448 rows (33 x 80 tiles of 256 x (128 + 128):
+    ten rounds of 256 CUs and 80 tiles) issues its last 256 rows as a second
+    launch of 128-row tiles; its rows equal those of the same rows as two items
+    of one launch (no peel), bit for bit."""
+    rng = np.random.default_rng(83)
+    n, ff, d = 8448, 10240, 256
+    x = to_dev(rng.normal(0, 1, (n, d)).astype(np.float16))
+    W = [to_dev(rng.integers(-127, 128, (ff, d)).astype(np.int8)) for _ in range(2)]
+    rs = [to_dev((0.002 * np.exp(0.25 * rng.normal(0, 1, ff))).astype(np.float32)) for _ in range(2)]
+    flags = B.ENC_EPI_GATE_SILU | B.ENC_Y_F16
+    Y1 = torch.empty((n, ff), dtype=torch.float16, device=DEV)
+    B.gemm_items(x, Y1, W, [(n, ff, d, d, ff, 0, 0, 0)], path=B.ENC_I8F16, row_scale=rs, flags=flags)
+    Y2 = torch.empty((n, ff), dtype=torch.float16, device=DEV)
+    h = n // 2
+    B.gemm_items(x, Y2, W, [(h, ff, d, d, ff, 0, 0, 0), (n - h, ff, d, d, ff, 0, h * d, h * ff)],
+                 path=B.ENC_I8F16, row_scale=rs, flags=flags)
+    assert torch.equal(Y1, Y2)
+    assert torch.isfinite(Y1.float()).all()
+    del Y1, Y2
+    torch.cuda.empty_cache()
+
+
 def test_gemm_i8f16_f16_output_and_items():
     rng = np.random.default_rng(12)
     n, d, f = 96, 256, 384

@@ -140,7 +140,32 @@ hipError_t launch_gemm_i8f16(const GemmArgs &a, hipStream_t s) {
         const uint32_t cus = (uint32_t)gemm::device_cus(), kWideTiles = cus, kWideGated = 2 * cus,
                        kSlots = 2 * cus;
         if (gated) {
-            if (tiles_of(a, 256, 128) >= kWideGated) return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
+            if (tiles_of(a, 256, 128) >= kWideGated) {
+                // a one-item launch whose last round of 256-row tiles leaves
+                // most CUs idle issues the rows of its last 256-row tile as a
+                // second launch of 128-row tiles, when rounds x rows / rate
+                // (as below) says so
+                const GemmItemK &it = a.items[0];
+                if (a.nitems == 1 && it.n > 256) {
+                    const uint32_t last = it.n - (it.n - 1) / 256 * 256;  // rows of the last row tile
+                    const uint32_t ct = (it.m + 127) / 128, t_all = tiles_of(a, 256, 128), t_head = t_all - ct;
+                    const uint32_t t_tail = ct * ((last + 127) / 128);
+                    const double c_all = (double)((t_all + cus - 1) / cus) * 256;
+                    const double c_peel =
+                        (double)((t_head + cus - 1) / cus) * 256 + (double)((t_tail + cus - 1) / cus) * 128 / 0.8;
+                    if (c_peel < c_all) {
+                        GemmArgs head = a, tail = a;
+                        head.items[0].n = it.n - last;
+                        tail.items[0].n = last;
+                        tail.items[0].x_off += (uint64_t)(it.n - last) * it.ldx;
+                        tail.items[0].y_off += (uint64_t)(it.n - last) * it.ldy;
+                        const hipError_t h = gemm::launch_q8d<256, 256, 2, 4, 1, true>(head, s);
+                        if (h != hipSuccess) return h;
+                        return gemm::launch_q8d<128, 256, 2, 4, 1, true, 5>(tail, s);
+                    }
+                }
+                return gemm::launch_q8d<256, 256, 2, 4, 1, true>(a, s);
+            }
             // one block per CU for every gated tile: rounds of the CUs times
             // the tile's rows over its measured relative rate
             const auto cost = [&](int bm, double rate) {
