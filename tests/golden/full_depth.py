@@ -14,6 +14,9 @@ source, of the draw module, of the workload's configuration and item table, and
 of the inputs themselves (the input rows, every float tensor of every layer,
 and the first, middle and last rows of every int8 weight, drawn on their own).
 A test recomputes the key from the workload it builds and refuses a stale file.
+The DiT step program (`zimage_dit_step_1056`: context refiner on the caption
+rows, noise refiner on the image rows, then the stack) runs its stages in place
+as the oracle's `forward_stages` does, and its key covers every stage's inputs.
 
     python tests/golden/full_depth.py gemma_text_f32 zimage_dit_1056 ...
 
@@ -51,7 +54,7 @@ ORACLE_SRC = os.path.join(ROOT, "oracle", "oracle.c")
 SYNTH_SRC = os.path.join(ROOT, "transformer_encoder_forward_amd", "synth.py")
 
 WORKLOADS = ("gemma_text_f32", "gemma_text_ple_f32", "zimage_dit_1056", "zimage_dit_cfg_8448",
-             "zimage_dit_pad_cfg", "zimage_dit_mod_1056")
+             "zimage_dit_pad_cfg", "zimage_dit_mod_1056", "zimage_dit_step_1056")
 FIRST_ITEM_ONLY = ("zimage_dit_cfg_8448", "zimage_dit_pad_cfg")  # the oracle runs item 0 alone (module doc)
 
 
@@ -88,6 +91,24 @@ def key(w, pos=None) -> str:
     h.update(json.dumps(w.cfg, sort_keys=True).encode())
     h.update(json.dumps([w.rows, w.items, w.grids]).encode())
     h.update(np.ascontiguousarray(w.x, np.float32).tobytes())
+    _hash_layers(h, w)
+    for a in (w.final_w, w.final_b):
+        if a is not None:
+            h.update(np.ascontiguousarray(a).tobytes())
+    # a staged program: each refiner stage's rows, items, config and weights
+    for label, st, row0 in w.stages:
+        if st is w:
+            continue
+        h.update(f"{label}@{row0}".encode())
+        h.update(json.dumps(st.cfg, sort_keys=True).encode())
+        h.update(json.dumps([st.rows, st.items, st.grids]).encode())
+        _hash_layers(h, st)
+    return h.hexdigest()
+
+
+def _hash_layers(h, w) -> None:
+    """The layers' float tensors and scalars whole; int8 weights by three rows
+    each (drawn by the seeded generator, so a row pins the draw)."""
     shapes = wl.weight_shapes(w.cfg)
     for li, t in enumerate(w.layers):
         for name in sorted(t):
@@ -105,10 +126,6 @@ def key(w, pos=None) -> str:
                 for r in (0, m // 2, m - 1):
                     h.update(wl.int8_weight_rows(w.seed, li, name, shape, r, r + 1,
                                                  w.prefix).tobytes())
-    for a in (w.final_w, w.final_b):
-        if a is not None:
-            h.update(np.ascontiguousarray(a).tobytes())
-    return h.hexdigest()
 
 
 def item_rows(rr) -> np.ndarray:
@@ -169,6 +186,11 @@ def write(name: str) -> None:
         out = np.zeros((w.rows, w.cfg["d"]))
         out[idx] = O.forward(single, pos=None if pos is None else pos[idx])
         assert np.isin(rows, idx).all()
+    elif w.stages:
+        # the staged program: each stage in place on its rows, with its rows'
+        # positions in the joint table of the whole batch
+        joint = O.positions(w.rows, w.items, w.grids, w.cfg["rope_sections"])
+        out = O.forward_stages([(st, r0, joint[r0:r0 + st.rows]) for _, st, r0 in w.stages], w.x)
     else:
         out = O.forward(w, pos=pos)
     dt = time.time() - t0
