@@ -230,16 +230,18 @@ def test_dit_1056_full_width_layer_vs_oracle():
     assert err <= TOL_I8F16
 
 
-@pytest.mark.parametrize("name", ["zimage_dit_1056", "zimage_dit_cfg_8448", "zimage_dit_mod_1056"])
+@pytest.mark.parametrize("name", ["zimage_dit_1056", "zimage_dit_cfg_8448", "zimage_dit_mod_1056",
+                                  "zimage_dit_pad_cfg"])
 def test_dit_full_stack_vs_stored_oracle(name):
     """The DiT stack whole (every layer, every row of the batch), its output rows
     sampled (each range's first, middle and last rows, tile edges, seeded draws)
     against the oracle's forward of the same batch with its f16 sites, stored by
     tests/golden/full_depth.py under a key of its inputs: the plain 1056-row
-    stack, the 8448-row CFG pair and the modulated q8_2f stack with the Turbo
-    guards.  For the CFG pair the stored rows are the first item's (the oracle
-    ran that item alone; the second item equals its own single forward bit for
-    bit, tested below)."""
+    stack, the 8448-row CFG pair, the modulated q8_2f stack with the Turbo
+    guards and the padded CFG pair (pad rows at position (0, 0)).  For the CFG
+    pairs the stored rows are the first item's (the oracle ran that item alone;
+    the second item equals its own single forward bit for bit, tested below and
+    in the stack tests)."""
     w = wl.make(name, lazy_int8=True)
     rows, ref = full_depth.load(name, w)
     got = host(run(w))
