@@ -852,13 +852,20 @@ def test_gated_epilogue_column_field_and_guard(path, n, ff, d):
     assert torch.equal(fused, unfused)
 
 
-@pytest.mark.parametrize("path,items,nq,hd", [(B.ENC_I8F16, [[(0, 300), (400, 40)], [(300, 100)]], 4, 128),
-                                              (B.ENC_I8F16, [[(0, 200)]], 4, 64),
-                                              (B.ENC_F32, [[(0, 1024)]], 12, 64),
-                                              (B.ENC_F32, [[(0, 100)], [(100, 50)]], 2, 128)])
-def test_attention_output_column_field_and_scale(path, items, nq, hd):
+@pytest.mark.parametrize("path,items,nq,hd,window", [
+    (B.ENC_I8F16, [[(0, 300), (400, 40)], [(300, 100)]], 4, 128, 0),
+    # unsplit f16 kernels: 128-query blocks; 256-query blocks; windowed
+    (B.ENC_I8F16, [[(0, 1100)]], 32, 128, 0),
+    (B.ENC_I8F16, [[(0, 500), (1100, 100)], [(500, 600)]], 128, 128, 0),
+    (B.ENC_I8F16, [[(0, 700)]], 4, 128, 96),
+    (B.ENC_I8F16, [[(0, 200)]], 4, 64, 0),
+    (B.ENC_F32, [[(0, 1024)]], 12, 64, 0),
+    (B.ENC_F32, [[(0, 100)], [(100, 50)]], 2, 128, 0)])
+def test_attention_output_column_field_and_scale(path, items, nq, hd, window):
     """out = o * out_scale * out_col (the O projection's column field and the
-    guards), in the attention epilogue and in the key-split merge."""
+    guards), in the attention epilogue of every kernel (f16: the split-key one,
+    the unsplit 128- and 256-query ones, the windowed one, hd 64; f32) and in
+    the key-split merge."""
     f16 = path == B.ENC_I8F16
     rows = max(r0 + n for rr in items for r0, n in rr)
     rng = np.random.default_rng(rows)
@@ -866,10 +873,10 @@ def test_attention_output_column_field_and_scale(path, items, nq, hd):
     dt = torch.float16 if f16 else torch.float32
     col = np.exp(0.25 * rng.normal(0, 1, nq * hd)).astype(np.float32)
     out = torch.zeros((rows, nq * hd), dtype=dt, device=DEV)
-    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.1, 0, path=path, out_col=to_dev(col),
+    B.attention_items(to_dev(p), out, items, nq, nq, hd, 0.1, window, path=path, out_col=to_dev(col),
                       out_scale=2.0)
     q, k, v = _split(p, nq, nq, hd)
-    ref = O.attention(items, q, k, v, nq, nq, hd, 0.1, 0) * col.astype(np.float64) * 2.0
+    ref = O.attention(items, q, k, v, nq, nq, hd, 0.1, window) * col.astype(np.float64) * 2.0
     if f16:
         ref = np.vectorize(O.round_f16)(ref)
     got = host(out)
