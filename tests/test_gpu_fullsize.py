@@ -251,6 +251,28 @@ def test_dit_full_stack_vs_stored_oracle(name):
     assert err <= TOL_I8F16
 
 
+def test_dit_step_program_full_vs_stored_oracle():
+    """The DiT step program whole, through encoder_stages_forward: the context
+    refiner (2 unmodulated blocks) on the 32 caption rows, the noise refiner (2
+    modulated blocks) on the 1024 image rows, then the 30-block modulated stack
+    on all 1056 rows, in place; sampled output rows against the oracle's
+    forward_stages stored by tests/golden/full_depth.py."""
+    name = "zimage_dit_step_1056"
+    w = wl.make(name, lazy_int8=True)
+    rows, ref = full_depth.load(name, w)
+    prog = M.DeviceProgram(w, DEV)
+    X = torch.from_numpy(np.ascontiguousarray(w.x)).to(DEV)
+    h = torch.empty_like(X)
+    ws = prog.workspace(DEV)
+    M.stages_forward(prog, X, h, ws)
+    torch.cuda.synchronize()
+    got = host(h)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got[rows], ref)
+    say(f"DiT step program ({len(w.stages)} stages, {w.rows} rows): {len(rows)} rows, error {err:.2e}")
+    assert err <= TOL_I8F16
+
+
 def test_dit_padded_pair_full_width_layer_vs_oracle():
     """The padded CFG pair at full width and rows (2 x (928 + 32) = 1920 rows:
     30x30 images padded to 928 rows, 20 captions padded to 32), one layer; every
