@@ -179,7 +179,11 @@ typedef struct {
  * merged by a second kernel in a fixed order: the same softmax, regrouped.
  * Whether and how an item is split depends only on its length, nq, the path
  * and the window, so a packed batch gives the same bits as its items alone.
- * With ws == NULL nothing is split.  A ws smaller than needed is ENC_ESHAPE. */
+ * With ws == NULL nothing is split.  A ws smaller than needed is ENC_ESHAPE.
+ * ENC_I8F16 at hd 128 never uses ws: a windowless item whose blocks of 64
+ * queries times nq number at most 512 has each query's keys split in two
+ * halves inside one block and merged there (the same length-only rule, so the
+ * same invariance). */
 ENC_API enc_status attention_items(enc_ctx *ctx, const enc_attn_desc *desc, const enc_item *items,
                            uint32_t nitems, enc_stream stream);
 
