@@ -381,6 +381,9 @@ ATTN_CASES = [
     ("window", [[(0, 700)], [(700, 33)], [(733, 260)]], 96),
     ("window_big", [[(0, 1100)]], 512),
     ("two_range", [[(0, 200), (420, 20)], [(200, 200), (440, 20)], [(400, 20)]], 0),
+    # the range seam inside a key block of the split f16 kernel's first key half
+    # (block 1 of 11 and of 5; "two_range" has it in the second half)
+    ("two_range_seams", [[(0, 40), (100, 300)], [(40, 60), (400, 90)]], 0),
 ]
 
 
